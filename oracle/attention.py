@@ -1,0 +1,144 @@
+"""Exact attention over a paged KV cache — oracle side (test infrastructure).
+
+Paging changes where K and V live, not what attention computes: the block
+table only maps logical order onto arbitrary physical blocks ("从静态批处理到
+状态化推理集群", "PagedAttention：把逻辑连续与物理连续分开"; the kernel reads
+K/V through the block table). So the oracle is the textbook definition,
+evaluated in float64 on values gathered through the block table:
+
+    s_j = scale * <q_h, K_j>,    out_h = sum_j exp(s_j - max s) V_j / sum_j exp(s_j - max s)
+
+(the output formula in "宣稱省下 106 倍成本…", "中：Kimi K3 的 DCP 選擇與 DEP 轉折",
+the online-softmax Q&A: output = sum exp(score) * value / sum exp(score), with
+the local maximum subtracted before exponentiating).
+
+Readings where the pages are silent (each is also listed in the design notes):
+* the new token's K/V is written before attention and the query attends to
+  itself: a decode query at position ctx-1 sees ctx keys (the prefill/decode
+  example of the agentic-serving page: step 2 "looks at 7 tokens" = the 6
+  prompt tokens plus the one just generated);
+* causal: key j is visible to the query at position p iff j <= p;
+* query row r of a sequence with q_len query tokens and ctx cached tokens
+  (this chunk included) sits at position p = ctx - q_len + r;
+* sliding window W > 0: keys [max(0, p - W + 1), p] (W keys including
+  itself; the DeepSeek-V4.1 write-up rebuilds the window [H-128, H));
+* grouped-query attention: query head h reads KV head h // (Hq / Hkv);
+* fp8 caches carry one fp32 scale per physical block for K and one for V:
+  stored value = e4m3fn_decode(byte) * scale[block].
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import FP8, to_f64
+
+
+def gather_kv(k_pool, v_pool, cache_dtype: str, k_scale, v_scale, block_table_row,
+              kv_head: int, positions, block_size: int = 16):
+    """K, V rows (float64, [n][head_size]) of one KV head at logical ``positions``.
+
+    Physical block of position j = block_table_row[j // block_size], slot
+    offset j % block_size; K pool is [NB][Hkv][B][D], V pool [NB][Hkv][D][B].
+    """
+    positions = np.asarray(positions, dtype=np.int64)
+    blk = np.asarray(block_table_row, dtype=np.int64)[positions // block_size]
+    off = positions % block_size
+    k_raw = k_pool[blk, kv_head, off, :]                   # [n][D]
+    v_raw = v_pool[:, kv_head].transpose(0, 2, 1)[blk, off, :]  # [NB][B][D] -> [n][D]
+    K = to_f64(k_raw, cache_dtype)
+    V = to_f64(v_raw, cache_dtype)
+    if cache_dtype == FP8:
+        ks = np.asarray(k_scale, dtype=np.float32).astype(np.float64)[blk]
+        vs = np.asarray(v_scale, dtype=np.float32).astype(np.float64)[blk]
+        K = K * ks[:, None]
+        V = V * vs[:, None]
+    return K, V
+
+
+def _visible(q_pos: np.ndarray, k_pos: np.ndarray, window: int) -> np.ndarray:
+    """mask[r, j]: key position k_pos[j] is visible to the query at q_pos[r]."""
+    vis = k_pos[None, :] <= q_pos[:, None]
+    if window > 0:
+        vis &= k_pos[None, :] >= (q_pos[:, None] - window + 1)
+    return vis
+
+
+def attend_sequence(q_f64, k_pool, v_pool, cache_dtype: str, k_scale, v_scale,
+                    block_table_row, ctx: int, num_kv_heads: int, scale: float,
+                    sliding_window: int = 0, block_size: int = 16, heads=None):
+    """Attention output of one sequence, float64.
+
+    q_f64: [q_len][Hq][D] queries of this sequence (already float64), the
+    last q_len positions of a context of ``ctx`` tokens. Returns
+    [q_len][Hq][D]; heads not listed in ``heads`` are left NaN.
+    """
+    q_len, Hq, D = q_f64.shape
+    assert 1 <= q_len <= ctx, "a sequence attends to at least itself"
+    G = Hq // num_kv_heads
+    q_pos = np.arange(ctx - q_len, ctx, dtype=np.int64)
+    lo = 0 if sliding_window <= 0 else max(0, int(q_pos[0]) - sliding_window + 1)
+    k_pos = np.arange(lo, ctx, dtype=np.int64)
+    vis = _visible(q_pos, k_pos, sliding_window)
+    out = np.full((q_len, Hq, D), np.nan)
+    heads = range(Hq) if heads is None else heads
+    for g in sorted({h // G for h in heads}):
+        K, V = gather_kv(k_pool, v_pool, cache_dtype, k_scale, v_scale, block_table_row,
+                         g, k_pos, block_size)
+        for h in [h for h in heads if h // G == g]:
+            s = scale * (q_f64[:, h, :] @ K.T)                # [q_len][n]
+            s = np.where(vis, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            out[:, h, :] = (p @ V) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def paged_attention(query, q_dtype: str, k_pool, v_pool, cache_dtype: str, k_scale, v_scale,
+                    block_table, cu_seqlens, context_lens, num_kv_heads: int, scale: float,
+                    sliding_window: int = 0, block_size: int = 16, seqs=None):
+    """Whole flattened varlen batch: out[num_q_tokens][Hq][D] in float64.
+
+    query: raw storage [num_q_tokens][Hq][D]; sequence s owns query rows
+    cu_seqlens[s] .. cu_seqlens[s+1]-1 and has context_lens[s] cached tokens
+    (this call's tokens included). Decode is the case q_len == 1.
+    Rows of sequences not in ``seqs`` are left NaN.
+    """
+    q = to_f64(query, q_dtype)
+    out = np.full(q.shape, np.nan)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    S = len(ctx)
+    for s in (range(S) if seqs is None else seqs):
+        r0, r1 = int(cu[s]), int(cu[s + 1])
+        out[r0:r1] = attend_sequence(q[r0:r1], k_pool, v_pool, cache_dtype, k_scale, v_scale,
+                                     block_table[s], int(ctx[s]), num_kv_heads, scale,
+                                     sliding_window, block_size)
+    return out
+
+
+def partial_softmax(scores, values):
+    """Summary of one key range: (m, l, o) = (max s, sum e^(s-m), sum e^(s-m) v).
+
+    The per-range state each worker hands over in the distributed
+    weighted-average Q&A ("local weighted sum" and "local weight sum", with the
+    local maximum subtracted before exponentiating).
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    v = np.asarray(values, dtype=np.float64)
+    m = s.max()
+    w = np.exp(s - m)
+    return m, w.sum(), w @ v
+
+
+def merge_partials(parts):
+    """Exact softmax output from per-range summaries (m_i, l_i, o_i).
+
+    M = max_i m_i, L = sum_i l_i e^(m_i - M), out = sum_i o_i e^(m_i - M) / L:
+    each range's sums are brought to the common maximum by the correction
+    factor e^(m_i - M), then added and divided once.
+    """
+    M = max(p[0] for p in parts)
+    L = sum(p[1] * np.exp(p[0] - M) for p in parts)
+    O = sum(np.asarray(p[2], dtype=np.float64) * np.exp(p[0] - M) for p in parts)
+    return O / L
