@@ -1,0 +1,176 @@
+/*
+ * pa.h — C ABI of libpa: attention over a paged KV cache on MI355X (gfx950).
+ *
+ * What the three calls compute (sources are the page titles and sections):
+ *
+ *  - pa_reshape_and_cache writes the new tokens' K and V into fixed-size
+ *    physical blocks of 16 tokens through a per-token slot_mapping
+ *    (vLLM architecture summary, "第一部分：LLM 引擎核心": the forward pass
+ *    builds slot_mapping while preparing inputs; "大模型推理优化学习笔记",
+ *    "KV Cache": K/V are written at prefill and appended at every decode step).
+ *  - pa_decode computes, for one query token per sequence, softmax attention
+ *    over that sequence's cached keys, reading K/V back through a per-sequence
+ *    block table ("从静态批处理到状态化推理集群", "PagedAttention：把逻辑连续与物理
+ *    连续分开": (sequence, logical block) -> physical block; the kernel reads
+ *    K/V by block table). Long contexts are split into key ranges whose
+ *    partial softmax summaries are merged exactly ("宣稱省下 106 倍成本…",
+ *    the online-softmax Q&A of "中：Kimi K3 的 DCP 選擇與 DEP 轉折").
+ *  - pa_prefill_chunk does the same for a flattened variable-length batch of
+ *    causal query chunks (cu_seqlens), e.g. decode tokens and one chunk of a
+ *    long prompt scheduled together under a token budget
+ *    ("大模型推理优化学习笔记", "Chunked Prefill"; "从静态批处理到状态化推理集群",
+ *    "Chunked prefill：在共置引擎里治理阶段干扰").
+ *
+ * Semantics fixed by this library where the pages are silent:
+ *  - the new tokens' K/V are written first and every query attends to itself:
+ *    query row r of a sequence with q_len rows and context_len cached tokens
+ *    (this call's tokens included) sits at position p = context_len - q_len + r
+ *    and sees keys j <= p; with sliding_window W > 0 only j >= p - W + 1;
+ *  - query head h reads KV head h / (num_heads / num_kv_heads);
+ *  - softmax scale is the caller's `scale` (1/sqrt(head_size) in practice).
+ *
+ * Layouts (all tensors dense, row-major, device memory unless noted):
+ *    k_cache  [num_blocks][num_kv_heads][block_size][head_size]
+ *    v_cache  [num_blocks][num_kv_heads][head_size][block_size]   (V is stored
+ *             transposed inside each block so that one block of one head is a
+ *             contiguous tile whose rows run along keys)
+ *    query/out [num_q_tokens][num_heads][head_size]
+ *    key/value (new tokens) [num_tokens][num_kv_heads][head_size]
+ *    block_table [num_seqs][block_table_stride] int32, physical block ids
+ *    k_scale/v_scale [num_blocks] fp32, fp8 caches only (stored value =
+ *             e4m3fn(byte) * scale[block]); NULL otherwise.
+ *
+ * Ownership and ordering: the caller allocates and frees every buffer,
+ * including the workspace sized by the *_workspace_bytes queries. The library
+ * never allocates, frees, synchronises or copies device-to-host; each call
+ * only enqueues kernels on `stream` and returns.
+ *
+ * Errors: arguments checked on the host (sizes, dtypes, null pointers,
+ * workspace size) return a non-PA_OK status, enqueue nothing and set a
+ * thread-local message readable by pa_last_error(). A failed launch returns
+ * PA_ERR_HIP. No C++ exception crosses this ABI.
+ *
+ * Device-side preconditions (the caller's; not checked on the device):
+ *  1 <= context_lens[s] <= max_context_len; ceil(context_lens[s]/16) <=
+ *  block_table_stride; every block id the sequence uses is in [0, num_blocks);
+ *  1 <= q_len(s) <= context_lens[s] and cu_seqlens non-decreasing with
+ *  cu_seqlens[0] = 0, cu_seqlens[num_seqs] = num_q_tokens, q_len(s) <= max_q_len;
+ *  slots of one write call are unique and name blocks the writer owns
+ *  exclusively (a shared non-full block is copied before it is written).
+ *
+ * Determinism: identical inputs and sizes give bitwise identical outputs.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t; NULL means the default stream. */
+typedef struct ihipStream_t* pa_stream_t;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = 1,   /* bad size, null pointer, inconsistent sizes */
+  PA_ERR_UNSUPPORTED = 2,        /* valid request this build has no kernel for */
+  PA_ERR_WORKSPACE_TOO_SMALL = 3,
+  PA_ERR_HIP = 4                 /* a HIP runtime call or launch failed */
+} pa_status;
+
+typedef enum {
+  PA_F32 = 0,
+  PA_BF16 = 1,
+  PA_FP8_E4M3 = 2                /* OCP e4m3fn, KV cache only */
+} pa_dtype;
+
+#define PA_ABI_VERSION 1
+#define PA_BLOCK_SIZE 16
+
+/*
+ * Write new K/V rows into the paged cache (one row per token and KV head).
+ * key, value: [num_tokens][num_kv_heads][head_size] of in_dtype.
+ * slot_mapping: int64 [num_tokens]; slot = physical_block * 16 + offset;
+ *   a negative slot skips the token (padding).
+ * cache_dtype == in_dtype: a bit-exact copy.
+ * cache_dtype == PA_FP8_E4M3 with in_dtype F32 or BF16: quantising write,
+ *   byte = e4m3fn(x / scale[block]) rounded to nearest even and saturated to
+ *   +-448, the fp32 quotient correctly rounded; k_scale/v_scale are read,
+ *   never written (the caller chose them).
+ * num_tokens == 0 enqueues nothing and returns PA_OK.
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                               const float* k_scale, const float* v_scale,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                               int32_t head_size, pa_dtype in_dtype, pa_dtype cache_dtype,
+                               pa_stream_t stream);
+
+/*
+ * Decode attention: one query token per sequence.
+ * out, query: [num_seqs][num_heads][head_size] of q_dtype (out has the query's
+ *   type; results are rounded to nearest even from fp32).
+ * context_lens: int32 [num_seqs]; max_context_len is a HOST scalar >= every
+ *   context length (it sizes the grid without a device-to-host copy).
+ * sliding_window: 0 = full attention, W > 0 = the last W positions.
+ * workspace: device scratch of at least pa_decode_workspace_bytes(...) bytes,
+ *   contents on entry irrelevant.
+ * Supported: block_size 16; head_size 64 or 128; num_heads / num_kv_heads in
+ *   {1, 2, 4, 8, 16}; (q, cache) dtypes (F32, F32), (BF16, BF16),
+ *   (BF16, FP8_E4M3).
+ */
+pa_status pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
+                    const float* k_scale, const float* v_scale, const int32_t* block_table,
+                    int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_size, int32_t block_size, int32_t num_blocks, pa_dtype q_dtype,
+                    pa_dtype cache_dtype, float scale, int32_t sliding_window, void* workspace,
+                    size_t workspace_bytes, pa_stream_t stream);
+
+/*
+ * Causal attention for a flattened variable-length batch.
+ * Sequence s owns query rows cu_seqlens[s] .. cu_seqlens[s+1]-1 (int32
+ * [num_seqs+1]); context_lens[s] counts its cached tokens including this
+ * chunk, whose K/V must already be in the cache. Rows of sequences with one
+ * query token take the decode kernel; longer chunks take the matrix-core
+ * (MFMA) kernel. num_q_tokens, max_q_len and max_context_len are HOST
+ * scalars bounding the device arrays.
+ * Supported as pa_decode, except that chunks longer than one token need
+ *   q_dtype BF16 (cache BF16 or FP8_E4M3).
+ */
+pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale, const int32_t* block_table,
+                           int32_t block_table_stride, const int32_t* cu_seqlens,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_tokens,
+                           int32_t max_q_len, int32_t max_context_len, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                           int32_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype, float scale,
+                           int32_t sliding_window, void* workspace, size_t workspace_bytes,
+                           pa_stream_t stream);
+
+/* Workspace bytes pa_decode needs for these sizes (0 if none). */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_size, int32_t sliding_window);
+
+/* Workspace bytes pa_prefill_chunk needs for these sizes (0 if none). */
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len,
+                                  int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_size, int32_t sliding_window);
+
+/* Static name of a status code. */
+const char* pa_status_string(pa_status s);
+
+/* Detail of the calling thread's last non-OK status ("" if none). */
+const char* pa_last_error(void);
+
+/* PA_ABI_VERSION of the built library. */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

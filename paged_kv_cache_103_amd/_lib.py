@@ -1,0 +1,187 @@
+"""ctypes binding of libpa (include/pa.h): argument marshalling only.
+
+Every call takes torch tensors for device memory, reads their sizes, and
+passes raw pointers plus the current HIP stream to the C ABI. All compute
+runs in the library's HIP kernels; if the library is missing this module
+raises instead of falling back to anything.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libpa.so")
+
+PA_OK = 0
+PA_ERR_INVALID_ARGUMENT = 1
+PA_ERR_UNSUPPORTED = 2
+PA_ERR_WORKSPACE_TOO_SMALL = 3
+PA_ERR_HIP = 4
+
+PA_F32 = 0
+PA_BF16 = 1
+PA_FP8_E4M3 = 2
+
+BLOCK_SIZE = 16
+
+# every symbol include/pa.h declares
+EXPORTED = (
+    "pa_reshape_and_cache",
+    "pa_decode",
+    "pa_prefill_chunk",
+    "pa_decode_workspace_bytes",
+    "pa_prefill_workspace_bytes",
+    "pa_status_string",
+    "pa_last_error",
+    "pa_abi_version",
+)
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{status_string(status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libpa.so (built in-tree by paged_kv_cache_103_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m paged_kv_cache_103_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64p, f32p, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
+    L.pa_reshape_and_cache.restype = ctypes.c_int
+    L.pa_reshape_and_cache.argtypes = [vp, vp, vp, vp, f32p, f32p, i64p, i32, i32, i32, i32, i32,
+                                       ctypes.c_int, ctypes.c_int, vp]
+    L.pa_decode.restype = ctypes.c_int
+    L.pa_decode.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32,
+                            ctypes.c_int, ctypes.c_int, ctypes.c_float, i32, vp, sz, vp]
+    L.pa_prefill_chunk.restype = ctypes.c_int
+    L.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                   i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_float, i32,
+                                   vp, sz, vp]
+    L.pa_decode_workspace_bytes.restype = sz
+    L.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.pa_prefill_workspace_bytes.restype = sz
+    L.pa_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    L.pa_status_string.restype = ctypes.c_char_p
+    L.pa_status_string.argtypes = [ctypes.c_int]
+    L.pa_last_error.restype = ctypes.c_char_p
+    L.pa_last_error.argtypes = []
+    L.pa_abi_version.restype = ctypes.c_int32
+    L.pa_abi_version.argtypes = []
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return load().pa_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load().pa_last_error().decode()
+
+
+def abi_version() -> int:
+    return int(load().pa_abi_version())
+
+
+def _check(status: int) -> None:
+    if status != PA_OK:
+        raise PAError(status, last_error())
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return PA_F32
+    if t == torch.bfloat16:
+        return PA_BF16
+    if t in (torch.uint8, torch.float8_e4m3fn):
+        return PA_FP8_E4M3
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libpa must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def decode_workspace_bytes(num_seqs: int, max_context_len: int, num_heads: int, num_kv_heads: int,
+                           head_size: int, sliding_window: int = 0) -> int:
+    return int(load().pa_decode_workspace_bytes(num_seqs, max_context_len, num_heads, num_kv_heads,
+                                                head_size, sliding_window))
+
+
+def prefill_workspace_bytes(num_seqs: int, num_q_tokens: int, max_q_len: int, max_context_len: int,
+                            num_heads: int, num_kv_heads: int, head_size: int,
+                            sliding_window: int = 0) -> int:
+    return int(load().pa_prefill_workspace_bytes(num_seqs, num_q_tokens, max_q_len, max_context_len,
+                                                 num_heads, num_kv_heads, head_size, sliding_window))
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                      k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    """pa_reshape_and_cache: key/value [T][Hkv][D]; k_cache [NB][Hkv][16][D];
+    v_cache [NB][Hkv][D][16]; slot_mapping int64 [T]."""
+    T, H, D = key.shape
+    NB = k_cache.shape[0]
+    assert slot_mapping.dtype == torch.int64 and slot_mapping.numel() == T
+    _check(load().pa_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping), T, NB,
+                                       k_cache.shape[2], H, D, dtype_code(key.dtype),
+                                       dtype_code(k_cache.dtype), _stream(stream)))
+
+
+def decode(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           block_table: torch.Tensor, context_lens: torch.Tensor, max_context_len: int, scale: float,
+           k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+           sliding_window: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """pa_decode: query/out [S][Hq][D]; block_table int32 [S][stride]; context_lens int32 [S]."""
+    S, Hq, D = query.shape
+    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().pa_decode(_ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                            _ptr(v_scale), _ptr(block_table), block_table.shape[1], _ptr(context_lens),
+                            S, int(max_context_len), Hq, Hkv, D, k_cache.shape[2], NB,
+                            dtype_code(query.dtype), dtype_code(k_cache.dtype), float(scale),
+                            int(sliding_window), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def prefill_chunk(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  block_table: torch.Tensor, cu_seqlens: torch.Tensor, context_lens: torch.Tensor,
+                  max_q_len: int, max_context_len: int, scale: float,
+                  k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                  sliding_window: int = 0, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> None:
+    """pa_prefill_chunk: flattened varlen batch; query/out [Nq][Hq][D]; cu_seqlens int32 [S+1]."""
+    Nq, Hq, D = query.shape
+    S = context_lens.shape[0]
+    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().pa_prefill_chunk(_ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                   _ptr(v_scale), _ptr(block_table), block_table.shape[1],
+                                   _ptr(cu_seqlens), _ptr(context_lens), S, Nq, int(max_q_len),
+                                   int(max_context_len), Hq, Hkv, D, k_cache.shape[2], NB,
+                                   dtype_code(query.dtype), dtype_code(k_cache.dtype), float(scale),
+                                   int(sliding_window), _ptr(workspace), ws_bytes, _stream(stream)))

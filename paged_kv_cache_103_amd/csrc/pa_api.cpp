@@ -1,0 +1,309 @@
+// C ABI of libpa: host-side validation, launch planning and error mapping.
+// The operations are defined in include/pa.h; this file only checks the
+// arguments that can be checked on the host, sizes the split-K plan from host
+// scalars (never reading device memory), and enqueues the kernels.
+#include "pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) {
+    g_last_error.clear();
+    return PA_OK;
+  }
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool known_dtype(pa_dtype d) { return d == PA_F32 || d == PA_BF16 || d == PA_FP8_E4M3; }
+const char* dtype_name(pa_dtype d) {
+  switch (d) {
+    case PA_F32: return "f32";
+    case PA_BF16: return "bf16";
+    case PA_FP8_E4M3: return "fp8_e4m3";
+  }
+  return "unknown";
+}
+
+// Checks shared by the two attention entry points.
+pa_status check_attention_common(const void* out, const void* query, const void* k_cache,
+                                 const void* v_cache, const float* k_scale, const float* v_scale,
+                                 const int32_t* block_table, int32_t block_table_stride,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_size, int32_t block_size, int32_t num_blocks,
+                                 pa_dtype q_dtype, pa_dtype cache_dtype, float scale,
+                                 int32_t sliding_window) {
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (block_size != PA_BLOCK_SIZE)
+    return fail(PA_ERR_UNSUPPORTED, "block_size must be %d (got %d)", PA_BLOCK_SIZE, block_size);
+  if (head_size != 64 && head_size != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_size must be 64 or 128 (got %d)", head_size);
+  if (num_heads <= 0 || num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_heads (%d) and num_kv_heads (%d) must be > 0",
+                num_heads, num_kv_heads);
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_heads (%d) must be a multiple of num_kv_heads (%d)",
+                num_heads, num_kv_heads);
+  if (!known_dtype(q_dtype) || !known_dtype(cache_dtype))
+    return fail(PA_ERR_INVALID_ARGUMENT, "unknown dtype (q %d, cache %d)", (int)q_dtype,
+                (int)cache_dtype);
+  if (q_dtype == PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "fp8 queries are not supported (cache only)");
+  if (!(scale > 0.0f) || scale != scale)
+    return fail(PA_ERR_INVALID_ARGUMENT, "scale must be a positive number");
+  if (sliding_window < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "sliding_window must be >= 0 (got %d)", sliding_window);
+  if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks must be > 0 (got %d)", num_blocks);
+  if (num_seqs == 0) return PA_OK;
+  if (max_context_len <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_context_len must be > 0 (got %d)", max_context_len);
+  if (block_table_stride < (max_context_len + block_size - 1) / block_size)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "block_table_stride (%d) is smaller than ceil(max_context_len/block_size) (%d)",
+                block_table_stride, (max_context_len + block_size - 1) / block_size);
+  if (!out || !query || !k_cache || !v_cache || !block_table || !context_lens)
+    return fail(PA_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale))
+    return fail(PA_ERR_INVALID_ARGUMENT, "fp8 cache needs k_scale and v_scale");
+  const int group = num_heads / num_kv_heads;
+  if (!pa::decode_supported((int)q_dtype, (int)cache_dtype, head_size, group))
+    return fail(PA_ERR_UNSUPPORTED, "no decode kernel for q %s, cache %s, head_size %d, group %d",
+                dtype_name(q_dtype), dtype_name(cache_dtype), head_size, group);
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                               const float* k_scale, const float* v_scale,
+                               const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                               int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                               pa_dtype in_dtype, pa_dtype cache_dtype, pa_stream_t stream) {
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_tokens must be >= 0 (got %d)", num_tokens);
+  if (block_size != PA_BLOCK_SIZE)
+    return fail(PA_ERR_UNSUPPORTED, "block_size must be %d (got %d)", PA_BLOCK_SIZE, block_size);
+  if (head_size != 64 && head_size != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_size must be 64 or 128 (got %d)", head_size);
+  if (num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_kv_heads must be > 0 (got %d)", num_kv_heads);
+  if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks must be > 0 (got %d)", num_blocks);
+  if (!known_dtype(in_dtype) || !known_dtype(cache_dtype))
+    return fail(PA_ERR_INVALID_ARGUMENT, "unknown dtype (in %d, cache %d)", (int)in_dtype, (int)cache_dtype);
+  if (in_dtype != cache_dtype && cache_dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "write from %s into a %s cache is not supported",
+                dtype_name(in_dtype), dtype_name(cache_dtype));
+  if (in_dtype == PA_FP8_E4M3 && cache_dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "fp8 input needs an fp8 cache");
+  const bool quantise = cache_dtype == PA_FP8_E4M3 && in_dtype != PA_FP8_E4M3;
+  if (num_tokens == 0) {
+    g_last_error.clear();
+    return PA_OK;
+  }
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (quantise && (!k_scale || !v_scale))
+    return fail(PA_ERR_INVALID_ARGUMENT, "quantising write needs k_scale and v_scale");
+  hipError_t e = pa::launch_reshape_and_cache(key, value, k_cache, v_cache, k_scale, v_scale,
+                                              slot_mapping, num_tokens, num_kv_heads, head_size,
+                                              (int)in_dtype, (int)cache_dtype, (hipStream_t)stream);
+  return hip_status(e, "reshape_and_cache launch");
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_size, int32_t sliding_window) {
+  if (num_seqs <= 0 || max_context_len <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0)
+    return 0;
+  const pa::DecodePlan plan = pa::plan_decode(num_seqs, max_context_len, num_kv_heads, sliding_window);
+  return pa::decode_workspace_bytes(plan, num_seqs, num_heads, head_size);
+}
+
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len,
+                                  int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_size, int32_t sliding_window) {
+  (void)num_q_tokens;
+  (void)max_q_len;
+  // the prefill tiles need no scratch; the one-token rows use the decode plan
+  return pa_decode_workspace_bytes(num_seqs, max_context_len, num_heads, num_kv_heads, head_size,
+                                   sliding_window);
+}
+
+pa_status pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
+                    const float* k_scale, const float* v_scale, const int32_t* block_table,
+                    int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_size, int32_t block_size, int32_t num_blocks, pa_dtype q_dtype,
+                    pa_dtype cache_dtype, float scale, int32_t sliding_window, void* workspace,
+                    size_t workspace_bytes, pa_stream_t stream) {
+  pa_status st = check_attention_common(out, query, k_cache, v_cache, k_scale, v_scale, block_table,
+                                        block_table_stride, context_lens, num_seqs, max_context_len,
+                                        num_heads, num_kv_heads, head_size, block_size, num_blocks,
+                                        q_dtype, cache_dtype, scale, sliding_window);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) {
+    g_last_error.clear();
+    return PA_OK;
+  }
+  const pa::DecodePlan plan = pa::plan_decode(num_seqs, max_context_len, num_kv_heads, sliding_window);
+  const size_t need = pa::decode_workspace_bytes(plan, num_seqs, num_heads, head_size);
+  if (workspace_bytes < need || (need > 0 && workspace == nullptr))
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes (got %zu)", need,
+                workspace_bytes);
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.query = query;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.cu_seqlens = nullptr;
+  const size_t slots = (size_t)num_seqs * num_heads * plan.max_parts;
+  a.part_o = need ? static_cast<float*>(workspace) : nullptr;
+  a.part_ml = need ? static_cast<float*>(workspace) + slots * head_size : nullptr;
+  a.bt_stride = block_table_stride;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.window = sliding_window;
+  a.pb = plan.pb;
+  a.max_parts = plan.max_parts;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pa::launch_decode(a, (int)q_dtype, (int)cache_dtype, head_size, (hipStream_t)stream);
+  return hip_status(e, "decode launch");
+}
+
+pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale, const int32_t* block_table,
+                           int32_t block_table_stride, const int32_t* cu_seqlens,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_tokens,
+                           int32_t max_q_len, int32_t max_context_len, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                           int32_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype, float scale,
+                           int32_t sliding_window, void* workspace, size_t workspace_bytes,
+                           pa_stream_t stream) {
+  pa_status st = check_attention_common(out, query, k_cache, v_cache, k_scale, v_scale, block_table,
+                                        block_table_stride, context_lens, num_seqs, max_context_len,
+                                        num_heads, num_kv_heads, head_size, block_size, num_blocks,
+                                        q_dtype, cache_dtype, scale, sliding_window);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) {
+    g_last_error.clear();
+    return PA_OK;
+  }
+  if (!cu_seqlens) return fail(PA_ERR_INVALID_ARGUMENT, "null cu_seqlens");
+  if (num_q_tokens < num_seqs)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_q_tokens (%d) < num_seqs (%d): every sequence needs a query",
+                num_q_tokens, num_seqs);
+  if (max_q_len < 1 || max_q_len > num_q_tokens || max_q_len > max_context_len)
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_q_len (%d) must be in [1, min(num_q_tokens, max_context_len)]",
+                max_q_len);
+  const int group = num_heads / num_kv_heads;
+  const bool has_chunks = max_q_len > 1;
+  if (has_chunks && !pa::prefill_supported((int)q_dtype, (int)cache_dtype, head_size, group))
+    return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for q %s, cache %s, head_size %d, group %d",
+                dtype_name(q_dtype), dtype_name(cache_dtype), head_size, group);
+  const pa::DecodePlan plan = pa::plan_decode(num_seqs, max_context_len, num_kv_heads, sliding_window);
+  const size_t need = pa::decode_workspace_bytes(plan, num_seqs, num_heads, head_size);
+  if (workspace_bytes < need || (need > 0 && workspace == nullptr))
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "prefill needs %zu workspace bytes (got %zu)", need,
+                workspace_bytes);
+  const hipStream_t hs = (hipStream_t)stream;
+  const float scale_log2 = scale * 1.4426950408889634f;
+
+  // one-token rows: the decode kernel (skips rows of longer chunks)
+  pa::DecodeArgs d{};
+  d.out = out;
+  d.query = query;
+  d.k_cache = k_cache;
+  d.v_cache = v_cache;
+  d.k_scale = k_scale;
+  d.v_scale = v_scale;
+  d.block_table = block_table;
+  d.context_lens = context_lens;
+  d.cu_seqlens = cu_seqlens;
+  const size_t slots = (size_t)num_seqs * num_heads * plan.max_parts;
+  d.part_o = need ? static_cast<float*>(workspace) : nullptr;
+  d.part_ml = need ? static_cast<float*>(workspace) + slots * head_size : nullptr;
+  d.bt_stride = block_table_stride;
+  d.num_seqs = num_seqs;
+  d.num_heads = num_heads;
+  d.num_kv_heads = num_kv_heads;
+  d.window = sliding_window;
+  d.pb = plan.pb;
+  d.max_parts = plan.max_parts;
+  d.scale_log2 = scale_log2;
+  // Rows with one query token may exist unless every sequence provably has
+  // max_q_len > 1 tokens (the only case the host scalars can prove).
+  const bool any_single = !(has_chunks && (long long)num_q_tokens == (long long)num_seqs * max_q_len);
+  if (any_single) {
+    hipError_t e = pa::launch_decode(d, (int)q_dtype, (int)cache_dtype, head_size, hs);
+    if (e != hipSuccess) return hip_status(e, "decode launch (one-token rows)");
+  }
+  if (has_chunks) {
+    pa::PrefillArgs p{};
+    p.out = out;
+    p.query = query;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.block_table = block_table;
+    p.cu_seqlens = cu_seqlens;
+    p.context_lens = context_lens;
+    p.bt_stride = block_table_stride;
+    p.num_seqs = num_seqs;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.window = sliding_window;
+    p.scale_log2 = scale_log2;
+    // bound on sum over sequences with q_len > 1 of ceil(q_len / TQ)
+    const long long tq = pa::prefill_tokens_per_tile(group);
+    const long long long_seqs = std::min<long long>(num_seqs, num_q_tokens / 2);
+    const long long bound_a = long_seqs + (num_q_tokens + tq - 1) / tq;
+    const long long bound_b = long_seqs * ((max_q_len + tq - 1) / tq);
+    p.num_tiles = (int)std::min(bound_a, bound_b);
+    hipError_t e = pa::launch_prefill(p, (int)cache_dtype, head_size, hs);
+    if (e != hipSuccess) return hip_status(e, "prefill launch");
+  }
+  g_last_error.clear();
+  return PA_OK;
+}
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+// Device helpers shared by the paged-attention kernels (gfx950 / CDNA4).
+//
+// Element storage: fp32 as float, bf16 as its 16 bits (uint16_t), OCP e4m3fn
+// as a byte. bf16 pairs travel packed in one 32-bit register so that the
+// dot2 instruction (two bf16 products accumulated in fp32) can consume them
+// without unpacking.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+enum CacheKind { KF32 = 0, KBF16 = 1, KFP8 = 2 };
+
+template <int CK> struct CacheElem;
+template <> struct CacheElem<KF32> { typedef float T; static constexpr int bytes = 4; };
+template <> struct CacheElem<KBF16> { typedef uint16_t T; static constexpr int bytes = 2; };
+template <> struct CacheElem<KFP8> { typedef uint8_t T; static constexpr int bytes = 1; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (the compiler emits v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v;
+  v.x = (__bf16)lo;
+  v.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi for packed bf16 pairs, fp32 accumulate.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// Two e4m3fn bytes (bytes 0,1 or 2,3 of w) -> two floats, exact.
+__device__ __forceinline__ f32x2 fp8x2_lo(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+}
+__device__ __forceinline__ f32x2 fp8x2_hi(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+}
+// Four e4m3fn bytes -> two packed bf16 pairs (exact: every e4m3 value is a bf16 value).
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& p01, uint32_t& p23) {
+  f32x2 a = fp8x2_lo(w);
+  f32x2 b = fp8x2_hi(w);
+  p01 = pack_bf16x2(a.x, a.y);
+  p23 = pack_bf16x2(b.x, b.y);
+}
+
+// Eight e4m3fn bytes (two words) -> eight bf16 (four packed pairs).
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  uint32_t a, b, c, d;
+  fp8x4_to_bf16x4(w0, a, b);
+  fp8x4_to_bf16x4(w1, c, d);
+  return u32x4{a, b, c, d};
+}
+
+// ---- cross-lane reductions -------------------------------------------------
+// DPP row (16-lane) patterns: quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror,
+// row_mirror. After the first two a quad holds its total; half-mirror pairs
+// quad i with quad 1-i of each 8-lane half, mirror pairs the two halves.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_QP_1032 = 0xB1;
+constexpr int DPP_QP_2301 = 0x4E;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+// Sum over aligned groups of N lanes (N in {1,2,4,8,16,32,64}); every lane of
+// the group receives the total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<DPP_QP_1032>(x);
+  if constexpr (N >= 4) x += dpp<DPP_QP_2301>(x);
+  if constexpr (N >= 8) x += dpp<DPP_ROW_HALF_MIRROR>(x);
+  if constexpr (N >= 16) x += dpp<DPP_ROW_MIRROR>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Max / sum over lanes that share (lane % STRIDE) — i.e. across the 64/STRIDE
+// groups of STRIDE consecutive lanes. STRIDE is a power of two.
+template <int STRIDE>
+__device__ __forceinline__ float strided_max(float x) {
+  if constexpr (STRIDE <= 1) x = fmaxf(x, dpp<DPP_QP_1032>(x));
+  if constexpr (STRIDE <= 2) x = fmaxf(x, dpp<DPP_QP_2301>(x));
+  if constexpr (STRIDE <= 4) x = fmaxf(x, __shfl_xor(x, 4));
+  if constexpr (STRIDE <= 8) x = fmaxf(x, __shfl_xor(x, 8));
+  if constexpr (STRIDE <= 16) x = fmaxf(x, __shfl_xor(x, 16));
+  if constexpr (STRIDE <= 32) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+template <int STRIDE>
+__device__ __forceinline__ float strided_sum(float x) {
+  if constexpr (STRIDE <= 1) x += dpp<DPP_QP_1032>(x);
+  if constexpr (STRIDE <= 2) x += dpp<DPP_QP_2301>(x);
+  if constexpr (STRIDE <= 4) x += __shfl_xor(x, 4);
+  if constexpr (STRIDE <= 8) x += __shfl_xor(x, 8);
+  if constexpr (STRIDE <= 16) x += __shfl_xor(x, 16);
+  if constexpr (STRIDE <= 32) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// log2(e): scores are kept premultiplied by scale*log2(e) so that exp2 is used.
+constexpr float LOG2E = 1.4426950408889634f;
+
+}  // namespace pa

@@ -1,0 +1,81 @@
+// Internal interface between the C ABI layer (pa_api.cpp) and the kernel
+// launchers. Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// e4m3fn saturation before the hardware conversion: finite values are clamped
+// to +-448, NaN stays NaN.
+__device__ __forceinline__ float sat_e4m3(float x) {
+  return (x != x) ? x : fminf(fmaxf(x, -448.0f), 448.0f);
+}
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                    const float* k_scale, const float* v_scale,
+                                    const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                                    int head_size, int in_kind, int cache_kind, hipStream_t stream);
+
+// Split-K plan of the decode kernel: every sequence's key blocks are cut into
+// partitions of `pb` blocks; `max_parts` bounds the partitions of any
+// sequence. One partition means no partial results and no merge.
+struct DecodePlan {
+  int pb;
+  int max_parts;
+};
+DecodePlan plan_decode(int num_seqs, int max_context_len, int num_kv_heads, int sliding_window);
+size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int num_heads, int head_size);
+
+struct DecodeArgs {
+  void* out;
+  const void* query;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int* block_table;
+  const int* context_lens;
+  const int* cu_seqlens;  // null: pure decode (query row s); else rows with q_len == 1 only
+  float* part_o;          // [num_seqs][num_heads][max_parts][head_size]
+  float* part_ml;         // [num_seqs][num_heads][max_parts][2]: running max (log2 units), sum
+  int bt_stride;
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int window;
+  int pb;
+  int max_parts;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+// q_kind / cache_kind: 0 = f32, 1 = bf16, 2 = fp8 e4m3fn.
+hipError_t launch_decode(const DecodeArgs& args, int q_kind, int cache_kind, int head_size,
+                         hipStream_t stream);
+bool decode_supported(int q_kind, int cache_kind, int head_size, int group);
+
+struct PrefillArgs {
+  void* out;
+  const void* query;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int* block_table;
+  const int* cu_seqlens;
+  const int* context_lens;
+  int bt_stride;
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int window;
+  int num_tiles;  // grid bound on (sequence, query tile) pairs
+  float scale_log2;
+};
+int prefill_tokens_per_tile(int group);
+hipError_t launch_prefill(const PrefillArgs& args, int cache_kind, int head_size, hipStream_t stream);
+bool prefill_supported(int q_kind, int cache_kind, int head_size, int group);
+
+}  // namespace pa

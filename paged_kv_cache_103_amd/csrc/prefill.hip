@@ -1,0 +1,379 @@
+// Chunked-prefill paged attention on gfx950 matrix cores (MFMA).
+//
+// What it computes: every query row of a chunk longer than one token attends
+// causally to its sequence's cached keys, read through the block table: the
+// chunk sits on top of a cached prefix, and query row r of a chunk of q_len
+// rows in a context of ctx tokens is at position ctx - q_len + r
+// ("大模型推理优化学习笔记", "Chunked Prefill"; "从静态批处理到状态化推理集群",
+// "Chunked prefill：在共置引擎里治理阶段干扰"). Prefill reuses each K/V row across
+// many queries and is compute-bound ("大模型推理优化学习笔记", "计算密集与访存密集"),
+// so QK^T and PV run on MFMA with fp32 accumulation.
+//
+// Tiling (one workgroup = 4 waves):
+//  * a tile is 128 query columns of one KV head: 128/G tokens x the G query
+//    heads of the group, so each staged K/V tile serves the whole group;
+//  * keys advance 32 at a time (two 16-token blocks), gathered through the
+//    block table into LDS — K as [32][head_size] (padded rows), V as the
+//    cache's own transposed [head_size][16] block tiles — with the next two
+//    blocks loaded into registers while the current ones are used;
+//  * each wave owns 32 columns and computes S^T = K Q^T (16x16x32 bf16 MFMA,
+//    queries as the B operand held in registers), so the score accumulator
+//    of a lane holds 4 keys x 1 column; exactly that layout is the B operand
+//    of O^T = V^T P^T, so probabilities never leave the lane, and the column
+//    statistics (running max and sum) need no shuffles to rescale O^T;
+//  * causal / window masks are applied only to key tiles that cross a
+//    column's boundary; keys past the context are zeroed in V while staging.
+//
+// Tiles are handed out heaviest-first (the last query tile of a sequence sees
+// the most keys), and the KV head is the fastest-varying part of the
+// workgroup index so that the tiles of one head land on the same XCD.
+#include <math.h>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+typedef __bf16 mfma_bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mfma_bf16x8, a),
+                                                  __builtin_bit_cast(mfma_bf16x8, b), c, 0, 0, 0);
+}
+
+template <int CK, int D>
+struct PrefillShape {
+  static constexpr int KROW = D + 8;              // LDS K row (bf16 elements), padded by 16 bytes
+  static constexpr int K_LDS = 32 * KROW;         // bf16 elements of one K tile
+  static constexpr int V_LDS = 2 * D * 16;        // two transposed V block tiles
+  static constexpr int BUF = K_LDS + V_LDS;       // one stage
+  static constexpr int E = CacheElem<CK>::bytes;
+  static constexpr int BLK_BYTES = 16 * D * E;    // global bytes of one (block, head) tile
+  // 16-byte global chunks per thread per tile (K and V each): 2 blocks
+  static constexpr int CHUNKS = (2 * BLK_BYTES / 16 + 255) / 256;
+};
+
+template <int CK, int D, int G>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  using S = PrefillShape<CK, D>;
+  constexpr int TQ = 128 / G;  // tokens per tile
+  constexpr int DS = D / 32;   // MFMA k-steps over head_size
+  constexpr int DT = D / 16;   // 16-row tiles of head_size in O^T
+  constexpr int E = S::E;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * S::BUF];
+  __shared__ int sh_scan[256];
+  __shared__ int sh_found[3];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = blockIdx.x % a.num_kv_heads;
+  const int t = blockIdx.x / a.num_kv_heads;
+
+  // ---- which (sequence, query tile) this workgroup owns ----
+  if (tid == 0) { sh_found[0] = -1; sh_found[1] = 0; sh_found[2] = 0; }
+  __syncthreads();
+  int running = 0;
+  for (int base = 0; base < a.num_seqs; base += 256) {
+    const int s = base + tid;
+    int n = 0;
+    if (s < a.num_seqs) {
+      const int ql = a.cu_seqlens[s + 1] - a.cu_seqlens[s];
+      n = ql > 1 ? (ql + TQ - 1) / TQ : 0;
+    }
+    sh_scan[tid] = n;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int v = tid >= off ? sh_scan[tid - off] : 0;
+      __syncthreads();
+      sh_scan[tid] += v;
+      __syncthreads();
+    }
+    const int incl = sh_scan[tid];
+    if (n > 0 && t >= running + incl - n && t < running + incl) {
+      sh_found[0] = s;
+      sh_found[1] = t - (running + incl - n);
+      sh_found[2] = n;
+    }
+    running += sh_scan[255];
+    __syncthreads();
+    if (sh_found[0] >= 0) break;
+  }
+  const int s = sh_found[0];
+  if (s < 0) return;
+  const int qt = sh_found[2] - 1 - sh_found[1];  // heaviest tile first
+
+  const int q0 = a.cu_seqlens[s];
+  const int qlen = a.cu_seqlens[s + 1] - q0;
+  const int ctx = a.context_lens[s];
+  const int tok0 = qt * TQ;
+  const int ntok = min(TQ, qlen - tok0);
+  const int qpos_first = ctx - qlen + tok0;
+  const int qpos_last = qpos_first + ntok - 1;
+  const int lo_first = a.window > 0 ? max(0, qpos_first - a.window + 1) : 0;
+  const int b_last = (ctx - 1) >> 4;
+  const int* bt = a.block_table + (size_t)s * a.bt_stride;
+
+  // ---- queries of this wave's 32 columns as B operands (registers) ----
+  u32x4 qf[2][DS];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int col = wave * 32 + ct * 16 + (lane & 15);
+    const int tok = col / G, h = col % G;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      if (tok < ntok) {
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) +
+                             ((size_t)(q0 + tok0 + tok) * a.num_heads + g * G + h) * D + ds * 32 +
+                             (lane >> 4) * 8;
+        qf[ct][ds] = load16(qp);
+      } else {
+        qf[ct][ds] = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+
+  f32x4 o[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) o[dt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+
+  // ---- staging: global (two blocks) -> registers -> LDS ----
+  const size_t head_stride = (size_t)a.num_kv_heads * S::BLK_BYTES;
+  const uint8_t* kcache = reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)g * S::BLK_BYTES;
+  const uint8_t* vcache = reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * S::BLK_BYTES;
+  u32x4 kreg[S::CHUNKS], vreg[S::CHUNKS];
+
+  auto load_tile = [&](int j) {
+    const int b0 = j >> 4;
+#pragma unroll
+    for (int r = 0; r < S::CHUNKS; ++r) {
+      const int c = tid + 256 * r;                 // 16-byte chunk within the two blocks
+      const int blk = c / (S::BLK_BYTES / 16);     // 0 or 1
+      const int off = (c % (S::BLK_BYTES / 16)) * 16;
+      if (c < 2 * S::BLK_BYTES / 16 && b0 + blk <= b_last) {
+        const size_t phys = (size_t)bt[b0 + blk];
+        kreg[r] = load16(kcache + phys * head_stride + off);
+        vreg[r] = load16(vcache + phys * head_stride + off);
+      } else {
+        kreg[r] = u32x4{0, 0, 0, 0};
+        vreg[r] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](int j, uint16_t* buf) {
+    uint16_t* ks = buf;
+    uint16_t* vs = buf + S::K_LDS;
+#pragma unroll
+    for (int r = 0; r < S::CHUNKS; ++r) {
+      const int c = tid + 256 * r;
+      if (c >= 2 * S::BLK_BYTES / 16) continue;
+      const int blk = c / (S::BLK_BYTES / 16);
+      const int off = (c % (S::BLK_BYTES / 16)) * 16;  // byte offset inside the block tile
+      // K: element offset off/E inside [16][D] -> LDS row blk*16 + row
+      const int kel = off / E;
+      const int krow = blk * 16 + kel / D, kcol = kel % D;
+      // V^T: element offset inside [D][16] -> d row, first key
+      const int vel = off / E;
+      const int vd = vel / 16, vkey = vel % 16;
+      const int key_base = j + blk * 16 + vkey;  // key position of the chunk's first element
+      if constexpr (CK == KBF16) {
+        *reinterpret_cast<u32x4*>(ks + krow * S::KROW + kcol) = kreg[r];
+        u32x4 v = vreg[r];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t mlo = (key_base + 2 * e < ctx) ? 0x0000ffffu : 0u;
+          const uint32_t mhi = (key_base + 2 * e + 1 < ctx) ? 0xffff0000u : 0u;
+          v[e] &= (mlo | mhi);
+        }
+        *reinterpret_cast<u32x4*>(vs + blk * D * 16 + vd * 16 + vkey) = v;
+      } else {
+        // fp8: 16 bytes -> 16 bf16 (exact), written as two 16-byte pieces
+        const u32x4 k0 = fp8x8_to_bf16x8(kreg[r][0], kreg[r][1]);
+        const u32x4 k1 = fp8x8_to_bf16x8(kreg[r][2], kreg[r][3]);
+        *reinterpret_cast<u32x4*>(ks + krow * S::KROW + kcol) = k0;
+        *reinterpret_cast<u32x4*>(ks + krow * S::KROW + kcol + 8) = k1;
+        u32x4 v0 = fp8x8_to_bf16x8(vreg[r][0], vreg[r][1]);
+        u32x4 v1 = fp8x8_to_bf16x8(vreg[r][2], vreg[r][3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v0[e] &= ((key_base + 2 * e < ctx) ? 0x0000ffffu : 0u) | ((key_base + 2 * e + 1 < ctx) ? 0xffff0000u : 0u);
+          v1[e] &= ((key_base + 8 + 2 * e < ctx) ? 0x0000ffffu : 0u) |
+                   ((key_base + 8 + 2 * e + 1 < ctx) ? 0xffff0000u : 0u);
+        }
+        *reinterpret_cast<u32x4*>(vs + blk * D * 16 + vd * 16 + vkey) = v0;
+        *reinterpret_cast<u32x4*>(vs + blk * D * 16 + vd * 16 + vkey + 8) = v1;
+      }
+    }
+  };
+
+  const int jstart = (lo_first >> 5) << 5;
+  const int jend = qpos_last;  // last key any column of the tile can see
+  int cur = 0;
+  load_tile(jstart);
+  store_tile(jstart, lds);
+  __syncthreads();
+
+  const int col_l = wave * 32 + (lane & 15);  // column of ct = 0; ct = 1 adds 16
+  for (int j = jstart; j <= jend; j += 32) {
+    const bool more = j + 32 <= jend;
+    if (more) load_tile(j + 32);
+
+    const uint16_t* ks = lds + cur * S::BUF;
+    const uint16_t* vs = ks + S::K_LDS;
+
+    // ---- S^T = K Q^T : 2 key tiles x 2 column tiles ----
+    f32x4 sc[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      sc[kt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sc[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + (kt * 16 + (lane & 15)) * S::KROW +
+                                                          ds * 32 + (lane >> 4) * 8);
+        sc[kt][0] = mfma16x16x32(kf, qf[0][ds], sc[kt][0]);
+        sc[kt][1] = mfma16x16x32(kf, qf[1][ds], sc[kt][1]);
+      }
+    }
+
+    // ---- scale, mask, online softmax per column ----
+    float ksc[2] = {a.scale_log2, a.scale_log2};
+    float vsc[2] = {1.f, 1.f};
+    if constexpr (CK == KFP8) {
+      const int b0 = j >> 4;
+      ksc[0] *= a.k_scale[bt[b0]];
+      vsc[0] = a.v_scale[bt[b0]];
+      if (b0 + 1 <= b_last) {
+        ksc[1] *= a.k_scale[bt[b0 + 1]];
+        vsc[1] = a.v_scale[bt[b0 + 1]];
+      }
+    }
+    const bool need_mask = (j + 31 > qpos_first) || (a.window > 0 && j < qpos_last - a.window + 1);
+    u32x4 pf[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int col = col_l + ct * 16;
+      const int qpos = qpos_first + col / G;
+      float x[2][4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = sc[kt][ct][r] * ksc[kt];
+          if (need_mask) {
+            const int kp = j + kt * 16 + (lane >> 4) * 4 + r;
+            const bool ok = kp <= qpos && kp < ctx && (a.window <= 0 || kp > qpos - a.window);
+            v = ok ? v : -INFINITY;
+          }
+          x[kt][r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = strided_max<16>(tmax);
+      const float mn = fmaxf(m[ct], tmax);
+      const float base = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = __builtin_amdgcn_exp2f(m[ct] - base);
+      m[ct] = mn;
+      float ps = 0.f;
+      float pv[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(x[kt][r] - base);
+          ps += p;
+          pv[kt][r] = p * vsc[kt];
+        }
+      lsum[ct] = lsum[ct] * alpha + ps;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        o[dt][ct][0] *= alpha; o[dt][ct][1] *= alpha; o[dt][ct][2] *= alpha; o[dt][ct][3] *= alpha;
+      }
+      pf[ct][0] = pack_bf16x2(pv[0][0], pv[0][1]);
+      pf[ct][1] = pack_bf16x2(pv[0][2], pv[0][3]);
+      pf[ct][2] = pack_bf16x2(pv[1][0], pv[1][1]);
+      pf[ct][3] = pack_bf16x2(pv[1][2], pv[1][3]);
+    }
+
+    // ---- O^T += V^T P^T over the 32 keys ----
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = dt * 16 + (lane & 15);
+      const int k4 = (lane >> 4) * 4;
+      const uint2 v0 = *reinterpret_cast<const uint2*>(vs + d * 16 + k4);           // block 0
+      const uint2 v1 = *reinterpret_cast<const uint2*>(vs + D * 16 + d * 16 + k4);  // block 1
+      const u32x4 vf = u32x4{v0.x, v0.y, v1.x, v1.y};
+      o[dt][0] = mfma16x16x32(vf, pf[0], o[dt][0]);
+      o[dt][1] = mfma16x16x32(vf, pf[1], o[dt][1]);
+    }
+
+    if (more) store_tile(j + 32, lds + (cur ^ 1) * S::BUF);
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  // ---- normalise and write this wave's columns ----
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const float L = strided_sum<16>(lsum[ct]);
+    const float inv = 1.f / L;
+    const int col = col_l + ct * 16;
+    const int tok = col / G, h = col % G;
+    if (tok < ntok) {
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) +
+                     ((size_t)(q0 + tok0 + tok) * a.num_heads + g * G + h) * D + (lane >> 4) * 4;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        uint2 w;
+        w.x = pack_bf16x2(o[dt][ct][0] * inv, o[dt][ct][1] * inv);
+        w.y = pack_bf16x2(o[dt][ct][2] * inv, o[dt][ct][3] * inv);
+        *reinterpret_cast<uint2*>(op + dt * 16) = w;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+int prefill_tokens_per_tile(int group) { return 128 / group; }
+
+bool prefill_supported(int q_kind, int cache_kind, int head_size, int group) {
+  if (head_size != 64 && head_size != 128) return false;
+  if (!(group == 1 || group == 2 || group == 4 || group == 8 || group == 16)) return false;
+  return q_kind == KBF16 && (cache_kind == KBF16 || cache_kind == KFP8);
+}
+
+template <int CK, int D, int G>
+static hipError_t run_prefill(const PrefillArgs& a, hipStream_t st) {
+  const unsigned blocks = (unsigned)a.num_tiles * (unsigned)a.num_kv_heads;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((prefill_kernel<CK, D, G>), dim3(blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int CK, int D>
+static hipError_t run_prefill_g(const PrefillArgs& a, int G, hipStream_t st) {
+  switch (G) {
+    case 1: return run_prefill<CK, D, 1>(a, st);
+    case 2: return run_prefill<CK, D, 2>(a, st);
+    case 4: return run_prefill<CK, D, 4>(a, st);
+    case 8: return run_prefill<CK, D, 8>(a, st);
+    case 16: return run_prefill<CK, D, 16>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int cache_kind, int head_size, hipStream_t stream) {
+  const int G = a.num_heads / a.num_kv_heads;
+  if (cache_kind == KBF16) {
+    if (head_size == 64) return run_prefill_g<KBF16, 64>(a, G, stream);
+    if (head_size == 128) return run_prefill_g<KBF16, 128>(a, G, stream);
+  } else if (cache_kind == KFP8) {
+    if (head_size == 64) return run_prefill_g<KFP8, 64>(a, G, stream);
+    if (head_size == 128) return run_prefill_g<KFP8, 128>(a, G, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa
