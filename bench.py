@@ -1,0 +1,266 @@
+"""Benchmark of the paged-KV hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--extra] [--no-cpu-baseline]
+
+Headline (the JSON line on stdout): decode KV GB/s on the Llama-3-8B-shaped
+decode batch (64 sequences, contexts U{1024..8192}, 32 query / 8 KV heads,
+head size 128, bf16, 16-token blocks). One step = the KV write of the 64 new
+tokens + paged decode over every sequence, inputs resident in HBM.
+value = algorithmic K+V bytes read per step / step time.
+
+Beside it in the same line: the mixed chunked-prefill step (192 decode rows +
+one 2048-token chunk on a 65536-token prefix, 2240 new tokens written first)
+in new tokens/s, the roofline of the decode kernel, the prefill chunk's
+MFMA throughput, and the CPU oracle timed on a bounded sample.
+Everything is one attention layer.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+
+METRIC = "paged-attn decode KV GB/s (% HBM peak); mixed-step tokens/s on 1 MI355X"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workspace(pa, torch, b, prefill=False):
+    if prefill:
+        n = pa.prefill_workspace_bytes(b.num_seqs, b.num_q_tokens, b.max_q_len, b.max_context_len,
+                                       b.num_heads, b.num_kv_heads, b.head_size, b.sliding_window)
+    else:
+        n = pa.decode_workspace_bytes(b.num_seqs, b.max_context_len, b.num_heads, b.num_kv_heads,
+                                      b.head_size, b.sliding_window)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+
+
+def decode_step_fns(pa, torch, b):
+    m = b.meta("cuda")
+    out = torch.empty_like(b.query)
+    ws = workspace(pa, torch, b)
+
+    def write():
+        pa.reshape_and_cache(b.new_key, b.new_value, b.k_cache, b.v_cache, m["slot_mapping"], b.k_scale,
+                             b.v_scale)
+
+    def attend():
+        pa.decode(out, b.query, b.k_cache, b.v_cache, m["block_table"], m["context_lens"],
+                  b.max_context_len, b.scale, b.k_scale, b.v_scale, b.sliding_window, ws)
+
+    return write, attend
+
+
+def prefill_step_fns(pa, torch, b):
+    m = b.meta("cuda")
+    out = torch.empty_like(b.query)
+    ws = workspace(pa, torch, b, prefill=True)
+
+    def write():
+        pa.reshape_and_cache(b.new_key, b.new_value, b.k_cache, b.v_cache, m["slot_mapping"], b.k_scale,
+                             b.v_scale)
+
+    def attend():
+        pa.prefill_chunk(out, b.query, b.k_cache, b.v_cache, m["block_table"], m["cu_seqlens"],
+                         m["context_lens"], b.max_q_len, b.max_context_len, b.scale, b.k_scale,
+                         b.v_scale, b.sliding_window, ws)
+
+    return write, attend
+
+
+def time_steps(torch, write, attend, steps, warmup):
+    """Warm up, then time exactly `steps` steps (write + attend) between two
+    synchronisations; HIP events on the launch stream bracket every attend
+    call. Returns (ms per step, mean ms of the attend call)."""
+    for _ in range(warmup):
+        write()
+        attend()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        write()
+        ev[i][0].record()
+        attend()
+        ev[i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - wall0) * 1e3 / steps
+    step_ms = t0.elapsed_time(t1) / steps
+    attend_ms = sum(a.elapsed_time(c) for a, c in ev) / steps
+    return step_ms, attend_ms, wall
+
+
+def causal_flops(b):
+    """Algorithmic MFMA flops of the chunks longer than one token: 4*d per
+    visible (query, key) pair per query head (QK^T and PV)."""
+    pairs = 0
+    for ctx, ql in zip(b.context_lens.tolist(), b.q_lens.tolist()):
+        if ql <= 1:
+            continue
+        for r in range(ql):
+            p = ctx - ql + r
+            lo = 0 if b.sliding_window <= 0 else max(0, p - b.sliding_window + 1)
+            pairs += p - lo + 1
+    return 4.0 * b.head_size * pairs * b.num_heads
+
+
+def cpu_baseline(b, budget_s=15.0):
+    """The oracle, as it stands, on a bounded sample of the batch: whole
+    sequences in order until the budget is spent. Reported in the same unit as
+    the GPU (K+V GB/s of the sequences it finished)."""
+    import numpy as np
+    from tests.helpers import oracle_rows
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    done, secs, nbytes = 0, 0.0, 0
+    e = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}[b.cache_dtype]
+    for s in range(b.num_seqs):
+        t = time.perf_counter()
+        oracle_rows(b, [s])
+        secs += time.perf_counter() - t
+        done += 1
+        nbytes += int(b.context_lens[s]) * b.num_kv_heads * b.head_size * 2 * e
+        if secs > budget_s:
+            break
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {b.num_seqs} sequences of the same batch (all heads), {secs:.1f} s; "
+                      f"includes the oracle's own host gather through the block table, not the D2H copy"}
+
+
+def run_config(pa, torch, W, name, steps, warmup):
+    b = W.make_config(name, device="cuda")
+    torch.cuda.synchronize()
+    prefill = b.max_q_len > 1
+    write, attend = (prefill_step_fns if prefill else decode_step_fns)(pa, torch, b)
+    step_ms, attend_ms, wall = time_steps(torch, write, attend, steps, warmup)
+    res = {"config": name, "step_ms": step_ms, "attend_ms": attend_ms, "wall_ms": wall,
+           "kv_bytes": b.kv_bytes_read(), "unique_kv_bytes": b.unique_kv_bytes_read(),
+           "new_tokens": b.num_q_tokens}
+    res["kv_gbs_step"] = res["kv_bytes"] / (step_ms * 1e-3) / 1e9
+    res["kv_gbs_attend"] = res["kv_bytes"] / (attend_ms * 1e-3) / 1e9
+    res["unique_gbs_attend"] = res["unique_kv_bytes"] / (attend_ms * 1e-3) / 1e9
+    res["tokens_per_s"] = b.num_q_tokens / (step_ms * 1e-3)
+    return b, res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--extra", action="store_true", help="also time the other named configurations (stderr)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from paged_kv_cache_103_amd import _lib as pa
+    from paged_kv_cache_103_amd import workloads as W
+
+    pa.load()
+    torch.cuda.set_device(0)
+
+    # ---- headline: decode on the Llama-3-8B-shaped batch ----
+    b, dec = run_config(pa, torch, W, "llama8b_decode", args.steps, args.warmup)
+    log(f"llama8b_decode: step {dec['step_ms']*1e3:.1f} us, pa_decode {dec['attend_ms']*1e3:.1f} us, "
+        f"{dec['kv_gbs_attend']:.0f} GB/s in pa_decode, {dec['kv_gbs_step']:.0f} GB/s per step")
+    cpu = None if args.no_cpu_baseline else cpu_baseline(b)
+    del b
+    torch.cuda.empty_cache()
+
+    # ---- mixed chunked-prefill step ----
+    mb, mix = run_config(pa, torch, W, "mixed_step", max(5, args.steps // 5), max(2, args.warmup // 2))
+    log(f"mixed_step: step {mix['step_ms']:.3f} ms -> {mix['tokens_per_s']:.0f} new tokens/s")
+    # the 2048-token chunk alone (prefill kernel only) for its MFMA rate
+    import copy
+    chunk = copy.copy(mb)
+    chunk.device_meta = {}
+    s = mb.num_seqs - 1
+    cu = mb.cu_seqlens
+    chunk.context_lens = mb.context_lens[s:s + 1].copy()
+    chunk.q_lens = mb.q_lens[s:s + 1].copy()
+    chunk.block_table = mb.block_table[s:s + 1].copy()
+    chunk.query = mb.query[cu[s]:cu[s + 1]].contiguous()
+    chunk.slot_mapping = mb.slot_mapping[cu[s]:cu[s + 1]].copy()
+    chunk.new_key = mb.new_key[cu[s]:cu[s + 1]].contiguous()
+    chunk.new_value = mb.new_value[cu[s]:cu[s + 1]].contiguous()
+    _, pre_attend = prefill_step_fns(pa, torch, chunk)
+    _, pre_ms, _ = time_steps(torch, lambda: None, pre_attend, max(5, args.steps // 5), 2)
+    flops = causal_flops(chunk)
+    pre_tflops = flops / (pre_ms * 1e-3) / 1e12
+    log(f"prefill chunk alone: {pre_ms:.3f} ms, {pre_tflops:.0f} TFLOP/s "
+        f"({100 * pre_tflops / BF16_MFMA_PEAK_TFLOPS:.1f}% of bf16 MFMA peak)")
+    del mb, chunk
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if args.extra:
+        for name in ("tiny_decode", "agentic_decode", "fp8_decode", "fp8_swa128"):
+            eb, r = run_config(pa, torch, W, name, max(5, args.steps // 2), args.warmup)
+            extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+            log(f"{name}: pa_decode {r['attend_ms']*1e3:.1f} us, {r['kv_gbs_attend']:.0f} GB/s logical, "
+                f"{r['unique_gbs_attend']:.0f} GB/s unique")
+            del eb
+            torch.cuda.empty_cache()
+
+    achieved = dec["kv_gbs_attend"]
+    line = {
+        "metric": METRIC,
+        "value": round(dec["kv_gbs_step"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama8b_decode: 64 sequences, context U{1024..8192}, 32 query / 8 KV "
+                               "heads, head 128, bf16 K/V and queries, 16-token blocks, one layer; "
+                               "step = KV write of 64 tokens + paged decode",
+                   "kv_bytes_per_step": dec["kv_bytes"], "pct_hbm_peak": round(100 * dec["kv_gbs_step"] / HBM_PEAK_GBS, 2)},
+        "roofline": {"bound": "hbm", "kernel": "pa_decode (partition kernel + merge kernel)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "mixed_step": {"value": round(mix["tokens_per_s"], 1), "unit": "tokens/s",
+                       "ms_per_step": round(mix["step_ms"], 5),
+                       "workload": "192 decode rows (context U{4096..32768}) + one 2048-token chunk on a "
+                                   "65536-token prefix; 2240 new tokens written; 32/8 heads, d128, bf16",
+                       "prefill_chunk_only_ms": round(pre_ms, 5), "prefill_tflops": round(pre_tflops, 2),
+                       "prefill_frac_bf16_peak": round(pre_tflops / BF16_MFMA_PEAK_TFLOPS, 4)},
+    }
+    if extra:
+        line["extra"] = extra
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,7 +23,10 @@
 //    選擇與 DEP 轉折");
 //  * PV: probabilities go through a few bytes of LDS from the key-row lanes
 //    to the value-row lanes; the transposed V tile gives bf16 pairs along keys
-//    that meet the probability pairs in dot2;
+//    that meet the probability pairs in dot2. A probability is sent as two
+//    bf16 numbers (hi = bf16(p), lo = bf16(p - hi)) so that PV keeps about 16
+//    significant bits of p: one bf16 rounding of p alone would move an output
+//    dominated by a few keys by up to 2^-8 |v|;
 //  * the 4 waves merge through LDS; a sequence with several partitions writes
 //    (max, sum, unnormalised output) per partition and a second kernel merges
 //    them with the same correction factors (flash-decoding split).
@@ -56,8 +59,11 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
   constexpr int NI = S::NI, LPR = S::LPR, RPI = S::RPI, EPL = S::EPL, E = S::E;
   constexpr bool F32 = (CK == KF32);
   // probabilities exchanged through LDS: fp32 for an fp32 cache, bf16 otherwise
+  // bf16 probabilities are carried as hi + lo (p = hi + lo to ~2^-16), so
+  // the PV products keep nearly fp32 precision while still using dot2
   constexpr int PBYTES = F32 ? 4 : 2;
-  __shared__ __attribute__((aligned(16))) uint8_t p_lds[4][G][16 * PBYTES];
+  constexpr int PLANES = F32 ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[4][PLANES][G][16 * PBYTES];
   __shared__ float w_m[4][G], w_l[4][G];
   __shared__ float w_o[4][G][D];
 
@@ -217,9 +223,11 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
           const int t = i * RPI + lane / LPR;
           const float pv = p[i][h] * vscale;
           if constexpr (F32) {
-            reinterpret_cast<float*>(p_lds[wave][h])[t] = pv;
+            reinterpret_cast<float*>(p_lds[wave][0][h])[t] = pv;
           } else {
-            reinterpret_cast<uint16_t*>(p_lds[wave][h])[t] = f32_to_bf16(pv);
+            const uint16_t hi = f32_to_bf16(pv);
+            reinterpret_cast<uint16_t*>(p_lds[wave][0][h])[t] = hi;
+            reinterpret_cast<uint16_t*>(p_lds[wave][1][h])[t] = f32_to_bf16(pv - bf16_to_f32(hi));
           }
         }
       }
@@ -250,18 +258,27 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       if constexpr (CK == KBF16) {
-        const u32x4 pp = *reinterpret_cast<const u32x4*>(p_lds[wave][h] + kk0 * 2);
+        const u32x4 ph = *reinterpret_cast<const u32x4*>(p_lds[wave][0][h] + kk0 * 2);
+        const u32x4 pl = *reinterpret_cast<const u32x4*>(p_lds[wave][1][h] + kk0 * 2);
 #pragma unroll
         for (int n = 0; n < NI; ++n) {
           float x = acc[n][h];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) x = dot2_bf16(pp[j], vr[n][j], x);
+          for (int j = 0; j < 4; ++j) {
+            x = dot2_bf16(ph[j], vr[n][j], x);
+            x = dot2_bf16(pl[j], vr[n][j], x);
+          }
           acc[n][h] = x;
         }
       } else if constexpr (CK == KFP8) {
-        const u32x4 pa = *reinterpret_cast<const u32x4*>(p_lds[wave][h]);
-        const u32x4 pb = *reinterpret_cast<const u32x4*>(p_lds[wave][h] + 16);
-        const uint32_t pp[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+        uint32_t ph[8], pl[8];
+#pragma unroll
+        for (int q4 = 0; q4 < 2; ++q4) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(p_lds[wave][0][h] + 16 * q4);
+          const u32x4 c = *reinterpret_cast<const u32x4*>(p_lds[wave][1][h] + 16 * q4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) { ph[4 * q4 + j] = a[j]; pl[4 * q4 + j] = c[j]; }
+        }
 #pragma unroll
         for (int n = 0; n < NI; ++n) {
           float x = acc[n][h];
@@ -269,13 +286,15 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
           for (int j = 0; j < 4; ++j) {
             uint32_t v01, v23;
             fp8x4_to_bf16x4(vr[n][j], v01, v23);
-            x = dot2_bf16(pp[2 * j], v01, x);
-            x = dot2_bf16(pp[2 * j + 1], v23, x);
+            x = dot2_bf16(ph[2 * j], v01, x);
+            x = dot2_bf16(pl[2 * j], v01, x);
+            x = dot2_bf16(ph[2 * j + 1], v23, x);
+            x = dot2_bf16(pl[2 * j + 1], v23, x);
           }
           acc[n][h] = x;
         }
       } else {
-        const f32x4 pp = *reinterpret_cast<const f32x4*>(p_lds[wave][h] + kk0 * 4);
+        const f32x4 pp = *reinterpret_cast<const f32x4*>(p_lds[wave][0][h] + kk0 * 4);
 #pragma unroll
         for (int n = 0; n < NI; ++n) {
           float x = acc[n][h];

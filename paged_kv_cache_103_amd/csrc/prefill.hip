@@ -21,6 +21,9 @@
 //    of a lane holds 4 keys x 1 column; exactly that layout is the B operand
 //    of O^T = V^T P^T, so probabilities never leave the lane, and the column
 //    statistics (running max and sum) need no shuffles to rescale O^T;
+//  * P enters PV as two bf16 operands (hi = bf16(p), lo = bf16(p - hi)), two
+//    MFMAs per tile: a single bf16 rounding of p would move an output that a
+//    few keys dominate by up to 2^-8 |v|, beyond the parity tolerance;
 //  * causal / window masks are applied only to key tiles that cross a
 //    column's boundary; keys past the context are zeroed in V while staging.
 //
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       }
     }
     const bool need_mask = (j + 31 > qpos_first) || (a.window > 0 && j < qpos_last - a.window + 1);
-    u32x4 pf[2];
+    u32x4 pf[2], pg[2];  // P^T as bf16 hi and lo parts
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const int col = col_l + ct * 16;
@@ -291,10 +294,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       for (int dt = 0; dt < DT; ++dt) {
         o[dt][ct][0] *= alpha; o[dt][ct][1] *= alpha; o[dt][ct][2] *= alpha; o[dt][ct][3] *= alpha;
       }
-      pf[ct][0] = pack_bf16x2(pv[0][0], pv[0][1]);
-      pf[ct][1] = pack_bf16x2(pv[0][2], pv[0][3]);
-      pf[ct][2] = pack_bf16x2(pv[1][0], pv[1][1]);
-      pf[ct][3] = pack_bf16x2(pv[1][2], pv[1][3]);
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const float a0 = pv[q2 >> 1][(q2 & 1) * 2], a1 = pv[q2 >> 1][(q2 & 1) * 2 + 1];
+        const uint32_t hi = pack_bf16x2(a0, a1);
+        pf[ct][q2] = hi;
+        pg[ct][q2] = pack_bf16x2(a0 - bf16_lo(hi), a1 - bf16_hi(hi));
+      }
     }
 
     // ---- O^T += V^T P^T over the 32 keys ----
@@ -306,7 +312,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       const uint2 v1 = *reinterpret_cast<const uint2*>(vs + D * 16 + d * 16 + k4);  // block 1
       const u32x4 vf = u32x4{v0.x, v0.y, v1.x, v1.y};
       o[dt][0] = mfma16x16x32(vf, pf[0], o[dt][0]);
+      o[dt][0] = mfma16x16x32(vf, pg[0], o[dt][0]);
       o[dt][1] = mfma16x16x32(vf, pf[1], o[dt][1]);
+      o[dt][1] = mfma16x16x32(vf, pg[1], o[dt][1]);
     }
 
     if (more) store_tile(j + 32, lds + (cur ^ 1) * S::BUF);
