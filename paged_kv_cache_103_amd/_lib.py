@@ -15,7 +15,7 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "lib", "libpa.so")
+LIB_PATH = os.environ.get("PA_LIB_PATH") or os.path.join(_HERE, "lib", "libpa.so")
 
 PA_OK = 0
 PA_ERR_INVALID_ARGUMENT = 1

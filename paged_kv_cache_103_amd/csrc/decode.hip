@@ -35,6 +35,8 @@
 // conversion; the block's K scale multiplies the score and the V scale the
 // probability used in PV (the running sum keeps the unscaled one).
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -401,11 +403,21 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     const float w = (p < nparts) ? __builtin_amdgcn_exp2f(ml[2 * p] - M) : 0.f;
     if (p < nparts) L += ml[2 * p + 1] * w;
     const int cnt = min(64, nparts - p0);
-    for (int j = 0; j < cnt; ++j) {
-      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
-      const float* row = po + (size_t)(p0 + j) * D;
+    // eight partitions' rows in flight at a time
+    for (int j0 = 0; j0 < cnt; j0 += 8) {
+      float v[8][DL];
 #pragma unroll
-      for (int k = 0; k < DL; ++k) o[k] = fmaf(wj, row[k * 64 + lane], o[k]);
+      for (int u = 0; u < 8; ++u) {
+        const float* row = po + (size_t)(p0 + j0 + u) * D;
+#pragma unroll
+        for (int k = 0; k < DL; ++k) v[u][k] = (j0 + u < cnt) ? row[k * 64 + lane] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), (j0 + u) & 63));
+#pragma unroll
+        for (int k = 0; k < DL; ++k) o[k] = fmaf(wj, v[u][k], o[k]);
+      }
     }
   }
   L = strided_sum<1>(L);
@@ -430,13 +442,18 @@ DecodePlan plan_decode(int num_seqs, int max_context_len, int num_kv_heads, int 
   if (max_blocks < 1) max_blocks = 1;
   // Largest partition (16..256 blocks) that still leaves enough work items
   // to fill the chip: about 16 (sequence, head, partition) items per CU,
-  // assuming contexts average half the maximum.
+  // assuming contexts average half the maximum. PA_DECODE_PB (a power of two
+  // >= 2) overrides the choice for measurements.
   const long long target = 4096;
   int pb = 16;
   for (int cand = 256; cand >= 16; cand /= 2) {
     const long long half = (max_blocks + 1) / 2;
     const long long items = (long long)num_seqs * num_kv_heads * ((half + cand - 1) / cand);
     if (items >= target) { pb = cand; break; }
+  }
+  if (const char* v = getenv("PA_DECODE_PB")) {
+    const int f = atoi(v);
+    if (f >= 2 && (f & (f - 1)) == 0) pb = f;
   }
   DecodePlan plan;
   plan.pb = pb;
@@ -463,10 +480,13 @@ template <typename QT, int CK, int D, int G>
 static hipError_t run_decode(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
   hipLaunchKernelGGL((decode_partition_kernel<QT, CK, D, G>), grid, dim3(256), 0, st, a);
-  if (a.max_parts > 1) {
-    const int waves = a.num_seqs * a.num_heads;
-    hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
-  }
+  return hipGetLastError();
+}
+
+template <typename QT, int D>
+static hipError_t run_merge(const DecodeArgs& a, hipStream_t st) {
+  const int waves = a.num_seqs * a.num_heads;
+  hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -489,13 +509,32 @@ static hipError_t run_decode_d(const DecodeArgs& a, int D, int G, hipStream_t st
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_decode_mfma(const DecodeArgs& a, int cache_kind, int head_size, hipStream_t st);
+
+// Which decode kernel serves a request: the matrix-core kernel for bf16/fp8
+// caches (any group up to 16 query heads per KV head), the VALU kernel for
+// fp32 caches. PA_DECODE_KERNEL=valu forces the VALU kernel (diagnostics and
+// side-by-side measurement).
+static bool use_mfma(int q_kind, int cache_kind, int group) {
+  const char* v = getenv("PA_DECODE_KERNEL");
+  const int forced = (v && strcmp(v, "valu") == 0) ? 1 : 0;
+  const bool ok = q_kind == KBF16 && (cache_kind == KBF16 || cache_kind == KFP8) && group <= 16;
+  if (forced == 1) return false;
+  return ok;
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int q_kind, int cache_kind, int head_size,
                          hipStream_t stream) {
   const int G = a.num_heads / a.num_kv_heads;
-  if (q_kind == KF32 && cache_kind == KF32) return run_decode_d<float, KF32>(a, head_size, G, stream);
-  if (q_kind == KBF16 && cache_kind == KBF16) return run_decode_d<uint16_t, KBF16>(a, head_size, G, stream);
-  if (q_kind == KBF16 && cache_kind == KFP8) return run_decode_d<uint16_t, KFP8>(a, head_size, G, stream);
-  return hipErrorInvalidValue;
+  hipError_t e;
+  if (use_mfma(q_kind, cache_kind, G)) e = launch_decode_mfma(a, cache_kind, head_size, stream);
+  else if (q_kind == KF32 && cache_kind == KF32) e = run_decode_d<float, KF32>(a, head_size, G, stream);
+  else if (q_kind == KBF16 && cache_kind == KBF16) e = run_decode_d<uint16_t, KBF16>(a, head_size, G, stream);
+  else if (q_kind == KBF16 && cache_kind == KFP8) e = run_decode_d<uint16_t, KFP8>(a, head_size, G, stream);
+  else return hipErrorInvalidValue;
+  if (e != hipSuccess || a.max_parts <= 1) return e;
+  if (q_kind == KF32) return head_size == 64 ? run_merge<float, 64>(a, stream) : run_merge<float, 128>(a, stream);
+  return head_size == 64 ? run_merge<uint16_t, 64>(a, stream) : run_merge<uint16_t, 128>(a, stream);
 }
 
 }  // namespace pa

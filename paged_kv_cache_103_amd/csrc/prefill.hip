@@ -46,18 +46,19 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, co
 
 template <int CK, int D>
 struct PrefillShape {
+  static constexpr int KT = 64;                   // keys per tile (four 16-token blocks)
   static constexpr int KROW = D + 8;              // LDS K row (bf16 elements), padded by 16 bytes
-  static constexpr int K_LDS = 32 * KROW;         // bf16 elements of one K tile
-  static constexpr int V_LDS = 2 * D * 16;        // two transposed V block tiles
+  static constexpr int K_LDS = KT * KROW;         // bf16 elements of one K tile
+  static constexpr int V_LDS = 4 * D * 16;        // four transposed V block tiles [D][16]
   static constexpr int BUF = K_LDS + V_LDS;       // one stage
   static constexpr int E = CacheElem<CK>::bytes;
   static constexpr int BLK_BYTES = 16 * D * E;    // global bytes of one (block, head) tile
-  // 16-byte global chunks per thread per tile (K and V each): 2 blocks
-  static constexpr int CHUNKS = (2 * BLK_BYTES / 16 + 255) / 256;
+  static constexpr int CHUNKS16 = 4 * BLK_BYTES / 16;       // 16-byte global chunks per tile (K or V)
+  static constexpr int CHUNKS = (CHUNKS16 + 255) / 256;     // per thread
 };
 
 template <int CK, int D, int G>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillArgs a) {
   using S = PrefillShape<CK, D>;
   constexpr int TQ = 128 / G;  // tokens per tile
   constexpr int DS = D / 32;   // MFMA k-steps over head_size
@@ -142,20 +143,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int ct = 0; ct < 2; ++ct) o[dt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
 
-  // ---- staging: global (two blocks) -> registers -> LDS ----
+  // ---- staging: global (four blocks) -> registers -> LDS ----
   const size_t head_stride = (size_t)a.num_kv_heads * S::BLK_BYTES;
   const uint8_t* kcache = reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)g * S::BLK_BYTES;
   const uint8_t* vcache = reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * S::BLK_BYTES;
   u32x4 kreg[S::CHUNKS], vreg[S::CHUNKS];
 
+  // Blocks past the context are not read (their chunks stay zero).
   auto load_tile = [&](int j) {
     const int b0 = j >> 4;
 #pragma unroll
     for (int r = 0; r < S::CHUNKS; ++r) {
-      const int c = tid + 256 * r;                 // 16-byte chunk within the two blocks
-      const int blk = c / (S::BLK_BYTES / 16);     // 0 or 1
+      const int c = tid + 256 * r;                 // 16-byte chunk within the four blocks
+      const int blk = c / (S::BLK_BYTES / 16);
       const int off = (c % (S::BLK_BYTES / 16)) * 16;
-      if (c < 2 * S::BLK_BYTES / 16 && b0 + blk <= b_last) {
+      if (c < S::CHUNKS16 && b0 + blk <= b_last) {
         const size_t phys = (size_t)bt[b0 + blk];
         kreg[r] = load16(kcache + phys * head_stride + off);
         vreg[r] = load16(vcache + phys * head_stride + off);
@@ -165,34 +167,29 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       }
     }
   };
+  // K rows keep key order in LDS ([64][D], padded); V keeps the cache's
+  // per-block [D][16] tiles. Values of keys past the context are zeroed.
   auto store_tile = [&](int j, uint16_t* buf) {
     uint16_t* ks = buf;
     uint16_t* vs = buf + S::K_LDS;
 #pragma unroll
     for (int r = 0; r < S::CHUNKS; ++r) {
       const int c = tid + 256 * r;
-      if (c >= 2 * S::BLK_BYTES / 16) continue;
+      if (c >= S::CHUNKS16) continue;
       const int blk = c / (S::BLK_BYTES / 16);
       const int off = (c % (S::BLK_BYTES / 16)) * 16;  // byte offset inside the block tile
-      // K: element offset off/E inside [16][D] -> LDS row blk*16 + row
-      const int kel = off / E;
-      const int krow = blk * 16 + kel / D, kcol = kel % D;
-      // V^T: element offset inside [D][16] -> d row, first key
-      const int vel = off / E;
-      const int vd = vel / 16, vkey = vel % 16;
-      const int key_base = j + blk * 16 + vkey;  // key position of the chunk's first element
+      const int el = off / E;
+      const int krow = blk * 16 + el / D, kcol = el % D;
+      const int vd = el / 16, vkey = el % 16;
+      const int key_base = j + blk * 16 + vkey;
       if constexpr (CK == KBF16) {
         *reinterpret_cast<u32x4*>(ks + krow * S::KROW + kcol) = kreg[r];
         u32x4 v = vreg[r];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t mlo = (key_base + 2 * e < ctx) ? 0x0000ffffu : 0u;
-          const uint32_t mhi = (key_base + 2 * e + 1 < ctx) ? 0xffff0000u : 0u;
-          v[e] &= (mlo | mhi);
-        }
+        for (int e = 0; e < 4; ++e)
+          v[e] &= ((key_base + 2 * e < ctx) ? 0x0000ffffu : 0u) | ((key_base + 2 * e + 1 < ctx) ? 0xffff0000u : 0u);
         *reinterpret_cast<u32x4*>(vs + blk * D * 16 + vd * 16 + vkey) = v;
       } else {
-        // fp8: 16 bytes -> 16 bf16 (exact), written as two 16-byte pieces
         const u32x4 k0 = fp8x8_to_bf16x8(kreg[r][0], kreg[r][1]);
         const u32x4 k1 = fp8x8_to_bf16x8(kreg[r][2], kreg[r][3]);
         *reinterpret_cast<u32x4*>(ks + krow * S::KROW + kcol) = k0;
@@ -211,113 +208,124 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  const int jstart = (lo_first >> 5) << 5;
+  const int jstart = (lo_first >> 6) << 6;
   const int jend = qpos_last;  // last key any column of the tile can see
   int cur = 0;
   load_tile(jstart);
   store_tile(jstart, lds);
   __syncthreads();
 
-  const int col_l = wave * 32 + (lane & 15);  // column of ct = 0; ct = 1 adds 16
-  for (int j = jstart; j <= jend; j += 32) {
-    const bool more = j + 32 <= jend;
-    if (more) load_tile(j + 32);
+  const int c16 = lane & 15, q4 = lane >> 4;
+  const int col_l = wave * 32 + c16;  // column of ct = 0; ct = 1 adds 16
+  // Score rows are fed in a permuted key order: in each 32-key step, tile kt
+  // row i holds key 8*(i/4) + 4*kt + i%4, so that lane group q ends up with
+  // keys 8q..8q+7 — the k-slice PV wants from it, and a contiguous 16-byte
+  // run of the transposed V block.
+  const int kperm0 = 8 * (c16 >> 2) + (c16 & 3);
+  for (int j = jstart; j <= jend; j += S::KT) {
+    const bool more = j + S::KT <= jend;
+    if (more) load_tile(j + S::KT);
 
     const uint16_t* ks = lds + cur * S::BUF;
     const uint16_t* vs = ks + S::K_LDS;
 
-    // ---- S^T = K Q^T : 2 key tiles x 2 column tiles ----
-    f32x4 sc[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      sc[kt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      sc[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + (kt * 16 + (lane & 15)) * S::KROW +
-                                                          ds * 32 + (lane >> 4) * 8);
-        sc[kt][0] = mfma16x16x32(kf, qf[0][ds], sc[kt][0]);
-        sc[kt][1] = mfma16x16x32(kf, qf[1][ds], sc[kt][1]);
-      }
-    }
-
-    // ---- scale, mask, online softmax per column ----
-    float ksc[2] = {a.scale_log2, a.scale_log2};
+    float ksc[2] = {a.scale_log2, a.scale_log2};  // per 32-key step: this lane group's block
     float vsc[2] = {1.f, 1.f};
     if constexpr (CK == KFP8) {
-      const int b0 = j >> 4;
-      ksc[0] *= a.k_scale[bt[b0]];
-      vsc[0] = a.v_scale[bt[b0]];
-      if (b0 + 1 <= b_last) {
-        ksc[1] *= a.k_scale[bt[b0 + 1]];
-        vsc[1] = a.v_scale[bt[b0 + 1]];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int blk = (j >> 4) + 2 * st + (q4 >> 1);
+        if (blk <= b_last) {
+          const int phys = bt[blk];
+          ksc[st] *= a.k_scale[phys];
+          vsc[st] = a.v_scale[phys];
+        }
       }
     }
-    const bool need_mask = (j + 31 > qpos_first) || (a.window > 0 && j < qpos_last - a.window + 1);
-    u32x4 pf[2], pg[2];  // P^T as bf16 hi and lo parts
+    const bool need_mask = (j + S::KT - 1 > qpos_first) || (a.window > 0 && j < qpos_last - a.window + 1);
+
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int col = col_l + ct * 16;
-      const int qpos = qpos_first + col / G;
-      float x[2][4];
-      float tmax = -INFINITY;
+    for (int st = 0; st < 2; ++st) {  // two 32-key steps
+      // ---- S^T = K Q^T : 2 key tiles x 2 column tiles ----
+      f32x4 sc[2][2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt) {
+        sc[kt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sc[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint16_t* krow = ks + (32 * st + kperm0 + 4 * kt) * S::KROW + q4 * 8;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = sc[kt][ct][r] * ksc[kt];
-          if (need_mask) {
-            const int kp = j + kt * 16 + (lane >> 4) * 4 + r;
-            const bool ok = kp <= qpos && kp < ctx && (a.window <= 0 || kp > qpos - a.window);
-            v = ok ? v : -INFINITY;
+        for (int ds = 0; ds < DS; ++ds) {
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + ds * 32);
+          sc[kt][0] = mfma16x16x32(kf, qf[0][ds], sc[kt][0]);
+          sc[kt][1] = mfma16x16x32(kf, qf[1][ds], sc[kt][1]);
+        }
+      }
+      // ---- scale, mask, online softmax per column ----
+      const int kbase = j + 32 * st + 8 * q4;  // this lane's keys: kbase + 4*kt + r
+      u32x4 ph[2], pl[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int qpos = qpos_first + (col_l + ct * 16) / G;
+        float x[2][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float v = sc[kt][ct][r] * ksc[st];
+            if (need_mask) {
+              const int kp = kbase + 4 * kt + r;
+              const bool ok = kp <= qpos && kp < ctx && (a.window <= 0 || kp > qpos - a.window);
+              v = ok ? v : -INFINITY;
+            }
+            x[kt][r] = v;
+            tmax = fmaxf(tmax, v);
           }
-          x[kt][r] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      tmax = strided_max<16>(tmax);
-      const float mn = fmaxf(m[ct], tmax);
-      const float base = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = __builtin_amdgcn_exp2f(m[ct] - base);
-      m[ct] = mn;
-      float ps = 0.f;
-      float pv[2][4];
+        tmax = strided_max<16>(tmax);
+        const float mn = fmaxf(m[ct], tmax);
+        const float base = (mn == -INFINITY) ? 0.f : mn;
+        const float alpha = __builtin_amdgcn_exp2f(m[ct] - base);
+        m[ct] = mn;
+        float ps = 0.f;
+        float pv[2][4];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(x[kt][r] - base);
-          ps += p;
-          pv[kt][r] = p * vsc[kt];
+          for (int r = 0; r < 4; ++r) {
+            const float p = __builtin_amdgcn_exp2f(x[kt][r] - base);
+            ps += p;
+            pv[kt][r] = p * vsc[st];
+          }
+        lsum[ct] = lsum[ct] * alpha + ps;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            o[dt][ct][0] *= alpha; o[dt][ct][1] *= alpha; o[dt][ct][2] *= alpha; o[dt][ct][3] *= alpha;
+          }
         }
-      lsum[ct] = lsum[ct] * alpha + ps;
+        // P^T operand, logical k 8*q4 + e <-> key kbase + e (e = 4*kt + r);
+        // p = hi + lo, both bf16
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float a0 = pv[t >> 1][(t & 1) * 2], a1 = pv[t >> 1][(t & 1) * 2 + 1];
+          const uint32_t hi = pack_bf16x2(a0, a1);
+          ph[ct][t] = hi;
+          pl[ct][t] = pack_bf16x2(a0 - bf16_lo(hi), a1 - bf16_hi(hi));
+        }
+      }
+      // ---- O^T += V^T P^T over these 32 keys ----
+      const uint16_t* vrow = vs + (2 * st + (q4 >> 1)) * D * 16 + 8 * (q4 & 1);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        o[dt][ct][0] *= alpha; o[dt][ct][1] *= alpha; o[dt][ct][2] *= alpha; o[dt][ct][3] *= alpha;
-      }
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        const float a0 = pv[q2 >> 1][(q2 & 1) * 2], a1 = pv[q2 >> 1][(q2 & 1) * 2 + 1];
-        const uint32_t hi = pack_bf16x2(a0, a1);
-        pf[ct][q2] = hi;
-        pg[ct][q2] = pack_bf16x2(a0 - bf16_lo(hi), a1 - bf16_hi(hi));
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + (dt * 16 + c16) * 16);
+        o[dt][0] = mfma16x16x32(vf, ph[0], o[dt][0]);
+        o[dt][1] = mfma16x16x32(vf, ph[1], o[dt][1]);
+        o[dt][0] = mfma16x16x32(vf, pl[0], o[dt][0]);
+        o[dt][1] = mfma16x16x32(vf, pl[1], o[dt][1]);
       }
     }
 
-    // ---- O^T += V^T P^T over the 32 keys ----
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = dt * 16 + (lane & 15);
-      const int k4 = (lane >> 4) * 4;
-      const uint2 v0 = *reinterpret_cast<const uint2*>(vs + d * 16 + k4);           // block 0
-      const uint2 v1 = *reinterpret_cast<const uint2*>(vs + D * 16 + d * 16 + k4);  // block 1
-      const u32x4 vf = u32x4{v0.x, v0.y, v1.x, v1.y};
-      o[dt][0] = mfma16x16x32(vf, pf[0], o[dt][0]);
-      o[dt][0] = mfma16x16x32(vf, pg[0], o[dt][0]);
-      o[dt][1] = mfma16x16x32(vf, pf[1], o[dt][1]);
-      o[dt][1] = mfma16x16x32(vf, pg[1], o[dt][1]);
-    }
-
-    if (more) store_tile(j + 32, lds + (cur ^ 1) * S::BUF);
+    if (more) store_tile(j + S::KT, lds + (cur ^ 1) * S::BUF);
     __syncthreads();
     cur ^= 1;
   }
