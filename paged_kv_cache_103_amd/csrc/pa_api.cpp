@@ -141,9 +141,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len, int3
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len,
                                   int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
                                   int32_t head_size, int32_t sliding_window) {
-  (void)num_q_tokens;
-  (void)max_q_len;
-  // the prefill tiles need no scratch; the one-token rows use the decode plan
+  // the prefill tiles need no scratch; one-token rows use the decode plan,
+  // and there are none when every sequence has max_q_len > 1 tokens
+  if (max_q_len > 1 && (long long)num_q_tokens == (long long)num_seqs * max_q_len) return 0;
   return pa_decode_workspace_bytes(num_seqs, max_context_len, num_heads, num_kv_heads, head_size,
                                    sliding_window);
 }
@@ -224,8 +224,11 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
   if (has_chunks && !pa::prefill_supported((int)q_dtype, (int)cache_dtype, head_size, group))
     return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for q %s, cache %s, head_size %d, group %d",
                 dtype_name(q_dtype), dtype_name(cache_dtype), head_size, group);
+  // Rows with one query token may exist unless every sequence provably has
+  // max_q_len > 1 tokens (the only case the host scalars can prove).
+  const bool any_single = !(has_chunks && (long long)num_q_tokens == (long long)num_seqs * max_q_len);
   const pa::DecodePlan plan = pa::plan_decode(num_seqs, max_context_len, num_kv_heads, sliding_window);
-  const size_t need = pa::decode_workspace_bytes(plan, num_seqs, num_heads, head_size);
+  const size_t need = any_single ? pa::decode_workspace_bytes(plan, num_seqs, num_heads, head_size) : 0;
   if (workspace_bytes < need || (need > 0 && workspace == nullptr))
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "prefill needs %zu workspace bytes (got %zu)", need,
                 workspace_bytes);
@@ -254,9 +257,6 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
   d.pb = plan.pb;
   d.max_parts = plan.max_parts;
   d.scale_log2 = scale_log2;
-  // Rows with one query token may exist unless every sequence provably has
-  // max_q_len > 1 tokens (the only case the host scalars can prove).
-  const bool any_single = !(has_chunks && (long long)num_q_tokens == (long long)num_seqs * max_q_len);
   if (any_single) {
     hipError_t e = pa::launch_decode(d, (int)q_dtype, (int)cache_dtype, head_size, hs);
     if (e != hipSuccess) return hip_status(e, "decode launch (one-token rows)");

@@ -32,6 +32,8 @@
 // workgroup index so that the tiles of one head land on the same XCD.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -47,15 +49,27 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, co
 template <int CK, int D>
 struct PrefillShape {
   static constexpr int KT = 64;                   // keys per tile (four 16-token blocks)
-  static constexpr int KROW = D + 8;              // LDS K row (bf16 elements), padded by 16 bytes
-  static constexpr int K_LDS = KT * KROW;         // bf16 elements of one K tile
-  static constexpr int V_LDS = 4 * D * 16;        // four transposed V block tiles [D][16]
+  static constexpr int K_LDS = KT * D;            // bf16 elements of one K tile ([64][D], swizzled)
+  static constexpr int V_LDS = 4 * D * 16;        // four transposed V block tiles ([D][16], swizzled)
   static constexpr int BUF = K_LDS + V_LDS;       // one stage
   static constexpr int E = CacheElem<CK>::bytes;
   static constexpr int BLK_BYTES = 16 * D * E;    // global bytes of one (block, head) tile
   static constexpr int CHUNKS16 = 4 * BLK_BYTES / 16;       // 16-byte global chunks per tile (K or V)
   static constexpr int CHUNKS = (CHUNKS16 + 255) / 256;     // per thread
 };
+
+// LDS bank swizzles (16-byte chunk index XOR a function of the row). A K row
+// holds D bf16 = D/8 chunks; the score MFMA reads, per 16-lane group, one
+// chunk from each of the rows 8q + 4kt + r (q, r in 0..3): the XOR spreads
+// those 16 reads over all 64 banks. A V^T row holds 16 keys = 2 chunks; the
+// PV MFMA reads one chunk from 16 consecutive rows: flipping the chunk for
+// rows 8..15 separates rows d and d+8.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  if constexpr (D == 128) return (row & 3) | (((row >> 3) & 3) << 2);
+  else return ((row >> 1) & 1) | (((row >> 3) & 3) << 1);
+}
+__device__ __forceinline__ int v_swz(int row) { return (row >> 3) & 1; }
 
 template <int CK, int D, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillArgs a) {
@@ -167,8 +181,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   };
-  // K rows keep key order in LDS ([64][D], padded); V keeps the cache's
-  // per-block [D][16] tiles. Values of keys past the context are zeroed.
+  // K rows keep key order in LDS ([64][D]); V keeps the cache's per-block
+  // [D][16] tiles; 16-byte chunks are placed by the bank swizzles. Values of
+  // keys past the context are zeroed.
   auto store_tile = [&](int j, uint16_t* buf) {
     uint16_t* ks = buf;
     uint16_t* vs = buf + S::K_LDS;
@@ -179,21 +194,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int blk = c / (S::BLK_BYTES / 16);
       const int off = (c % (S::BLK_BYTES / 16)) * 16;  // byte offset inside the block tile
       const int el = off / E;
-      const int krow = blk * 16 + el / D, kcol = el % D;
-      const int vd = el / 16, vkey = el % 16;
-      const int key_base = j + blk * 16 + vkey;
+      const int krow = blk * 16 + el / D, kchunk = (el % D) / 8;
+      const int vd = el / 16, vchunk = (el % 16) / 8;
+      const int key_base = j + blk * 16 + (el % 16);
+      uint16_t* kdst = ks + krow * D;
+      uint16_t* vdst = vs + (blk * D + vd) * 16;
       if constexpr (CK == KBF16) {
-        *reinterpret_cast<u32x4*>(ks + krow * S::KROW + kcol) = kreg[r];
+        *reinterpret_cast<u32x4*>(kdst + 8 * (kchunk ^ k_swz<D>(krow))) = kreg[r];
         u32x4 v = vreg[r];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           v[e] &= ((key_base + 2 * e < ctx) ? 0x0000ffffu : 0u) | ((key_base + 2 * e + 1 < ctx) ? 0xffff0000u : 0u);
-        *reinterpret_cast<u32x4*>(vs + blk * D * 16 + vd * 16 + vkey) = v;
+        *reinterpret_cast<u32x4*>(vdst + 8 * (vchunk ^ v_swz(vd))) = v;
       } else {
         const u32x4 k0 = fp8x8_to_bf16x8(kreg[r][0], kreg[r][1]);
         const u32x4 k1 = fp8x8_to_bf16x8(kreg[r][2], kreg[r][3]);
-        *reinterpret_cast<u32x4*>(ks + krow * S::KROW + kcol) = k0;
-        *reinterpret_cast<u32x4*>(ks + krow * S::KROW + kcol + 8) = k1;
+        *reinterpret_cast<u32x4*>(kdst + 8 * (kchunk ^ k_swz<D>(krow))) = k0;
+        *reinterpret_cast<u32x4*>(kdst + 8 * ((kchunk + 1) ^ k_swz<D>(krow))) = k1;
         u32x4 v0 = fp8x8_to_bf16x8(vreg[r][0], vreg[r][1]);
         u32x4 v1 = fp8x8_to_bf16x8(vreg[r][2], vreg[r][3]);
 #pragma unroll
@@ -202,17 +219,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           v1[e] &= ((key_base + 8 + 2 * e < ctx) ? 0x0000ffffu : 0u) |
                    ((key_base + 8 + 2 * e + 1 < ctx) ? 0xffff0000u : 0u);
         }
-        *reinterpret_cast<u32x4*>(vs + blk * D * 16 + vd * 16 + vkey) = v0;
-        *reinterpret_cast<u32x4*>(vs + blk * D * 16 + vd * 16 + vkey + 8) = v1;
+        *reinterpret_cast<u32x4*>(vdst + 8 * (0 ^ v_swz(vd))) = v0;
+        *reinterpret_cast<u32x4*>(vdst + 8 * (1 ^ v_swz(vd))) = v1;
       }
+    }
+  };
+
+  // bf16 caches skip the register staging: each wave copies one block's K
+  // rows and V^T tile straight from global memory into LDS (one 16-byte chunk
+  // per lane, lane i to byte 16*i of a 1 KiB region), choosing per lane the
+  // global chunk that the bank swizzle wants at that LDS position. Blocks past
+  // the context re-read the last block; their keys are masked (scores) and
+  // zeroed (values) in the masked tiles.
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  typedef __attribute__((address_space(1))) void glob_void_t;
+  auto dma_tile = [&](int j, uint16_t* buf) {
+    const int b = min((j >> 4) + wave, b_last);
+    const size_t phys = (size_t)bt[b];
+    const uint8_t* kb = kcache + phys * head_stride;
+    const uint8_t* vb = vcache + phys * head_stride;
+    uint16_t* kdst = buf + wave * 16 * D;
+    uint16_t* vdst = buf + S::K_LDS + wave * D * 16;
+    constexpr int RPR = D / 8;            // 16-byte chunks per K row
+    constexpr int ROWS_PER_KB = 64 / RPR;  // K rows per 1 KiB region
+    constexpr int REGIONS = 16 * D * 2 / 1024;
+#pragma unroll
+    for (int n = 0; n < REGIONS; ++n) {
+      const int rr = n * ROWS_PER_KB + lane / RPR;
+      const int c = (lane % RPR) ^ k_swz<D>(16 * wave + rr);
+      __builtin_amdgcn_global_load_lds((glob_void_t*)(kb + rr * (2 * D) + c * 16), (lds_void_t*)(kdst + n * 512),
+                                       16, 0, 0);
+    }
+#pragma unroll
+    for (int n = 0; n < REGIONS; ++n) {
+      const int d = n * 32 + lane / 2;
+      const int c = (lane & 1) ^ v_swz(d);
+      __builtin_amdgcn_global_load_lds((glob_void_t*)(vb + d * 32 + c * 16), (lds_void_t*)(vdst + n * 512), 16,
+                                       0, 0);
     }
   };
 
   const int jstart = (lo_first >> 6) << 6;
   const int jend = qpos_last;  // last key any column of the tile can see
   int cur = 0;
-  load_tile(jstart);
-  store_tile(jstart, lds);
+  if constexpr (CK == KBF16) {
+    dma_tile(jstart, lds);
+    __builtin_amdgcn_s_waitcnt(0);
+  } else {
+    load_tile(jstart);
+    store_tile(jstart, lds);
+  }
   __syncthreads();
 
   const int c16 = lane & 15, q4 = lane >> 4;
@@ -222,13 +278,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // keys 8q..8q+7 — the k-slice PV wants from it, and a contiguous 16-byte
   // run of the transposed V block.
   const int kperm0 = 8 * (c16 >> 2) + (c16 & 3);
-  for (int j = jstart; j <= jend; j += S::KT) {
-    const bool more = j + S::KT <= jend;
-    if (more) load_tile(j + S::KT);
+  int qpos_c[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) qpos_c[ct] = qpos_first + (col_l + ct * 16) / G;
 
-    const uint16_t* ks = lds + cur * S::BUF;
-    const uint16_t* vs = ks + S::K_LDS;
-
+  // One 64-key tile. MASKED tiles cross a column's causal or window edge or
+  // the context end; interior tiles carry no masking code.
+  auto tile = [&](auto masked_tag, int j, const uint16_t* ks, const uint16_t* vs) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     float ksc[2] = {a.scale_log2, a.scale_log2};  // per 32-key step: this lane group's block
     float vsc[2] = {1.f, 1.f};
     if constexpr (CK == KFP8) {
@@ -242,9 +299,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     }
-    const bool need_mask = (j + S::KT - 1 > qpos_first) || (a.window > 0 && j < qpos_last - a.window + 1);
-
-#pragma unroll
+#pragma unroll 1
     for (int st = 0; st < 2; ++st) {  // two 32-key steps
       // ---- S^T = K Q^T : 2 key tiles x 2 column tiles ----
       f32x4 sc[2][2];
@@ -252,10 +307,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int kt = 0; kt < 2; ++kt) {
         sc[kt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
         sc[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint16_t* krow = ks + (32 * st + kperm0 + 4 * kt) * S::KROW + q4 * 8;
+        const int row = 32 * st + kperm0 + 4 * kt;
+        const uint16_t* krow = ks + row * D;
+        const int sw = k_swz<D>(row);
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + ds * 32);
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 8 * ((4 * ds + q4) ^ sw));
           sc[kt][0] = mfma16x16x32(kf, qf[0][ds], sc[kt][0]);
           sc[kt][1] = mfma16x16x32(kf, qf[1][ds], sc[kt][1]);
         }
@@ -265,7 +322,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       u32x4 ph[2], pl[2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const int qpos = qpos_first + (col_l + ct * 16) / G;
         float x[2][4];
         float tmax = -INFINITY;
 #pragma unroll
@@ -273,8 +329,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float v = sc[kt][ct][r] * ksc[st];
-            if (need_mask) {
+            if constexpr (MASKED) {
               const int kp = kbase + 4 * kt + r;
+              const int qpos = qpos_c[ct];
               const bool ok = kp <= qpos && kp < ctx && (a.window <= 0 || kp > qpos - a.window);
               v = ok ? v : -INFINITY;
             }
@@ -282,10 +339,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             tmax = fmaxf(tmax, v);
           }
         tmax = strided_max<16>(tmax);
-        const float mn = fmaxf(m[ct], tmax);
-        const float base = (mn == -INFINITY) ? 0.f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(m[ct] - base);
-        m[ct] = mn;
+        // Lazy rescaling: the running max moves only when the tile's max
+        // exceeds it by more than 2^8 (p stays below 256 otherwise), so the
+        // O^T rescale is rare; the final division uses the same max.
+        const bool up = tmax > m[ct] + 8.f;
+        if (__any(up)) {
+          const float alpha = up ? __builtin_amdgcn_exp2f(m[ct] - tmax) : 1.f;  // 0 when m was -inf
+          m[ct] = up ? tmax : m[ct];
+          lsum[ct] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            o[dt][ct][0] *= alpha; o[dt][ct][1] *= alpha; o[dt][ct][2] *= alpha; o[dt][ct][3] *= alpha;
+          }
+        }
+        const float base = (m[ct] == -INFINITY) ? 0.f : m[ct];
         float ps = 0.f;
         float pv[2][4];
 #pragma unroll
@@ -294,15 +361,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int r = 0; r < 4; ++r) {
             const float p = __builtin_amdgcn_exp2f(x[kt][r] - base);
             ps += p;
-            pv[kt][r] = p * vsc[st];
+            pv[kt][r] = (CK == KFP8) ? p * vsc[st] : p;
           }
-        lsum[ct] = lsum[ct] * alpha + ps;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            o[dt][ct][0] *= alpha; o[dt][ct][1] *= alpha; o[dt][ct][2] *= alpha; o[dt][ct][3] *= alpha;
-          }
-        }
+        lsum[ct] += ps;
         // P^T operand, logical k 8*q4 + e <-> key kbase + e (e = 4*kt + r);
         // p = hi + lo, both bf16
 #pragma unroll
@@ -314,18 +375,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
       // ---- O^T += V^T P^T over these 32 keys ----
-      const uint16_t* vrow = vs + (2 * st + (q4 >> 1)) * D * 16 + 8 * (q4 & 1);
+      // (values of keys past the context may hold anything, even NaN: the
+      // masked tiles zero this lane's 8 keys kbase..kbase+7 that are >= ctx)
+      uint32_t vmask[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        vmask[t] = (kbase + 2 * t < ctx ? 0x0000ffffu : 0u) | (kbase + 2 * t + 1 < ctx ? 0xffff0000u : 0u);
+      (void)vmask;
+      const uint16_t* vblk = vs + (2 * st + (q4 >> 1)) * D * 16;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + (dt * 16 + c16) * 16);
+        const int d = dt * 16 + c16;
+        u32x4 vf = *reinterpret_cast<const u32x4*>(vblk + d * 16 + 8 * ((q4 & 1) ^ v_swz(d)));
+        if constexpr (MASKED && CK == KBF16) {
+          vf[0] &= vmask[0]; vf[1] &= vmask[1]; vf[2] &= vmask[2]; vf[3] &= vmask[3];
+        }
         o[dt][0] = mfma16x16x32(vf, ph[0], o[dt][0]);
         o[dt][1] = mfma16x16x32(vf, ph[1], o[dt][1]);
         o[dt][0] = mfma16x16x32(vf, pl[0], o[dt][0]);
         o[dt][1] = mfma16x16x32(vf, pl[1], o[dt][1]);
       }
     }
+  };
 
-    if (more) store_tile(j + S::KT, lds + (cur ^ 1) * S::BUF);
+  for (int j = jstart; j <= jend; j += S::KT) {
+    const bool more = j + S::KT <= jend;
+    if constexpr (CK == KBF16) {
+      if (more) dma_tile(j + S::KT, lds + (cur ^ 1) * S::BUF);
+    } else {
+      if (more) load_tile(j + S::KT);
+    }
+    const uint16_t* ks = lds + cur * S::BUF;
+    const uint16_t* vs = ks + S::K_LDS;
+    const bool need_mask = (j + S::KT - 1 > qpos_first) || (a.window > 0 && j < qpos_last - a.window + 1);
+    if (need_mask) tile(std::true_type{}, j, ks, vs);
+    else tile(std::false_type{}, j, ks, vs);
+    if constexpr (CK == KBF16) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies into the other stage are done
+    } else {
+      if (more) store_tile(j + S::KT, lds + (cur ^ 1) * S::BUF);
+    }
     __syncthreads();
     cur ^= 1;
   }
