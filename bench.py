@@ -40,10 +40,10 @@ def log(*a):
 def workspace(pa, torch, b, prefill=False):
     if prefill:
         n = pa.prefill_workspace_bytes(b.num_seqs, b.num_q_tokens, b.max_q_len, b.max_context_len,
-                                       b.num_heads, b.num_kv_heads, b.head_size, b.sliding_window)
+                                       b.num_heads, b.num_kv_heads, b.head_size, b.cache_dtype, b.sliding_window)
     else:
         n = pa.decode_workspace_bytes(b.num_seqs, b.max_context_len, b.num_heads, b.num_kv_heads,
-                                      b.head_size, b.sliding_window)
+                                      b.head_size, b.cache_dtype, b.sliding_window)
     return torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
 
 
@@ -171,6 +171,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--extra", action="store_true", help="also time the other named configurations (stderr)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="only the kernels a counter run needs: a plain 1 GiB device copy (the "
+                         "calibration kernel for FETCH_SIZE/WRITE_SIZE) and a few decode and mixed steps")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
@@ -184,6 +187,27 @@ def main():
 
     pa.load()
     torch.cuda.set_device(0)
+
+    if args.profile_pass:
+        # plain copy kernel of known size: 1 GiB read + 1 GiB written per launch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
+        for name in ("llama8b_decode", "mixed_step"):
+            b = W.make_config(name, device="cuda")
+            write, attend = (prefill_step_fns if b.max_q_len > 1 else decode_step_fns)(pa, torch, b)
+            for _ in range(3):
+                write()
+                attend()
+            torch.cuda.synchronize()
+            del b
+            torch.cuda.empty_cache()
+        log("profile pass done")
+        return
 
     # ---- headline: decode on the Llama-3-8B-shaped batch ----
     b, dec = run_config(pa, torch, W, "llama8b_decode", args.steps, args.warmup)

@@ -151,14 +151,18 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
                            int32_t sliding_window, void* workspace, size_t workspace_bytes,
                            pa_stream_t stream);
 
-/* Workspace bytes pa_decode needs for these sizes (0 if none). */
+/* Workspace bytes pa_decode needs for these sizes and cache type (0 if
+ * none): the split-K partition summaries, num_seqs x num_heads x partitions
+ * x (head_size + 2) floats. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
-                                 int32_t num_kv_heads, int32_t head_size, int32_t sliding_window);
+                                 int32_t num_kv_heads, int32_t head_size, pa_dtype cache_dtype,
+                                 int32_t sliding_window);
 
-/* Workspace bytes pa_prefill_chunk needs for these sizes (0 if none). */
+/* Workspace bytes pa_prefill_chunk needs for these sizes (0 if none; the
+ * one-token rows of a mixed batch use the decode plan). */
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len,
                                   int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
-                                  int32_t head_size, int32_t sliding_window);
+                                  int32_t head_size, pa_dtype cache_dtype, int32_t sliding_window);
 
 /* Static name of a status code. */
 const char* pa_status_string(pa_status s);

@@ -71,9 +71,9 @@ def load() -> ctypes.CDLL:
                                    i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_float, i32,
                                    vp, sz, vp]
     L.pa_decode_workspace_bytes.restype = sz
-    L.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, i32]
     L.pa_prefill_workspace_bytes.restype = sz
-    L.pa_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    L.pa_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_last_error.restype = ctypes.c_char_p
@@ -125,17 +125,31 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+CACHE_CODES = {"f32": PA_F32, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3}
+
+
+def _cache_code(cache_dtype) -> int:
+    if isinstance(cache_dtype, str):
+        return CACHE_CODES[cache_dtype]
+    if isinstance(cache_dtype, torch.dtype):
+        return dtype_code(cache_dtype)
+    return int(cache_dtype)
+
+
 def decode_workspace_bytes(num_seqs: int, max_context_len: int, num_heads: int, num_kv_heads: int,
-                           head_size: int, sliding_window: int = 0) -> int:
+                           head_size: int, cache_dtype="bf16", sliding_window: int = 0) -> int:
+    """Bytes of device workspace pa_decode needs (cache_dtype: 'f32' | 'bf16' |
+    'fp8_e4m3', a torch dtype, or a PA_* code)."""
     return int(load().pa_decode_workspace_bytes(num_seqs, max_context_len, num_heads, num_kv_heads,
-                                                head_size, sliding_window))
+                                                head_size, _cache_code(cache_dtype), sliding_window))
 
 
 def prefill_workspace_bytes(num_seqs: int, num_q_tokens: int, max_q_len: int, max_context_len: int,
-                            num_heads: int, num_kv_heads: int, head_size: int,
+                            num_heads: int, num_kv_heads: int, head_size: int, cache_dtype="bf16",
                             sliding_window: int = 0) -> int:
     return int(load().pa_prefill_workspace_bytes(num_seqs, num_q_tokens, max_q_len, max_context_len,
-                                                 num_heads, num_kv_heads, head_size, sliding_window))
+                                                 num_heads, num_kv_heads, head_size, _cache_code(cache_dtype),
+                                                 sliding_window))
 
 
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,

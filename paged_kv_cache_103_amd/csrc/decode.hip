@@ -436,14 +436,48 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // host side: plan and dispatch
 // ---------------------------------------------------------------------------
-DecodePlan plan_decode(int num_seqs, int max_context_len, int num_kv_heads, int sliding_window) {
+int device_cu_count() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+// Which decode kernel serves a request: the matrix-core kernel for bf16/fp8
+// caches (any group up to 16 query heads per KV head), the VALU kernel for
+// fp32 caches. PA_DECODE_KERNEL=valu forces the VALU kernel (diagnostics and
+// side-by-side measurement).
+bool decode_uses_mfma(int q_kind, int cache_kind, int group) {
+  const char* v = getenv("PA_DECODE_KERNEL");
+  if (v && strcmp(v, "valu") == 0) return false;
+  return q_kind == KBF16 && (cache_kind == KBF16 || cache_kind == KFP8) && group <= 16;
+}
+
+DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num_kv_heads, int head_size,
+                       int q_kind, int cache_kind, int sliding_window) {
+  DecodePlan plan{};
+  const int G = std::max(1, num_heads / std::max(1, num_kv_heads));
+  // (the matrix-core kernel keeps per-sequence prefix sums in LDS: up to
+  // 16000 sequences per call; larger batches take the VALU kernel)
+  if (decode_uses_mfma(q_kind, cache_kind, G) && num_seqs <= 16000) {
+    // two resident workgroups of four waves per CU
+    plan.split_waves = 8 * device_cu_count();
+    plan.pb = 0;
+    plan.max_parts = 0;
+    return plan;
+  }
   int max_blocks = (max_context_len + 15) / 16;
   if (sliding_window > 0) max_blocks = std::min(max_blocks, (sliding_window + 15) / 16 + 1);
   if (max_blocks < 1) max_blocks = 1;
-  // Largest partition (16..256 blocks) that still leaves enough work items
-  // to fill the chip: about 16 (sequence, head, partition) items per CU,
-  // assuming contexts average half the maximum. PA_DECODE_PB (a power of two
-  // >= 2) overrides the choice for measurements.
+  // VALU kernel: a workgroup per (sequence, KV head, partition of pb blocks);
+  // the largest partition (16..256 blocks) that still leaves about 16 work
+  // items per CU, assuming contexts average half the maximum.
   const long long target = 4096;
   int pb = 16;
   for (int cand = 256; cand >= 16; cand /= 2) {
@@ -451,17 +485,27 @@ DecodePlan plan_decode(int num_seqs, int max_context_len, int num_kv_heads, int 
     const long long items = (long long)num_seqs * num_kv_heads * ((half + cand - 1) / cand);
     if (items >= target) { pb = cand; break; }
   }
+  // PA_DECODE_PB (a power of two >= 2) overrides the choice for measurements.
   if (const char* v = getenv("PA_DECODE_PB")) {
     const int f = atoi(v);
     if (f >= 2 && (f & (f - 1)) == 0) pb = f;
   }
-  DecodePlan plan;
   plan.pb = pb;
   plan.max_parts = (max_blocks + pb - 1) / pb;
+  plan.split_waves = 0;
   return plan;
 }
 
-size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int num_heads, int head_size) {
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int num_heads, int num_kv_heads,
+                              int head_size) {
+  if (plan.split_waves > 0) {
+    const int G = num_heads / num_kv_heads;
+    const size_t slots = (size_t)plan.split_waves + (size_t)num_seqs * num_kv_heads;
+    return align256((size_t)(num_seqs + 2) * sizeof(int)) + align256(slots * G * head_size * sizeof(float)) +
+           slots * G * 2 * sizeof(float);
+  }
   if (plan.max_parts <= 1) return 0;
   const size_t slots = (size_t)num_seqs * num_heads * plan.max_parts;
   return slots * head_size * sizeof(float) + slots * 2 * sizeof(float);
@@ -511,24 +555,13 @@ static hipError_t run_decode_d(const DecodeArgs& a, int D, int G, hipStream_t st
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int cache_kind, int head_size, hipStream_t st);
 
-// Which decode kernel serves a request: the matrix-core kernel for bf16/fp8
-// caches (any group up to 16 query heads per KV head), the VALU kernel for
-// fp32 caches. PA_DECODE_KERNEL=valu forces the VALU kernel (diagnostics and
-// side-by-side measurement).
-static bool use_mfma(int q_kind, int cache_kind, int group) {
-  const char* v = getenv("PA_DECODE_KERNEL");
-  const int forced = (v && strcmp(v, "valu") == 0) ? 1 : 0;
-  const bool ok = q_kind == KBF16 && (cache_kind == KBF16 || cache_kind == KFP8) && group <= 16;
-  if (forced == 1) return false;
-  return ok;
-}
 
 hipError_t launch_decode(const DecodeArgs& a, int q_kind, int cache_kind, int head_size,
                          hipStream_t stream) {
   const int G = a.num_heads / a.num_kv_heads;
   hipError_t e;
-  if (use_mfma(q_kind, cache_kind, G)) e = launch_decode_mfma(a, cache_kind, head_size, stream);
-  else if (q_kind == KF32 && cache_kind == KF32) e = run_decode_d<float, KF32>(a, head_size, G, stream);
+  if (a.split_waves > 0) return launch_decode_mfma(a, cache_kind, head_size, stream);
+  if (q_kind == KF32 && cache_kind == KF32) e = run_decode_d<float, KF32>(a, head_size, G, stream);
   else if (q_kind == KBF16 && cache_kind == KBF16) e = run_decode_d<uint16_t, KBF16>(a, head_size, G, stream);
   else if (q_kind == KBF16 && cache_kind == KFP8) e = run_decode_d<uint16_t, KFP8>(a, head_size, G, stream);
   else return hipErrorInvalidValue;

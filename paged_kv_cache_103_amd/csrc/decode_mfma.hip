@@ -25,6 +25,7 @@
 //    multiplies the score, its V scale the probability used in PV.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -101,172 +102,181 @@ __device__ __forceinline__ void load_pair(PairRegs<CK, D>& r, const uint8_t* kca
   }
 }
 
-template <int CK, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mfma_kernel(DecodeArgs a) {
+// Running state of one wave over its keys: O^T (column = head), the running
+// max m (log2 units, uniform over the lane groups) and the partial sum of
+// exponentials of this lane's keys.
+template <int D>
+struct WaveAcc {
+  f32x4 o[D / 16];
+  float m, lsum;
+};
+
+// Scores, online softmax and PV for one pair of blocks (b, b+1). EDGE pairs
+// straddle the window start or the context end and carry the masking code.
+// Keys of the pair outside [lo, kend) are masked: kend is the end of the
+// wave's segment of the stream (at most the context end), so a pair whose
+// second block belongs to the next segment, or lies past the context (and
+// then re-reads the first block), contributes only its own keys.
+template <int CK, int D, bool EDGE>
+__device__ __forceinline__ void pair_step(WaveAcc<D>& acc, const PairRegs<CK, D>& r, const u32x4* qf,
+                                          size_t phys0, size_t phys1, int b, int lo, int ctx,
+                                          const DecodeArgs& a, int c16, int q4) {
+  // (ctx is the segment's exclusive key end here)
   using S = MfmaDecodeShape<CK, D>;
   constexpr int E = S::E, DS = S::DS, DT = S::DT;
-  __shared__ float w_m[4][16], w_l[4][16];
-  __shared__ float w_o[4][16][D];
+  f32x4* o = acc.o;
+  float& m = acc.m;
+  float& lsum = acc.lsum;
 
-  const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c16 = lane & 15, q4 = lane >> 4;
-  const int G = a.num_heads / a.num_kv_heads;
-
-  int qrow = s;
-  if (a.cu_seqlens != nullptr) {
-    const int q0 = a.cu_seqlens[s];
-    if (a.cu_seqlens[s + 1] - q0 != 1) return;
-    qrow = q0;
+  // ---- scores S^T (2 tiles of 16 permuted keys x 16 heads) ----
+  f32x4 st[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+  st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < DS; ++j) {
+    u32x4 kf;
+    if constexpr (E == 2) {
+      kf = r.k[kt * DS + j];
+    } else {
+      const u32x4& w = r.k[kt * (DS / 2) + (j >> 1)];
+      kf = (j & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
+    }
+    st[kt] = mfma_bf16_16x16x32(kf, qf[j], st[kt]);
   }
-  const int ctx = a.context_lens[s];
-  const int lo = a.window > 0 ? max(0, ctx - a.window) : 0;
-  const int b_first = lo >> 4, b_last = (ctx - 1) >> 4;
-  const int nparts = (b_last - b_first + a.pb) / a.pb;
-  if (part >= nparts) return;
-  const int blk0 = b_first + part * a.pb;
-  const int blk1 = min(blk0 + a.pb, b_last + 1);
-
-  u32x4 qf[DS];
-  f32x4 o[DT];
+  }
+  // this lane's keys: b*16 + 8*q4 + 4*kt + r, all in block b + q4/2
+  float ks = a.scale_log2, vs = 1.f;
+  if constexpr (CK == KFP8) {
+  const size_t phys = (q4 >> 1) ? phys1 : phys0;
+  ks *= a.k_scale[phys];
+  vs = a.v_scale[phys];
+  }
+  const int key0 = b * 16 + 8 * q4;
+  float x[2][4];
+  float tmax = -INFINITY;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
-
-  const size_t head_stride = (size_t)a.num_kv_heads * S::TILE;
-  const uint8_t* kcache = reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)g * S::TILE;
-  const uint8_t* vcache = reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * S::TILE;
-  const int* bt = a.block_table + (size_t)s * a.bt_stride;
-
-  // wave-strided pairs of blocks; several waves per SIMD keep loads in flight
-  // (pairs that straddle the window start or the context end take the
-  // masked variant of the step; interior pairs carry no masking code)
-  auto step = [&](auto edge_tag, const PairRegs<CK, D>& r, size_t phys0, size_t phys1, int b) {
-    constexpr bool EDGE = decltype(edge_tag)::value;
-
-    // ---- scores S^T (2 tiles of 16 permuted keys x 16 heads) ----
-    f32x4 st[2];
+  for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < DS; ++j) {
-        u32x4 kf;
-        if constexpr (E == 2) {
-          kf = r.k[kt * DS + j];
-        } else {
-          const u32x4& w = r.k[kt * (DS / 2) + (j >> 1)];
-          kf = (j & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
-        }
-        st[kt] = mfma_bf16_16x16x32(kf, qf[j], st[kt]);
-      }
-    }
-    // this lane's keys: b*16 + 8*q4 + 4*kt + r, all in block b + q4/2
-    float ks = a.scale_log2, vs = 1.f;
-    if constexpr (CK == KFP8) {
-      const size_t phys = (q4 >> 1) ? phys1 : phys0;
-      ks *= a.k_scale[phys];
-      vs = a.v_scale[phys];
-    }
-    const int key0 = b * 16 + 8 * q4;
-    float x[2][4];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        float v = st[kt][rr] * ks;
-        if constexpr (EDGE) {
-          const int kp = key0 + 4 * kt + rr;
-          v = (kp >= lo && kp < ctx) ? v : -INFINITY;
-        }
-        x[kt][rr] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = strided_max<16>(tmax);
-    const float mn = fmaxf(m, tmax);  // finite: every pair has a key in [lo, ctx)
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    m = mn;
-    float ps = 0.f, pv[2][4];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float p = __builtin_amdgcn_exp2f(x[kt][rr] - mn);
-        ps += p;
-        pv[kt][rr] = p * vs;
-      }
-    lsum = lsum * alpha + ps;
-    if (__any(alpha != 1.f)) {  // the running max rarely moves after the first blocks
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        o[dt][0] *= alpha; o[dt][1] *= alpha; o[dt][2] *= alpha; o[dt][3] *= alpha;
-      }
-    }
-    // P^T operand: logical k 8*q4 + e <-> key 8*q4 + e (e = 4*kt + rr)
-    u32x4 ph, pl;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float a0 = pv[t >> 1][(t & 1) * 2], a1 = pv[t >> 1][(t & 1) * 2 + 1];
-      const uint32_t hi = pack_bf16x2(a0, a1);
-      ph[t] = hi;
-      pl[t] = pack_bf16x2(a0 - bf16_lo(hi), a1 - bf16_hi(hi));
-    }
-    // value slices of keys >= ctx may hold anything (even NaN): zero them
-    uint32_t vmask[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+  for (int rr = 0; rr < 4; ++rr) {
+    float v = st[kt][rr] * ks;
     if constexpr (EDGE) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int k0 = key0 + 2 * t;
-        vmask[t] = (k0 < ctx ? 0x0000ffffu : 0u) | (k0 + 1 < ctx ? 0xffff0000u : 0u);
-      }
+      const int kp = key0 + 4 * kt + rr;
+      v = (kp >= lo && kp < ctx) ? v : -INFINITY;
     }
-    // ---- O^T += V^T P^T ----
+    x[kt][rr] = v;
+    tmax = fmaxf(tmax, v);
+  }
+  tmax = strided_max<16>(tmax);
+  // Lazy rescaling: the running max moves only when this pair's max exceeds
+  // it by more than 2^8 (p stays below 256 otherwise); the final division
+  // uses the same max. tmax is finite: every pair has a key in [lo, ctx).
+  const bool up = tmax > m + 8.f;
+  if (__any(up)) {
+    const float alpha = up ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;
+    m = up ? tmax : m;
+    lsum *= alpha;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      u32x4 vf;
-      if constexpr (E == 2) {
-        vf = r.v[dt];
-      } else {
-        const u32x4& w = r.v[dt >> 1];
-        vf = (dt & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
-      }
-      if constexpr (EDGE) {
-        vf[0] &= vmask[0]; vf[1] &= vmask[1]; vf[2] &= vmask[2]; vf[3] &= vmask[3];
-      }
-      o[dt] = mfma_bf16_16x16x32(vf, ph, o[dt]);
-      o[dt] = mfma_bf16_16x16x32(vf, pl, o[dt]);
+      o[dt][0] *= alpha; o[dt][1] *= alpha; o[dt][2] *= alpha; o[dt][3] *= alpha;
     }
+  }
+  float ps = 0.f, pv[2][4];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float p = __builtin_amdgcn_exp2f(x[kt][rr] - m);
+      ps += p;
+      pv[kt][rr] = p * vs;
+    }
+  lsum += ps;
+  // P^T operand: logical k 8*q4 + e <-> key 8*q4 + e (e = 4*kt + rr)
+  u32x4 ph, pl;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+  const float a0 = pv[t >> 1][(t & 1) * 2], a1 = pv[t >> 1][(t & 1) * 2 + 1];
+  const uint32_t hi = pack_bf16x2(a0, a1);
+  ph[t] = hi;
+  pl[t] = pack_bf16x2(a0 - bf16_lo(hi), a1 - bf16_hi(hi));
+  }
+  // value slices of keys past the segment may hold anything (even NaN): zero them
+  uint32_t vmask[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+  if constexpr (EDGE) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int k0 = key0 + 2 * t;
+    vmask[t] = (k0 < ctx ? 0x0000ffffu : 0u) | (k0 + 1 < ctx ? 0xffff0000u : 0u);
+  }
+  }
+  // ---- O^T += V^T P^T ----
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+  u32x4 vf;
+  if constexpr (E == 2) {
+    vf = r.v[dt];
+  } else {
+    const u32x4& w = r.v[dt >> 1];
+    vf = (dt & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
+  }
+  if constexpr (EDGE) {
+    vf[0] &= vmask[0]; vf[1] &= vmask[1]; vf[2] &= vmask[2]; vf[3] &= vmask[3];
+  }
+  o[dt] = mfma_bf16_16x16x32(vf, ph, o[dt]);
+  o[dt] = mfma_bf16_16x16x32(vf, pl, o[dt]);
+  }
+}
+
+// Writes one wave's result for its (sequence, KV head, partition): the
+// normalised output when the sequence has one partition, else the partition's
+// (max, sum, unnormalised output) for the merge kernel.
+template <int D>
+__device__ __forceinline__ void wave_write(WaveAcc<D>& acc, const DecodeArgs& a, int slot, int qrow, int g, int G,
+                                           bool single, int c16, int q4) {
+  const float L = strided_sum<16>(acc.lsum);
+  if (c16 >= G) return;
+  if (single) {
+    const float inv = 1.f / L;
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * a.num_heads + g * G + c16) * D + 4 * q4;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      uint2 w;
+      w.x = pack_bf16x2(acc.o[dt][0] * inv, acc.o[dt][1] * inv);
+      w.y = pack_bf16x2(acc.o[dt][2] * inv, acc.o[dt][3] * inv);
+      *reinterpret_cast<uint2*>(op + dt * 16) = w;
+    }
+  } else {
+    const size_t rec = (size_t)slot * G + c16;
+    float* op = a.part_o + rec * D + 4 * q4;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(op + dt * 16) = acc.o[dt];
+    if (q4 == 0) {
+      a.part_ml[rec * 2] = acc.m;
+      a.part_ml[rec * 2 + 1] = L;
+    }
+  }
+}
+
+// Blocks of one partition not taken by the wave: the running pair loop with
+// the next pair's loads in flight while one is computed.
+template <int CK, int D>
+__device__ __forceinline__ void wave_blocks(WaveAcc<D>& acc, const u32x4* qf, const uint8_t* kcache,
+                                            const uint8_t* vcache, const int* bt, int b, int step, int blk1,
+                                            int lo, int ctx, size_t head_stride, const DecodeArgs& a, int c16,
+                                            int q4) {
+  auto run = [&](const PairRegs<CK, D>& r, size_t p0, size_t p1, int bb) {
+    if (bb * 16 < lo || bb * 16 + 32 > ctx) pair_step<CK, D, true>(acc, r, qf, p0, p1, bb, lo, ctx, a, c16, q4);
+    else pair_step<CK, D, false>(acc, r, qf, p0, p1, bb, lo, ctx, a, c16, q4);
   };
-  auto run = [&](const PairRegs<CK, D>& r, size_t p0, size_t p1, int b) {
-    if (b * 16 < lo || b * 16 + 32 > ctx) step(std::true_type{}, r, p0, p1, b);
-    else step(std::false_type{}, r, p0, p1, b);
-  };
-  // The wave's next pair is always in flight while one is computed (two
-  // register buffers, alternating).
   PairRegs<CK, D> ra, rb;
   size_t a0 = 0, a1 = 0, b0 = 0, b1 = 0;
-  int b = blk0 + 2 * wave;
   if (b < blk1) {
     a0 = (size_t)bt[b];
     a1 = (b + 1 < blk1) ? (size_t)bt[b + 1] : a0;
     load_pair<CK, D>(ra, kcache, vcache, a0, a1, head_stride, c16, q4);
   }
-  // queries of the group as the B operand (column = head; columns >= G are 0)
-#pragma unroll
-  for (int j = 0; j < DS; ++j) {
-    if (c16 < G) {
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) +
-                           ((size_t)qrow * a.num_heads + g * G + c16) * D + kstep_d0<E>(j, q4);
-      qf[j] = load16(qp);
-    } else {
-      qf[j] = u32x4{0, 0, 0, 0};
-    }
-  }
-
   while (b < blk1) {
-    const int bn = b + 8;
+    const int bn = b + step;
     if (bn < blk1) {
       b0 = (size_t)bt[bn];
       b1 = (bn + 1 < blk1) ? (size_t)bt[bn + 1] : b0;
@@ -274,7 +284,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     run(ra, a0, a1, b);
     if (bn >= blk1) break;
-    const int bnn = bn + 8;
+    const int bnn = bn + step;
     if (bnn < blk1) {
       a0 = (size_t)bt[bnn];
       a1 = (bnn + 1 < blk1) ? (size_t)bt[bnn + 1] : a0;
@@ -283,55 +293,223 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     run(rb, b0, b1, bn);
     b = bnn;
   }
+}
 
-  // ---- merge the 4 waves; write the output or this partition's summary ----
-  lsum = strided_sum<16>(lsum);
-  if (q4 == 0) { w_m[wave][c16] = m; w_l[wave][c16] = lsum; }
+template <int CK, int D>
+__device__ __forceinline__ void load_query(u32x4* qf, const DecodeArgs& a, int qrow, int g, int G, int c16,
+                                           int q4) {
+  constexpr int E = CacheElem<CK>::bytes;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) w_o[wave][c16][dt * 16 + 4 * q4 + rr] = o[dt][rr];
-  __syncthreads();
-
-  const bool single = (nparts == 1);
-  for (int e = threadIdx.x; e < G * D; e += 256) {
-    const int h = e / D, d = e % D;
-    float M = w_m[0][h];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, w_m[w][h]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float c = __builtin_amdgcn_exp2f(w_m[w][h] - M);
-      L += w_l[w][h] * c;
-      O += w_o[w][h][d] * c;
-    }
-    const int hq = g * G + h;
-    if (single) {
-      reinterpret_cast<uint16_t*>(a.out)[((size_t)qrow * a.num_heads + hq) * D + d] = f32_to_bf16(O / L);
+  for (int j = 0; j < D / 32; ++j) {
+    if (c16 < G) {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) +
+                           ((size_t)qrow * a.num_heads + g * G + c16) * D + kstep_d0<E>(j, q4);
+      qf[j] = load16(qp);
     } else {
-      const size_t slot = ((size_t)s * a.num_heads + hq) * a.max_parts + part;
-      a.part_o[slot * D + d] = O;
-      if (d == 0) {
-        a.part_ml[slot * 2] = M;
-        a.part_ml[slot * 2 + 1] = L;
-      }
+      qf[j] = u32x4{0, 0, 0, 0};
     }
   }
 }
 
+// Blocks of sequence s's key range [lo, ctx) (0 for rows of longer chunks
+// in a mixed batch, which the prefill kernel serves).
+__device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int s, int& qrow, int& ctx, int& lo) {
+  qrow = s;
+  ctx = 0;
+  lo = 0;
+  if (a.cu_seqlens != nullptr) {
+    const int q0 = a.cu_seqlens[s];
+    if (a.cu_seqlens[s + 1] - q0 != 1) return 0;
+    qrow = q0;
+  }
+  ctx = a.context_lens[s];
+  lo = a.window > 0 ? max(0, ctx - a.window) : 0;
+  return ((ctx - 1) >> 4) - (lo >> 4) + 1;
+}
+
+// Exclusive prefix sums of seq_blocks over the sequences, into psum[0..S]
+// (LDS), using 256 scan slots after them. Returns the total.
+__device__ __forceinline__ int block_prefix(const DecodeArgs& a, int* psum) {
+  int* scan = psum + a.num_seqs + 1;
+  const int tid = threadIdx.x;
+  int running = 0;
+  for (int base = 0; base < a.num_seqs; base += 256) {
+    const int s = base + tid;
+    int n = 0;
+    if (s < a.num_seqs) {
+      int qr, cx, l0;
+      n = seq_blocks(a, s, qr, cx, l0);
+    }
+    scan[tid] = n;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    if (s < a.num_seqs) psum[s] = running + scan[tid] - n;
+    running += scan[255];
+    __syncthreads();
+  }
+  if (tid == 0) psum[a.num_seqs] = running;
+  __syncthreads();
+  return running;
+}
+
+// Blocks each wave takes: an even share of T block-heads, at least 8 and even.
+__device__ __forceinline__ int split_chunk(int total, int nwaves) {
+  int c = (total + nwaves - 1) / nwaves;
+  c = max(c, 8);
+  return (c + 1) & ~1;
+}
+
+// Decode with an even split: the (sequence, KV head) block streams, sequence
+// major, are laid end to end (T block-heads in all) and wave w takes
+// [w*C, (w+1)*C) with C = ceil(T / waves). A wave walks the one to few
+// stream segments in its range on its own (no workgroup barrier in the loop);
+// a stream covered by one segment is finished in place, others leave one
+// (max, sum, unnormalised output) summary per segment in slot wave + stream
+// for the merge kernel.
+template <int CK, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mfma_split(
+    DecodeArgs a) {
+  using S = MfmaDecodeShape<CK, D>;
+  extern __shared__ int psum[];  // [num_seqs + 1] block prefix sums, then 256 scan slots
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, q4 = lane >> 4;
+  const int H = a.num_kv_heads;
+  const int G = a.num_heads / H;
+
+  const int per_head = block_prefix(a, psum);
+  const long long T = (long long)per_head * H;
+  const int C = split_chunk((int)min<long long>(T, 0x7fffffff), a.split_waves);
+  if (blockIdx.x == 0) {  // for the merge kernel
+    if (tid == 0) a.meta[0] = C;
+    for (int s = tid; s <= a.num_seqs; s += 256) a.meta[1 + s] = psum[s];
+  }
+
+  const int w = blockIdx.x * 4 + wave;
+  const long long x_end = min<long long>((long long)(w + 1) * C, T);
+  const size_t head_stride = (size_t)H * S::TILE;
+  long long x = (long long)w * C;
+  while (x < x_end) {
+    // stream containing block-head x: sequence = last s with psum[s]*H <= x
+    int lo_s = 0, hi_s = a.num_seqs;  // psum[lo_s]*H <= x < psum[hi_s]*H
+    while (hi_s - lo_s > 1) {
+      const int mid = (lo_s + hi_s) >> 1;
+      if ((long long)psum[mid] * H <= x) lo_s = mid; else hi_s = mid;
+    }
+    const int s = lo_s;
+    const int nb = psum[s + 1] - psum[s];
+    const long long base = (long long)psum[s] * H;
+    const int g = (int)((x - base) / nb);
+    const long long sstart = base + (long long)g * nb;  // this stream's first block-head
+    const long long seg_end = min(x_end, sstart + nb);
+    int qrow, ctx, lo;
+    seq_blocks(a, s, qrow, ctx, lo);
+    const int blk0 = (lo >> 4) + (int)(x - sstart);
+    const int blk1 = (lo >> 4) + (int)(seg_end - sstart);
+    const int kend = min(ctx, blk1 * 16);
+
+    u32x4 qf[S::DS];
+    load_query<CK, D>(qf, a, qrow, g, G, c16, q4);
+    WaveAcc<D> acc;
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) acc.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc.m = -INFINITY;
+    acc.lsum = 0.f;
+    const uint8_t* kcache = reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)g * S::TILE;
+    const uint8_t* vcache = reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * S::TILE;
+    wave_blocks<CK, D>(acc, qf, kcache, vcache, a.block_table + (size_t)s * a.bt_stride, blk0, 2, blk1, lo,
+                       kend, head_stride, a, c16, q4);
+    const int stream = s * H + g;
+    const bool single = (sstart / C) == ((sstart + nb - 1) / C);
+    wave_write<D>(acc, a, w + stream, qrow, g, G, single, c16, q4);
+    x = seg_end;
+  }
+}
+
+// Exact merge of one stream's segment summaries: one wave per (sequence,
+// query head); M = max m_i, L = sum l_i 2^(m_i - M), out = sum o_i 2^(m_i - M) / L.
+template <int D>
+__global__ __launch_bounds__(256) void decode_split_merge(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (idx >= a.num_seqs * a.num_heads) return;
+  const int H = a.num_kv_heads, G = a.num_heads / H;
+  const int s = idx / a.num_heads, hq = idx % a.num_heads, g = hq / G, h = hq % G;
+  const int* psum = a.meta + 1;
+  const int nb = psum[s + 1] - psum[s];
+  if (nb == 0) return;
+  const int C = a.meta[0];
+  const long long sstart = (long long)psum[s] * H + (long long)g * nb;
+  const int w0 = (int)(sstart / C), w1 = (int)((sstart + nb - 1) / C);
+  if (w0 == w1) return;  // finished in place
+  int qrow = s;
+  if (a.cu_seqlens != nullptr) qrow = a.cu_seqlens[s];
+  const int stream = s * H + g;
+  const int n = w1 - w0 + 1;
+  // slot of segment i: w0 + i + stream
+  float M = -INFINITY;
+  for (int i = lane; i < n; i += 64) M = fmaxf(M, a.part_ml[((size_t)(w0 + i + stream) * G + h) * 2]);
+  M = strided_max<1>(M);
+  constexpr int DL = D / 64;
+  float o[DL];
+#pragma unroll
+  for (int k = 0; k < DL; ++k) o[k] = 0.f;
+  float L = 0.f;
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int i = i0 + lane;
+    const size_t slot = (size_t)(w0 + i + stream);
+    const float wgt = (i < n) ? __builtin_amdgcn_exp2f(a.part_ml[(slot * G + h) * 2] - M) : 0.f;
+    if (i < n) L += a.part_ml[(slot * G + h) * 2 + 1] * wgt;
+    const int cnt = min(64, n - i0);
+    for (int j0 = 0; j0 < cnt; j0 += 8) {
+      float v[8][DL];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float* row = a.part_o + ((size_t)(w0 + i0 + j0 + u + stream) * G + h) * D;
+#pragma unroll
+        for (int k = 0; k < DL; ++k) v[u][k] = (j0 + u < cnt) ? row[k * 64 + lane] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), (j0 + u) & 63));
+#pragma unroll
+        for (int k = 0; k < DL; ++k) o[k] = fmaf(wj, v[u][k], o[k]);
+      }
+    }
+  }
+  L = strided_sum<1>(L);
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int k = 0; k < DL; ++k)
+    reinterpret_cast<uint16_t*>(a.out)[((size_t)qrow * a.num_heads + hq) * D + k * 64 + lane] =
+        f32_to_bf16(o[k] * inv);
+}
+
 hipError_t launch_decode_mfma(const DecodeArgs& a, int cache_kind, int head_size, hipStream_t st) {
-  dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+  const dim3 grid((unsigned)(a.split_waves / 4));
+  const size_t lds = (size_t)(a.num_seqs + 1 + 256) * sizeof(int);
   if (cache_kind == KBF16 && head_size == 128)
-    hipLaunchKernelGGL((decode_mfma_kernel<KBF16, 128>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_mfma_split<KBF16, 128>), grid, dim3(256), lds, st, a);
   else if (cache_kind == KBF16 && head_size == 64)
-    hipLaunchKernelGGL((decode_mfma_kernel<KBF16, 64>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_mfma_split<KBF16, 64>), grid, dim3(256), lds, st, a);
   else if (cache_kind == KFP8 && head_size == 128)
-    hipLaunchKernelGGL((decode_mfma_kernel<KFP8, 128>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_mfma_split<KFP8, 128>), grid, dim3(256), lds, st, a);
   else if (cache_kind == KFP8 && head_size == 64)
-    hipLaunchKernelGGL((decode_mfma_kernel<KFP8, 64>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_mfma_split<KFP8, 64>), grid, dim3(256), lds, st, a);
   else
     return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int waves = a.num_seqs * a.num_heads;
+  if (head_size == 128)
+    hipLaunchKernelGGL((decode_split_merge<128>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_split_merge<64>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -130,22 +130,64 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
   return hip_status(e, "reshape_and_cache launch");
 }
 
+static int elem_bytes(pa_dtype d) { return d == PA_F32 ? 4 : (d == PA_BF16 ? 2 : 1); }
+
+// The supported (query, cache) pairs are (f32, f32), (bf16, bf16) and
+// (bf16, fp8): the cache type decides the query type.
+static pa::DecodePlan make_plan(int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_size, pa_dtype cache_dtype,
+                                int32_t sliding_window) {
+  const int q_kind = cache_dtype == PA_F32 ? PA_F32 : PA_BF16;
+  return pa::plan_decode(num_seqs, max_context_len, num_heads, num_kv_heads, head_size, q_kind,
+                         (int)cache_dtype, sliding_window);
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Points the decode arguments' summary buffers into the workspace.
+static void bind_workspace(pa::DecodeArgs& a, const pa::DecodePlan& plan, void* workspace, int32_t num_seqs,
+                           int32_t num_heads, int32_t num_kv_heads, int32_t head_size) {
+  a.pb = plan.pb;
+  a.max_parts = plan.max_parts;
+  a.split_waves = plan.split_waves;
+  a.meta = nullptr;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  if (workspace == nullptr) return;
+  char* ws = static_cast<char*>(workspace);
+  if (plan.split_waves > 0) {
+    const int G = num_heads / num_kv_heads;
+    const size_t slots = (size_t)plan.split_waves + (size_t)num_seqs * num_kv_heads;
+    a.meta = reinterpret_cast<int*>(ws);
+    ws += align256((size_t)(num_seqs + 2) * sizeof(int));
+    a.part_o = reinterpret_cast<float*>(ws);
+    ws += align256(slots * G * head_size * sizeof(float));
+    a.part_ml = reinterpret_cast<float*>(ws);
+  } else if (plan.max_parts > 1) {
+    const size_t slots = (size_t)num_seqs * num_heads * plan.max_parts;
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_ml = reinterpret_cast<float*>(ws) + slots * head_size;
+  }
+}
+
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
-                                 int32_t num_kv_heads, int32_t head_size, int32_t sliding_window) {
+                                 int32_t num_kv_heads, int32_t head_size, pa_dtype cache_dtype,
+                                 int32_t sliding_window) {
   if (num_seqs <= 0 || max_context_len <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0)
     return 0;
-  const pa::DecodePlan plan = pa::plan_decode(num_seqs, max_context_len, num_kv_heads, sliding_window);
-  return pa::decode_workspace_bytes(plan, num_seqs, num_heads, head_size);
+  const pa::DecodePlan plan = make_plan(num_seqs, max_context_len, num_heads, num_kv_heads, head_size,
+                                        cache_dtype, sliding_window);
+  return pa::decode_workspace_bytes(plan, num_seqs, num_heads, num_kv_heads, head_size);
 }
 
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len,
                                   int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
-                                  int32_t head_size, int32_t sliding_window) {
+                                  int32_t head_size, pa_dtype cache_dtype, int32_t sliding_window) {
   // the prefill tiles need no scratch; one-token rows use the decode plan,
   // and there are none when every sequence has max_q_len > 1 tokens
   if (max_q_len > 1 && (long long)num_q_tokens == (long long)num_seqs * max_q_len) return 0;
   return pa_decode_workspace_bytes(num_seqs, max_context_len, num_heads, num_kv_heads, head_size,
-                                   sliding_window);
+                                   cache_dtype, sliding_window);
 }
 
 pa_status pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
@@ -164,8 +206,9 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
     g_last_error.clear();
     return PA_OK;
   }
-  const pa::DecodePlan plan = pa::plan_decode(num_seqs, max_context_len, num_kv_heads, sliding_window);
-  const size_t need = pa::decode_workspace_bytes(plan, num_seqs, num_heads, head_size);
+  const pa::DecodePlan plan = make_plan(num_seqs, max_context_len, num_heads, num_kv_heads, head_size,
+                                        cache_dtype, sliding_window);
+  const size_t need = pa::decode_workspace_bytes(plan, num_seqs, num_heads, num_kv_heads, head_size);
   if (workspace_bytes < need || (need > 0 && workspace == nullptr))
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes (got %zu)", need,
                 workspace_bytes);
@@ -179,16 +222,12 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
   a.block_table = block_table;
   a.context_lens = context_lens;
   a.cu_seqlens = nullptr;
-  const size_t slots = (size_t)num_seqs * num_heads * plan.max_parts;
-  a.part_o = need ? static_cast<float*>(workspace) : nullptr;
-  a.part_ml = need ? static_cast<float*>(workspace) + slots * head_size : nullptr;
+  bind_workspace(a, plan, need ? workspace : nullptr, num_seqs, num_heads, num_kv_heads, head_size);
   a.bt_stride = block_table_stride;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;
   a.window = sliding_window;
-  a.pb = plan.pb;
-  a.max_parts = plan.max_parts;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = pa::launch_decode(a, (int)q_dtype, (int)cache_dtype, head_size, (hipStream_t)stream);
   return hip_status(e, "decode launch");
@@ -227,8 +266,10 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
   // Rows with one query token may exist unless every sequence provably has
   // max_q_len > 1 tokens (the only case the host scalars can prove).
   const bool any_single = !(has_chunks && (long long)num_q_tokens == (long long)num_seqs * max_q_len);
-  const pa::DecodePlan plan = pa::plan_decode(num_seqs, max_context_len, num_kv_heads, sliding_window);
-  const size_t need = any_single ? pa::decode_workspace_bytes(plan, num_seqs, num_heads, head_size) : 0;
+  const pa::DecodePlan plan = make_plan(num_seqs, max_context_len, num_heads, num_kv_heads, head_size,
+                                        cache_dtype, sliding_window);
+  const size_t need =
+      any_single ? pa::decode_workspace_bytes(plan, num_seqs, num_heads, num_kv_heads, head_size) : 0;
   if (workspace_bytes < need || (need > 0 && workspace == nullptr))
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "prefill needs %zu workspace bytes (got %zu)", need,
                 workspace_bytes);
@@ -246,16 +287,12 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
   d.block_table = block_table;
   d.context_lens = context_lens;
   d.cu_seqlens = cu_seqlens;
-  const size_t slots = (size_t)num_seqs * num_heads * plan.max_parts;
-  d.part_o = need ? static_cast<float*>(workspace) : nullptr;
-  d.part_ml = need ? static_cast<float*>(workspace) + slots * head_size : nullptr;
+  bind_workspace(d, plan, need ? workspace : nullptr, num_seqs, num_heads, num_kv_heads, head_size);
   d.bt_stride = block_table_stride;
   d.num_seqs = num_seqs;
   d.num_heads = num_heads;
   d.num_kv_heads = num_kv_heads;
   d.window = sliding_window;
-  d.pb = plan.pb;
-  d.max_parts = plan.max_parts;
   d.scale_log2 = scale_log2;
   if (any_single) {
     hipError_t e = pa::launch_decode(d, (int)q_dtype, (int)cache_dtype, head_size, hs);

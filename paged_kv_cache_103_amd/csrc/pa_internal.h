@@ -22,12 +22,23 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
 // Split-K plan of the decode kernel: every sequence's key blocks are cut into
 // partitions of `pb` blocks; `max_parts` bounds the partitions of any
 // sequence. One partition means no partial results and no merge.
+//
+// The matrix-core kernel instead splits the concatenated (sequence, KV head)
+// block streams evenly over a fixed number of waves (`split_waves` > 0); each
+// wave writes one summary per stream segment it covers, in slot
+// wave + stream (unique, since consecutive segments advance exactly one of
+// the two).
 struct DecodePlan {
   int pb;
   int max_parts;
+  int split_waves;  // > 0: even split over this many waves (matrix-core kernel)
 };
-DecodePlan plan_decode(int num_seqs, int max_context_len, int num_kv_heads, int sliding_window);
-size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int num_heads, int head_size);
+DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num_kv_heads, int head_size,
+                       int q_kind, int cache_kind, int sliding_window);
+size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int num_heads, int num_kv_heads,
+                              int head_size);
+bool decode_uses_mfma(int q_kind, int cache_kind, int group);
+int device_cu_count();
 
 struct DecodeArgs {
   void* out;
@@ -39,8 +50,10 @@ struct DecodeArgs {
   const int* block_table;
   const int* context_lens;
   const int* cu_seqlens;  // null: pure decode (query row s); else rows with q_len == 1 only
-  float* part_o;          // [num_seqs][num_heads][max_parts][head_size]
-  float* part_ml;         // [num_seqs][num_heads][max_parts][2]: running max (log2 units), sum
+  float* part_o;          // pb plan: [num_seqs][num_heads][max_parts][head_size]
+                          // split plan: [slots][group][head_size]
+  float* part_ml;         // running max (log2 units) and sum per summary
+  int* meta;              // split plan: [0] = blocks per wave, [1 + s] = block prefix sums
   int bt_stride;
   int num_seqs;
   int num_heads;
@@ -48,6 +61,7 @@ struct DecodeArgs {
   int window;
   int pb;
   int max_parts;
+  int split_waves;
   float scale_log2;  // softmax scale * log2(e)
 };
 

@@ -135,10 +135,16 @@ def test_prefill_rejects_bad_arguments(lib):
 
 def test_workspace_queries(lib):
     # short contexts: one partition, no workspace
-    assert lib.decode_workspace_bytes(4, 100, 8, 2, 64) == 0
-    ws = lib.decode_workspace_bytes(64, 8192, 32, 8, 128)
+    assert lib.decode_workspace_bytes(4, 30, 8, 2, 64, "f32") == 0
+    ws = lib.decode_workspace_bytes(64, 8192, 32, 8, 128, "bf16")
     assert ws > 0 and ws % 4 == 0
-    # a sliding window bounds the partitions whatever the context
-    assert lib.decode_workspace_bytes(128, 131072, 64, 8, 128, 128) == 0
-    assert lib.prefill_workspace_bytes(193, 2240, 2048, 67584, 32, 8, 128) == \
-        lib.decode_workspace_bytes(193, 67584, 32, 8, 128)
+    # a sliding window never needs more than full attention
+    assert lib.decode_workspace_bytes(128, 131072, 64, 8, 128, "fp8_e4m3", 128) <= \
+        lib.decode_workspace_bytes(128, 131072, 64, 8, 128, "fp8_e4m3", 0)
+    assert lib.decode_workspace_bytes(8, 131072, 8, 2, 64, "f32", 128) < \
+        lib.decode_workspace_bytes(8, 131072, 8, 2, 64, "f32", 0)
+    # the one-token rows of a mixed batch use the decode plan
+    assert lib.prefill_workspace_bytes(193, 2240, 2048, 67584, 32, 8, 128, "bf16") == \
+        lib.decode_workspace_bytes(193, 67584, 32, 8, 128, "bf16")
+    # no one-token rows possible: no workspace
+    assert lib.prefill_workspace_bytes(2, 600, 300, 5000, 32, 8, 128, "bf16") == 0

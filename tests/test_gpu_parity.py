@@ -32,7 +32,7 @@ def run_decode(b, out=None, **kw):
     m = b.meta(DEV)
     out = torch.empty_like(b.query) if out is None else out
     ws_bytes = pa.decode_workspace_bytes(b.num_seqs, b.max_context_len, b.num_heads, b.num_kv_heads,
-                                         b.head_size, b.sliding_window)
+                                         b.head_size, b.cache_dtype, b.sliding_window)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=DEV)
     pa.decode(out, b.query, b.k_cache, b.v_cache, m["block_table"], m["context_lens"],
               b.max_context_len, b.scale, b.k_scale, b.v_scale, b.sliding_window, ws, **kw)
@@ -43,7 +43,7 @@ def run_prefill(b, out=None):
     m = b.meta(DEV)
     out = torch.empty_like(b.query) if out is None else out
     ws_bytes = pa.prefill_workspace_bytes(b.num_seqs, b.num_q_tokens, b.max_q_len, b.max_context_len,
-                                          b.num_heads, b.num_kv_heads, b.head_size, b.sliding_window)
+                                          b.num_heads, b.num_kv_heads, b.head_size, b.cache_dtype, b.sliding_window)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=DEV)
     pa.prefill_chunk(out, b.query, b.k_cache, b.v_cache, m["block_table"], m["cu_seqlens"],
                      m["context_lens"], b.max_q_len, b.max_context_len, b.scale, b.k_scale, b.v_scale,
