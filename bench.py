@@ -148,6 +148,37 @@ def cpu_baseline(b, budget_s=15.0):
                       f"includes the oracle's own host gather through the block table, not the D2H copy"}
 
 
+def kernel_source_digest():
+    """sha256 over the sources of the decode path (kernel, shared device code,
+    plan/dispatch), used to tell whether a stored counter summary still
+    describes the kernel that runs."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("decode_mfma.hip", "decode.hip", "pa_device.h", "pa_internal.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_103_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per pa_decode launch on this workload from the committed
+    rocprofv3 counter summary (FETCH_SIZE, WRITE_SIZE scaled by the plain-copy
+    calibration), or None if missing or taken on another kernel version."""
+    import re
+    path = os.path.join(ROOT, "profiles", "decode_mfma_split_llama8b_decode.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    m = re.search(r"<!-- traffic (\{.*?\}) -->", text)
+    if not m:
+        return None
+    t = json.loads(m.group(1))
+    if t.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return int(t["fetch_bytes_per_launch"]) + int(t["write_bytes_per_launch"])
+
+
 def run_config(pa, torch, W, name, steps, warmup):
     b = W.make_config(name, device="cuda")
     torch.cuda.synchronize()
@@ -270,9 +301,10 @@ def main():
                                "heads, head 128, bf16 K/V and queries, 16-token blocks, one layer; "
                                "step = KV write of 64 tokens + paged decode",
                    "kv_bytes_per_step": dec["kv_bytes"], "pct_hbm_peak": round(100 * dec["kv_gbs_step"] / HBM_PEAK_GBS, 2)},
-        "roofline": {"bound": "hbm", "kernel": "pa_decode (partition kernel + merge kernel)",
+        "roofline": {"bound": "hbm", "kernel": "pa_decode call: decode_mfma_split + decode_split_merge",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(),
+                     "algorithmic_bytes_per_launch": dec["kv_bytes"]},
         "cpu_baseline": cpu,
         "mixed_step": {"value": round(mix["tokens_per_s"], 1), "unit": "tokens/s",
                        "ms_per_step": round(mix["step_ms"], 5),

@@ -73,6 +73,10 @@ __device__ __forceinline__ void load_pair(PairRegs<CK, D>& r, const uint8_t* kca
                                           size_t phys0, size_t phys1, size_t head_stride, int c16, int q4) {
   using S = MfmaDecodeShape<CK, D>;
   constexpr int E = S::E;
+  // bf16 tiles are streamed with nontemporal loads (faster on scattered
+  // tiles); fp8 tiles, half the size and read with 8-byte V loads, measured
+  // faster with ordinary loads
+  auto ld16 = [](const void* p) { return E == 2 ? load16_stream(p) : load16(p); };
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     const int kp = 8 * (c16 >> 2) + 4 * kt + (c16 & 3);  // this lane's key row in score tile kt
@@ -80,10 +84,10 @@ __device__ __forceinline__ void load_pair(PairRegs<CK, D>& r, const uint8_t* kca
     const uint8_t* row = kcache + phys * head_stride + (size_t)(kp & 15) * (D * E);
     if constexpr (E == 2) {
 #pragma unroll
-      for (int j = 0; j < S::DS; ++j) r.k[kt * S::DS + j] = load16(row + kstep_d0<E>(j, q4) * 2);
+      for (int j = 0; j < S::DS; ++j) r.k[kt * S::DS + j] = ld16(row + kstep_d0<E>(j, q4) * 2);
     } else {
 #pragma unroll
-      for (int c = 0; c < S::DS / 2; ++c) r.k[kt * (S::DS / 2) + c] = load16(row + 64 * c + 16 * q4);
+      for (int c = 0; c < S::DS / 2; ++c) r.k[kt * (S::DS / 2) + c] = ld16(row + 64 * c + 16 * q4);
     }
   }
   // V^T: lane group q reads keys 8q..8q+7 = block q/2, keys 8(q&1)..+8
@@ -91,7 +95,7 @@ __device__ __forceinline__ void load_pair(PairRegs<CK, D>& r, const uint8_t* kca
   const uint8_t* vt = vcache + vphys * head_stride + 8 * (q4 & 1) * E;
   if constexpr (E == 2) {
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) r.v[dt] = load16(vt + (size_t)(dt * 16 + c16) * 32);
+    for (int dt = 0; dt < D / 16; ++dt) r.v[dt] = ld16(vt + (size_t)(dt * 16 + c16) * 32);
   } else {
 #pragma unroll
     for (int dp = 0; dp < D / 32; ++dp) {
