@@ -23,7 +23,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libpa.so")
 
 ARCH = "gfx950"
-SOURCES = ["pa_api.cpp", "reshape_and_cache.hip", "decode.hip", "decode_mfma.hip", "prefill.hip"]
+SOURCES = ["pa_api.cpp", "reshape_and_cache.hip", "decode.hip", "decode_mfma.hip", "prefill.hip", "prefill_bf16.hip"]
 
 
 def hipcc() -> str:

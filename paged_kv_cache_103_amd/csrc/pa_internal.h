@@ -90,6 +90,8 @@ struct PrefillArgs {
 };
 int prefill_tokens_per_tile(int group);
 hipError_t launch_prefill(const PrefillArgs& args, int cache_kind, int head_size, hipStream_t stream);
+// bf16 caches: the 32x32x16 MFMA kernel with direct global->LDS copies.
+hipError_t launch_prefill_bf16(const PrefillArgs& args, int head_size, hipStream_t stream);
 bool prefill_supported(int q_kind, int cache_kind, int head_size, int group);
 
 }  // namespace pa

@@ -31,6 +31,8 @@
 // the most keys), and the KV head is the fastest-varying part of the
 // workgroup index so that the tiles of one head land on the same XCD.
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <type_traits>
 
@@ -472,8 +474,11 @@ static hipError_t run_prefill_g(const PrefillArgs& a, int G, hipStream_t st) {
 hipError_t launch_prefill(const PrefillArgs& a, int cache_kind, int head_size, hipStream_t stream) {
   const int G = a.num_heads / a.num_kv_heads;
   if (cache_kind == KBF16) {
-    if (head_size == 64) return run_prefill_g<KBF16, 64>(a, G, stream);
-    if (head_size == 128) return run_prefill_g<KBF16, 128>(a, G, stream);
+    if (getenv("PA_PREFILL_KERNEL") && strcmp(getenv("PA_PREFILL_KERNEL"), "mfma16") == 0) {
+      if (head_size == 64) return run_prefill_g<KBF16, 64>(a, G, stream);
+      if (head_size == 128) return run_prefill_g<KBF16, 128>(a, G, stream);
+    }
+    return launch_prefill_bf16(a, head_size, stream);
   } else if (cache_kind == KFP8) {
     if (head_size == 64) return run_prefill_g<KFP8, 64>(a, G, stream);
     if (head_size == 128) return run_prefill_g<KFP8, 128>(a, G, stream);

@@ -1,0 +1,450 @@
+// Chunked-prefill paged attention for bf16 KV caches on gfx950 matrix cores,
+// 32x32x16 bf16 MFMA with fp32 accumulation.
+//
+// What it computes: every query row of a chunk longer than one token attends
+// causally to its sequence's cached keys, read through the block table; query
+// row r of a chunk of q_len rows in a context of ctx tokens sits at position
+// ctx - q_len + r ("大模型推理优化学习笔记", "Chunked Prefill";
+// "从静态批处理到状态化推理集群", "Chunked prefill：在共置引擎里治理阶段干扰").
+// Each cached K/V row serves many queries, so the work is a dense contraction
+// ("大模型推理优化学习笔记", "计算密集与访存密集") and runs on MFMA.
+//
+// Shape of the work (one workgroup = 4 waves = 128 query columns of one KV
+// head: 128/G tokens x the G query heads of the group):
+//  * keys advance in steps of 32 (two 16-token blocks). A wave computes the
+//    32 x 32 score tile S^T = K Q^T of its 32 columns with head_size/16 MFMAs
+//    (queries are the B operand, kept in registers), then O^T += V^T P^T with
+//    head_size/32 output tiles x 2 key halves x 2 (P as bf16 hi + lo);
+//  * score rows are fed in a permuted key order, so that the accumulator of
+//    lane l holds, for its column, exactly the 8-key runs the PV B operand
+//    wants from it: probabilities never leave the lane. A column's 32 keys
+//    live in lanes l and l^32, so its running max needs one lane swap;
+//  * the loop is software-pipelined inside each wave: iteration i issues the
+//    score MFMAs of step i+1 and the PV MFMAs of step i-1 while the vector
+//    ALUs run the softmax of step i. The O^T rescale that a new running max
+//    asks for (lazy: only when the max grows by more than 2^8) is applied at
+//    the top of the next iteration, after step i-1's PV and before step i's;
+//  * K and V reach LDS by direct global->LDS copies into rings of three
+//    32-key slots; K is fetched three steps ahead and V one step ahead of
+//    their use, one barrier per step. The copies place 16-byte chunks so
+//    that the MFMA operand reads hit distinct LDS banks;
+//  * masks (causal edge, sliding window, context end) are evaluated only in
+//    the steps that cross an edge; values of keys past the context are
+//    zeroed in the last step, because the block of a partial last block may
+//    hold anything past the context.
+#include <math.h>
+
+#include <type_traits>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+#include "prefill_tiles.h"
+
+namespace pa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+template <int D>
+struct PfShape {
+  static constexpr int STEP = 32;            // keys per step (two blocks)
+  static constexpr int DK = D / 16;          // score MFMAs per step (k = 16 over head_size)
+  static constexpr int DT = D / 32;          // 32-row tiles of head_size in O^T
+  static constexpr int KSLOT = STEP * D;     // bf16 elements of one K slot: [32][D]
+  static constexpr int VSLOT = 2 * D * 16;   // one V slot: two [D][16] block tiles
+  static constexpr int SLOTS = 3;
+  static constexpr int COPIES = D / 64;      // 1 KiB copies per wave and operand per step
+  static constexpr int BLK_BYTES = 16 * D * 2;
+};
+
+// Chunk swizzles (16-byte chunk index XOR a function of the row), chosen so
+// that the 16 lanes the LDS serves together read 16 distinct bank groups:
+// K rows are read by 32 lanes (32 permuted keys, one chunk column each);
+// V^T rows by 32 lanes (32 consecutive rows, one of two chunks).
+template <int D>
+__device__ __forceinline__ int k_swizzle(int key) {
+  if constexpr (D == 128) return key & 15;
+  else return (key >> 1) & 7;
+}
+__device__ __forceinline__ int v_swizzle(int d) { return (d >> 3) & 1; }
+
+// p = hi + lo with hi = bf16(p) and lo = bf16(p - hi), for a pair of
+// probabilities packed as the PV MFMA operand wants them. hi's low half is
+// moved up with a byte permute (the compiler would otherwise round a0 again).
+__device__ __forceinline__ void split_bf16x2(float a0, float a1, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(a0, a1);
+  const float h0 = __uint_as_float(__builtin_amdgcn_perm(0u, hi, 0x01000c0cu));
+  const float h1 = __uint_as_float(hi & 0xffff0000u);
+  lo = pack_bf16x2(a0 - h0, a1 - h1);
+}
+
+// Score row m of a step holds this key of the step.
+__device__ __forceinline__ int step_key_of_row(int m) {
+  return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// N 16-byte global -> LDS copies per lane, from base + lane_offset[n] (base
+// uniform): lane i's chunk of copy n lands at byte lds_base + 1024 n + 16 i.
+// Written as inline assembly so that the compiler does not see an LDS store:
+// it would otherwise drain every outstanding copy before each LDS read of
+// the loop. Completion is tracked by the vector-memory counter (wait_vmcnt)
+// and made visible to the workgroup by a barrier. M0 holds the LDS base of
+// a copy (read when the copy issues) and is restored afterwards; a copy must
+// not directly follow a write of M0.
+template <int N>
+__device__ __forceinline__ void copy_to_lds(const void* base, const uint32_t* lane_offset, uint32_t lds_base) {
+  uint32_t saved;
+  if constexpr (N == 1) {
+    __asm__ volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(lane_offset[0]), "s"(base), "s"(lds_base)
+        : "memory");
+  } else {
+    static_assert(N == 2, "one or two copies");
+    __asm__ volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %3\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(lane_offset[0]), "v"(lane_offset[1]), "s"(base), "s"(lds_base)
+        : "memory");
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u16*)p);
+}
+
+// Workgroup barrier that does not wait for this wave's outstanding memory
+// operations (the copies of later steps stay in flight across it).
+__device__ __forceinline__ void step_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(PrefillArgs a) {
+  using S = PfShape<D>;
+  constexpr int TQ = 128 / G;
+  __shared__ __attribute__((aligned(16))) uint16_t kring[S::SLOTS * S::KSLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t vring[S::SLOTS * S::VSLOT];
+  __shared__ int sh_scan[256];
+  __shared__ int sh_found[3];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = blockIdx.x % a.num_kv_heads;
+  const PrefillTile tile = find_prefill_tile(a.cu_seqlens, a.num_seqs, TQ, blockIdx.x / a.num_kv_heads, sh_scan,
+                                             sh_found);
+  if (tile.seq < 0) return;
+  const int s = tile.seq;
+
+  // lengths and block ids are read-only for the kernel's lifetime: read them
+  // through the constant address space, so that the uniform ones take scalar
+  // loads (vector loads would share the counter of the in-flight copies)
+  typedef __attribute__((address_space(4))) const int cint;
+  const cint* cu = ((const cint*)(a.cu_seqlens));
+  const int q0 = cu[s];
+  const int qlen = cu[s + 1] - q0;
+  const int ctx = ((const cint*)(a.context_lens))[s];
+  const int tok0 = tile.tile * TQ;
+  const int ntok = min(TQ, qlen - tok0);
+  const int qpos_first = ctx - qlen + tok0;
+  const int qpos_last = qpos_first + ntok - 1;
+  const int W = a.window;
+  const int lo_first = W > 0 ? max(0, qpos_first - W + 1) : 0;
+  const int b_last = (ctx - 1) >> 4;
+  const cint* bt = ((const cint*)(a.block_table)) + (size_t)s * a.bt_stride;
+  const int jstart = (lo_first >> 5) << 5;
+  const int nsteps = (qpos_last - jstart) / 32 + 1;
+
+  // ---- this lane's column and its queries (B operand of S^T = K Q^T) ----
+  const int h = lane >> 5, c32 = lane & 31;
+  const int col = wave * 32 + c32;
+  const int tok = col / G, head = col % G;
+  const int qpos = qpos_first + tok;
+  // scores are max-reduced before scaling, so the scale must be positive: a
+  // negative scale flips the query signs instead (exact in bf16)
+  const bool neg = a.scale_log2 < 0.f;
+  float c = fabsf(a.scale_log2);
+  c = c > 0.f ? c : 1.17549435e-38f;  // scale 0 (uniform weights) as the smallest normal
+  u32x4 qf[S::DK];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) +
+                         ((size_t)(q0 + tok0 + tok) * a.num_heads + g * G + head) * D + 8 * h;
+    const uint32_t flip = neg ? 0x80008000u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < S::DK; ++ks) {
+      qf[ks] = tok < ntok ? load16(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+      qf[ks][0] ^= flip; qf[ks][1] ^= flip; qf[ks][2] ^= flip; qf[ks][3] ^= flip;
+    }
+  }
+
+  // ---- global -> LDS copies (one 16-byte chunk per lane, lane i to byte
+  // 16 i of a 1 KiB region); wave w copies half of block w/2 of the step.
+  // Blocks past the context re-read the last block (masked, zeroed).
+  const uint32_t head_stride = (uint32_t)a.num_kv_heads * S::BLK_BYTES;
+  const uint8_t* kcache = reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)g * S::BLK_BYTES;
+  const uint8_t* vcache = reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * S::BLK_BYTES;
+  const int b0 = jstart >> 4;
+  constexpr int CPR = D / 8;     // chunks per K row
+  constexpr int RPC = 64 / CPR;  // K rows per 1 KiB copy
+  uint32_t koff[S::COPIES], voff[S::COPIES];
+#pragma unroll
+  for (int n = 0; n < S::COPIES; ++n) {
+    const int row = 8 * (wave & 1) + n * RPC + lane / CPR;  // K row within the block
+    koff[n] = row * (2 * D) + 16 * ((lane % CPR) ^ k_swizzle<D>(16 * (wave >> 1) + row));
+    const int d = (D / 2) * (wave & 1) + 32 * n + lane / 2;  // V^T row within the block
+    voff[n] = d * 32 + 16 * ((lane & 1) ^ v_swizzle(d));
+  }
+  // block ids are non-negative and a head's block stride is below 4 GiB
+  auto block_of = [&](int step) {
+    const int b = min(b0 + 2 * step + (wave >> 1), b_last);
+    return (uint64_t)(uint32_t)bt[b] * (uint32_t)head_stride;
+  };
+  const uint32_t kring_lds = lds_offset(kring) + 2 * (16 * (wave >> 1) + 8 * (wave & 1)) * D;
+  const uint32_t vring_lds = lds_offset(vring) + 2 * ((wave >> 1) * D * 16 + (D / 2) * (wave & 1) * 16);
+  auto copy_k = [&](int step, int slot) {
+    copy_to_lds<S::COPIES>(kcache + block_of(step), koff, kring_lds + slot * (2 * S::KSLOT));
+  };
+  auto copy_v = [&](int step, int slot) {
+    copy_to_lds<S::COPIES>(vcache + block_of(step), voff, vring_lds + slot * (2 * S::VSLOT));
+  };
+
+  // ---- per-lane LDS read offsets ----
+  const int key_l = step_key_of_row(c32);
+  const int kswz_l = k_swizzle<D>(key_l);
+  const int vswz_l = v_swizzle(c32);
+  const uint16_t* vrow = vring + c32 * 16 + 8 * (h ^ vswz_l);
+  // per-lane byte offsets of the K operand chunks (the slot adds a uniform
+  // offset)
+  uint32_t kaddr[S::DK];
+#pragma unroll
+  for (int ks = 0; ks < S::DK; ++ks)
+    kaddr[ks] = lds_offset(kring) + 2 * (key_l * D + 8 * ((2 * ks + h) ^ kswz_l));
+  auto scores = [&](int slot) {
+    const uint32_t sb = __builtin_amdgcn_readfirstlane(slot * S::KSLOT * 2);
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < S::DK; ++ks) {
+      typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+      const u32x4 kf = *(const lds_u32x4*)(uintptr_t)(kaddr[ks] + sb);
+      acc = mfma32x32x16(kf, qf[ks], acc);
+    }
+    return acc;
+  };
+
+  f32x16 o[S::DT];
+#pragma unroll
+  for (int dt = 0; dt < S::DT; ++dt) o[dt] = f32x16{};
+  float m = -INFINITY, lsum = 0.f, alpha = 1.f;
+  bool pending = false;            // o waits for a rescale by alpha
+  u32x4 ph[2], pl[2];              // P of the previous step: per key half, hi and lo
+#pragma unroll
+  for (int t = 0; t < 2; ++t) { ph[t] = u32x4{0, 0, 0, 0}; pl[t] = u32x4{0, 0, 0, 0}; }
+
+  auto pv = [&](int slot, const u32x4* hi, const u32x4* lo, const uint32_t (*vmask)[4]) {
+    const uint16_t* vp = vrow + slot * S::VSLOT;
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 vf = *reinterpret_cast<const u32x4*>(vp + t * D * 16 + dt * 32 * 16);
+        if (vmask) { vf[0] &= vmask[t][0]; vf[1] &= vmask[t][1]; vf[2] &= vmask[t][2]; vf[3] &= vmask[t][3]; }
+        o[dt] = mfma32x32x16(vf, hi[t], o[dt]);
+        o[dt] = mfma32x32x16(vf, lo[t], o[dt]);
+      }
+  };
+
+  // ---- prologue: K of steps 0..2 and V of step 0; V slot 2 (read with
+  // P = 0 by the first iteration) is cleared ----
+  copy_k(0, 0);
+  copy_k(1, 1);
+  copy_k(2, 2);
+  copy_v(0, 0);
+  {
+    u32x4* vz = reinterpret_cast<u32x4*>(vring + 2 * S::VSLOT);
+    for (int i = tid; i < S::VSLOT / 8; i += 256) vz[i] = u32x4{0, 0, 0, 0};
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  f32x16 sc = scores(0), sc2;
+  int rot = 0;  // step % 3 of the next iteration
+
+  // lane's keys in a step: key_off(v) + 8h, v = 0..15 (value v of the score
+  // accumulator)
+  auto iteration = [&](auto masked_tag, int st, f32x16& sc, f32x16& sn) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    wait_vmcnt<2 * S::COPIES>();  // copies issued two iterations ago have landed
+    step_barrier();
+    if (pending) {
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt) o[dt] *= alpha;
+    }
+    const int slot_k3 = rot;                        // = st % 3: K of step st+3 replaces K of step st
+    const int slot_k1 = rot == 2 ? 0 : rot + 1;     // K of step st+1; V of step st+1 goes here
+    const int slot_vp = rot == 0 ? 2 : rot - 1;     // V of step st-1
+    rot = slot_k1;
+    copy_k(st + 3, slot_k3);
+    copy_v(st + 1, slot_k1);
+    sn = scores(slot_k1);                   // S of step st+1 (unused past the end)
+    pv(slot_vp, ph, pl, nullptr);           // O^T += V^T P^T of step st-1
+
+    // ---- softmax of step st ----
+    float x[16];
+    float tmax = -INFINITY;
+    const int kbase = jstart + 32 * st + 8 * h;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float sv = sc[v];
+      if constexpr (MASKED) {
+        const int kp = kbase + 16 * (v >> 3) + 4 * ((v >> 2) & 1) + (v & 3);
+        const bool ok = kp <= qpos && kp < ctx && (W <= 0 || kp > qpos - W);
+        sv = ok ? sv : -INFINITY;
+      }
+      x[v] = sv;
+      tmax = fmaxf(tmax, sv);
+    }
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+    }
+    // lazy rescaling: the running max moves only when the step's max exceeds
+    // it by more than 2^8 (p stays below 256 otherwise); the final division
+    // uses the same max
+    const bool up = tmax > m + 8.f;
+    alpha = up ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;  // 0 when m was -inf
+    m = up ? tmax : m;
+    lsum *= alpha;
+    pending = __any(up);
+    const float nb = (m == -INFINITY) ? 0.f : -m;
+    float p[16];
+    float ps = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      p[v] = __builtin_amdgcn_exp2f(fmaf(x[v], c, nb));
+      ps += p[v];
+    }
+    lsum += ps;
+    // P^T operand of key half t: logical k = 8h + e <-> value v = 8t + e;
+    // p = hi + lo, both bf16
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t hi, lo;
+        split_bf16x2(p[8 * t + 2 * e], p[8 * t + 2 * e + 1], hi, lo);
+        ph[t][e] = hi;
+        pl[t][e] = lo;
+      }
+  };
+
+  // steps that need no mask: every column sees all 32 keys causally and
+  // inside its window
+  const int x1 = qpos_first - 31 - jstart;
+  const int y2 = W > 0 ? qpos_last - W + 1 - jstart : 0;
+  const int a_end = min(nsteps, y2 > 0 ? (y2 + 31) / 32 : 0);
+  const int b_end = max(a_end, min(nsteps, x1 >= 0 ? x1 / 32 + 1 : 0));
+  int st = 0;
+  for (; st < a_end; ++st) { iteration(std::true_type{}, st, sc, sc2); sc = sc2; }
+  for (; st + 2 <= b_end; st += 2) {  // two steps per trip: the score tiles swap roles
+    iteration(std::false_type{}, st, sc, sc2);
+    iteration(std::false_type{}, st + 1, sc2, sc);
+  }
+  for (; st < b_end; ++st) { iteration(std::false_type{}, st, sc, sc2); sc = sc2; }
+  for (; st < nsteps; ++st) { iteration(std::true_type{}, st, sc, sc2); sc = sc2; }
+
+  // ---- epilogue: PV of the last step, values past the context zeroed ----
+  wait_vmcnt<0>();
+  step_barrier();
+  if (pending) {
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) o[dt] *= alpha;
+  }
+  {
+    uint32_t vmask[2][4];
+    const int kb = jstart + 32 * (nsteps - 1) + 8 * h;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kp = kb + 16 * t + 2 * e;
+        vmask[t][e] = (kp < ctx ? 0x0000ffffu : 0u) | (kp + 1 < ctx ? 0xffff0000u : 0u);
+      }
+    pv((nsteps + 2) % 3, ph, pl, vmask);  // V of step nsteps-1
+  }
+
+  // ---- normalise and write: lane holds rows d = 32 dt + 8 i + 4 h + r of
+  // its column ----
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+    const float L = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const float inv = 1.f / L;
+    if (tok < ntok) {
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) +
+                     ((size_t)(q0 + tok0 + tok) * a.num_heads + g * G + head) * D + 4 * h;
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint2 w;
+          w.x = pack_bf16x2(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv);
+          w.y = pack_bf16x2(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv);
+          *reinterpret_cast<uint2*>(op + dt * 32 + 8 * i) = w;
+        }
+    }
+  }
+}
+
+template <int D, int G>
+static hipError_t run_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
+  const unsigned blocks = (unsigned)a.num_tiles * (unsigned)a.num_kv_heads;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, G>), dim3(blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t run_prefill_bf16_g(const PrefillArgs& a, int G, hipStream_t st) {
+  switch (G) {
+    case 1: return run_prefill_bf16<D, 1>(a, st);
+    case 2: return run_prefill_bf16<D, 2>(a, st);
+    case 4: return run_prefill_bf16<D, 4>(a, st);
+    case 8: return run_prefill_bf16<D, 8>(a, st);
+    case 16: return run_prefill_bf16<D, 16>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_size, hipStream_t stream) {
+  const int G = a.num_heads / a.num_kv_heads;
+  if (head_size == 64) return run_prefill_bf16_g<64>(a, G, stream);
+  if (head_size == 128) return run_prefill_bf16_g<128>(a, G, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa
