@@ -1,5 +1,6 @@
-// Chunked-prefill paged attention for bf16 KV caches on gfx950 matrix cores,
-// 32x32x16 bf16 MFMA with fp32 accumulation.
+// Chunked-prefill paged attention for bf16 KV caches on gfx950 matrix cores:
+// scores on 32x32x16 bf16 MFMA, the weighted sum of values on 32x32x16 fp16
+// MFMA, both with fp32 accumulation.
 //
 // What it computes: every query row of a chunk longer than one token attends
 // causally to its sequence's cached keys, read through the block table; query
@@ -14,7 +15,15 @@
 //  * keys advance in steps of 32 (two 16-token blocks). A wave computes the
 //    32 x 32 score tile S^T = K Q^T of its 32 columns with head_size/16 MFMAs
 //    (queries are the B operand, kept in registers), then O^T += V^T P^T with
-//    head_size/32 output tiles x 2 key halves x 2 (P as bf16 hi + lo);
+//    head_size/32 output tiles x 2 key halves;
+//  * the softmax weights enter the PV product as fp16 (11 significant bits;
+//    bf16's 8 move outputs dominated by a few keys by up to 2^-9 |v|), scaled
+//    by 2^7 so that they stay in fp16's range (p <= 2^15) and keep 2^-31 of
+//    resolution below the running maximum. The values are therefore
+//    converted to fp16 once per workgroup, in LDS: exact for |v| in
+//    [2^-14, 65504]; smaller magnitudes keep 2^-24 of absolute resolution and
+//    larger ones overflow, so bf16 values beyond fp16's range are outside
+//    this kernel's domain;
 //  * score rows are fed in a permuted key order, so that the accumulator of
 //    lane l holds, for its column, exactly the 8-key runs the PV B operand
 //    wants from it: probabilities never leave the lane. A column's 32 keys
@@ -24,10 +33,12 @@
 //    ALUs run the softmax of step i. The O^T rescale that a new running max
 //    asks for (lazy: only when the max grows by more than 2^8) is applied at
 //    the top of the next iteration, after step i-1's PV and before step i's;
-//  * K and V reach LDS by direct global->LDS copies into rings of three
-//    32-key slots; K is fetched three steps ahead and V one step ahead of
-//    their use, one barrier per step. The copies place 16-byte chunks so
-//    that the MFMA operand reads hit distinct LDS banks;
+//  * K and V reach LDS by direct global->LDS copies, issued three steps
+//    ahead, into rings of three (K) and five (V) 32-key slots, one barrier
+//    per step. A V slot is converted to fp16 in place two steps after its
+//    copy was issued and read by the PV product two steps later. The copies
+//    place 16-byte chunks so that the MFMA operand reads hit distinct LDS
+//    banks;
 //  * masks (causal edge, sliding window, context end) are evaluated only in
 //    the steps that cross an edge; values of keys past the context are
 //    zeroed in the last step, because the block of a partial last block may
@@ -43,11 +54,26 @@
 namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32x32x16_f16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
+}
+// Two floats as packed fp16, rounded to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
+}
+// A pair of bf16 values as a pair of fp16 values (exact inside fp16's range).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 
 template <int D>
@@ -57,7 +83,8 @@ struct PfShape {
   static constexpr int DT = D / 32;          // 32-row tiles of head_size in O^T
   static constexpr int KSLOT = STEP * D;     // bf16 elements of one K slot: [32][D]
   static constexpr int VSLOT = 2 * D * 16;   // one V slot: two [D][16] block tiles
-  static constexpr int SLOTS = 3;
+  static constexpr int KSLOTS = 3;
+  static constexpr int VSLOTS = 5;
   static constexpr int COPIES = D / 64;      // 1 KiB copies per wave and operand per step
   static constexpr int BLK_BYTES = 16 * D * 2;
 };
@@ -72,16 +99,6 @@ __device__ __forceinline__ int k_swizzle(int key) {
   else return (key >> 1) & 7;
 }
 __device__ __forceinline__ int v_swizzle(int d) { return (d >> 3) & 1; }
-
-// p = hi + lo with hi = bf16(p) and lo = bf16(p - hi), for a pair of
-// probabilities packed as the PV MFMA operand wants them. hi's low half is
-// moved up with a byte permute (the compiler would otherwise round a0 again).
-__device__ __forceinline__ void split_bf16x2(float a0, float a1, uint32_t& hi, uint32_t& lo) {
-  hi = pack_bf16x2(a0, a1);
-  const float h0 = __uint_as_float(__builtin_amdgcn_perm(0u, hi, 0x01000c0cu));
-  const float h1 = __uint_as_float(hi & 0xffff0000u);
-  lo = pack_bf16x2(a0 - h0, a1 - h1);
-}
 
 // Score row m of a step holds this key of the step.
 __device__ __forceinline__ int step_key_of_row(int m) {
@@ -150,8 +167,8 @@ template <int D, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(PrefillArgs a) {
   using S = PfShape<D>;
   constexpr int TQ = 128 / G;
-  __shared__ __attribute__((aligned(16))) uint16_t kring[S::SLOTS * S::KSLOT];
-  __shared__ __attribute__((aligned(16))) uint16_t vring[S::SLOTS * S::VSLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t kring[S::KSLOTS * S::KSLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t vring[S::VSLOTS * S::VSLOT];
   __shared__ int sh_scan[256];
   __shared__ int sh_found[3];
 
@@ -263,11 +280,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int dt = 0; dt < S::DT; ++dt) o[dt] = f32x16{};
   float m = -INFINITY, lsum = 0.f, alpha = 1.f;
   bool pending = false;            // o waits for a rescale by alpha
-  u32x4 ph[2], pl[2];              // P of the previous step: per key half, hi and lo
+  u32x4 pf[2];                     // P of the previous step (fp16, x 2^7), per key half
 #pragma unroll
-  for (int t = 0; t < 2; ++t) { ph[t] = u32x4{0, 0, 0, 0}; pl[t] = u32x4{0, 0, 0, 0}; }
+  for (int t = 0; t < 2; ++t) pf[t] = u32x4{0, 0, 0, 0};
 
-  auto pv = [&](int slot, const u32x4* hi, const u32x4* lo, const uint32_t (*vmask)[4]) {
+  auto pv = [&](int slot, const u32x4* pk, const uint32_t (*vmask)[4]) {
     const uint16_t* vp = vrow + slot * S::VSLOT;
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
@@ -275,25 +292,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int t = 0; t < 2; ++t) {
         u32x4 vf = *reinterpret_cast<const u32x4*>(vp + t * D * 16 + dt * 32 * 16);
         if (vmask) { vf[0] &= vmask[t][0]; vf[1] &= vmask[t][1]; vf[2] &= vmask[t][2]; vf[3] &= vmask[t][3]; }
-        o[dt] = mfma32x32x16(vf, hi[t], o[dt]);
-        o[dt] = mfma32x32x16(vf, lo[t], o[dt]);
+        o[dt] = mfma32x32x16_f16(vf, pk[t], o[dt]);
       }
   };
+  // bf16 -> fp16 in place: thread tid owns D/4 bytes of the slot
+  auto convert_v = [&](int slot) {
+    u32x4* vp = reinterpret_cast<u32x4*>(vring + slot * S::VSLOT) + tid * (D / 64);
+#pragma unroll
+    for (int n = 0; n < D / 64; ++n) {
+      u32x4 w = vp[n];
+      w[0] = bf16x2_to_f16x2(w[0]); w[1] = bf16x2_to_f16x2(w[1]);
+      w[2] = bf16x2_to_f16x2(w[2]); w[3] = bf16x2_to_f16x2(w[3]);
+      vp[n] = w;
+    }
+  };
 
-  // ---- prologue: K of steps 0..2 and V of step 0; V slot 2 (read with
-  // P = 0 by the first iteration) is cleared ----
-  copy_k(0, 0);
-  copy_k(1, 1);
-  copy_k(2, 2);
-  copy_v(0, 0);
+  // ---- prologue: K and V of steps 0..2; V of step 0 converted; the V slot
+  // of step -1 (read with P = 0 by the first iteration) cleared ----
+#pragma unroll
+  for (int i = 0; i < 3; ++i) { copy_v(i, i); copy_k(i, i); }
   {
-    u32x4* vz = reinterpret_cast<u32x4*>(vring + 2 * S::VSLOT);
+    u32x4* vz = reinterpret_cast<u32x4*>(vring + (S::VSLOTS - 1) * S::VSLOT);
     for (int i = tid; i < S::VSLOT / 8; i += 256) vz[i] = u32x4{0, 0, 0, 0};
   }
   wait_vmcnt<0>();
   __syncthreads();
+  convert_v(0);
   f32x16 sc = scores(0), sc2;
-  int rot = 0;  // step % 3 of the next iteration
+  int krot = 0;  // step % 3 of the next iteration
+  int vrot = 0;  // step % 5 of the next iteration
 
   // lane's keys in a step: key_off(v) + 8h, v = 0..15 (value v of the score
   // accumulator)
@@ -305,14 +332,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt) o[dt] *= alpha;
     }
-    const int slot_k3 = rot;                        // = st % 3: K of step st+3 replaces K of step st
-    const int slot_k1 = rot == 2 ? 0 : rot + 1;     // K of step st+1; V of step st+1 goes here
-    const int slot_vp = rot == 0 ? 2 : rot - 1;     // V of step st-1
-    rot = slot_k1;
+    const int slot_k3 = krot;                          // = st % 3: K of step st+3 replaces K of step st
+    const int slot_k1 = krot == 2 ? 0 : krot + 1;      // K of step st+1
+    krot = slot_k1;
+    const int slot_vp = vrot == 0 ? 4 : vrot - 1;      // V of step st-1
+    const int slot_v1 = vrot == 4 ? 0 : vrot + 1;      // V of step st+1
+    const int slot_v3 = vrot >= 2 ? vrot - 2 : vrot + 3;  // V of step st+3 replaces V of step st-2
+    vrot = slot_v1;
+    copy_v(st + 3, slot_v3);
     copy_k(st + 3, slot_k3);
-    copy_v(st + 1, slot_k1);
+    convert_v(slot_v1);                     // read by the PV product two iterations on
     sn = scores(slot_k1);                   // S of step st+1 (unused past the end)
-    pv(slot_vp, ph, pl, nullptr);           // O^T += V^T P^T of step st-1
+    pv(slot_vp, pf, nullptr);               // O^T += V^T P^T of step st-1
 
     // ---- softmax of step st ----
     float x[16];
@@ -341,7 +372,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     m = up ? tmax : m;
     lsum *= alpha;
     pending = __any(up);
-    const float nb = (m == -INFINITY) ? 0.f : -m;
+    const float nb = (m == -INFINITY) ? 0.f : 7.f - m;  // weights carry a factor 2^7
     float p[16];
     float ps = 0.f;
 #pragma unroll
@@ -350,17 +381,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       ps += p[v];
     }
     lsum += ps;
-    // P^T operand of key half t: logical k = 8h + e <-> value v = 8t + e;
-    // p = hi + lo, both bf16
+    // P^T operand of key half t: logical k = 8h + e <-> value v = 8t + e
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint32_t hi, lo;
-        split_bf16x2(p[8 * t + 2 * e], p[8 * t + 2 * e + 1], hi, lo);
-        ph[t][e] = hi;
-        pl[t][e] = lo;
-      }
+      for (int e = 0; e < 4; ++e) pf[t][e] = pack_f16x2(p[8 * t + 2 * e], p[8 * t + 2 * e + 1]);
   };
 
   // steps that need no mask: every column sees all 32 keys causally and
@@ -395,7 +420,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int kp = kb + 16 * t + 2 * e;
         vmask[t][e] = (kp < ctx ? 0x0000ffffu : 0u) | (kp + 1 < ctx ? 0xffff0000u : 0u);
       }
-    pv((nsteps + 2) % 3, ph, pl, vmask);  // V of step nsteps-1
+    pv((nsteps + 4) % 5, pf, vmask);  // V of step nsteps-1
   }
 
   // ---- normalise and write: lane holds rows d = 32 dt + 8 i + 4 h + r of
