@@ -263,17 +263,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int ks = 0; ks < S::DK; ++ks)
     kaddr[ks] = lds_offset(kring) + 2 * (key_l * D + 8 * ((2 * ks + h) ^ kswz_l));
-  auto scores = [&](int slot) {
+  u32x4 kf[S::DK];
+  auto scores_load = [&](int slot) {
     const uint32_t sb = __builtin_amdgcn_readfirstlane(slot * S::KSLOT * 2);
-    f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < S::DK; ++ks) {
       typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-      const u32x4 kf = *(const lds_u32x4*)(uintptr_t)(kaddr[ks] + sb);
-      acc = mfma32x32x16(kf, qf[ks], acc);
+      kf[ks] = *(const lds_u32x4*)(uintptr_t)(kaddr[ks] + sb);
     }
+  };
+  auto scores_mfma = [&]() {
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < S::DK; ++ks) acc = mfma32x32x16(kf[ks], qf[ks], acc);
     return acc;
   };
+  auto scores = [&](int slot) { scores_load(slot); return scores_mfma(); };
 
   f32x16 o[S::DT];
 #pragma unroll
@@ -295,15 +300,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         o[dt] = mfma32x32x16_f16(vf, pk[t], o[dt]);
       }
   };
-  // bf16 -> fp16 in place: thread tid owns D/4 bytes of the slot
-  auto convert_v = [&](int slot) {
-    u32x4* vp = reinterpret_cast<u32x4*>(vring + slot * S::VSLOT) + tid * (D / 64);
+  // bf16 -> fp16 in place: thread tid owns the 16-byte chunks tid + 256 n of
+  // the slot (consecutive lanes, consecutive chunks: no bank conflicts).
+  // The chunks are read early in an iteration and written back at its end.
+  u32x4 cvt[D / 64];
+  auto convert_load = [&](int slot) {
+    const u32x4* vp = reinterpret_cast<const u32x4*>(vring + slot * S::VSLOT) + tid;
+#pragma unroll
+    for (int n = 0; n < D / 64; ++n) cvt[n] = vp[256 * n];
+  };
+  auto convert_store = [&](int slot) {
+    u32x4* vp = reinterpret_cast<u32x4*>(vring + slot * S::VSLOT) + tid;
 #pragma unroll
     for (int n = 0; n < D / 64; ++n) {
-      u32x4 w = vp[n];
+      u32x4 w = cvt[n];
       w[0] = bf16x2_to_f16x2(w[0]); w[1] = bf16x2_to_f16x2(w[1]);
       w[2] = bf16x2_to_f16x2(w[2]); w[3] = bf16x2_to_f16x2(w[3]);
-      vp[n] = w;
+      vp[256 * n] = w;
     }
   };
 
@@ -317,7 +330,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   wait_vmcnt<0>();
   __syncthreads();
-  convert_v(0);
+  convert_load(0);
+  convert_store(0);
   f32x16 sc = scores(0), sc2;
   int krot = 0;  // step % 3 of the next iteration
   int vrot = 0;  // step % 5 of the next iteration
@@ -341,8 +355,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     vrot = slot_v1;
     copy_v(st + 3, slot_v3);
     copy_k(st + 3, slot_k3);
-    convert_v(slot_v1);                     // read by the PV product two iterations on
-    sn = scores(slot_k1);                   // S of step st+1 (unused past the end)
+    convert_load(slot_v1);                  // converted below; read by the PV product two iterations on
+    scores_load(slot_k1);
+    __builtin_amdgcn_sched_barrier(0);
+    sn = scores_mfma();                     // S of step st+1 (unused past the end)
     pv(slot_vp, pf, nullptr);               // O^T += V^T P^T of step st-1
 
     // ---- softmax of step st ----
@@ -386,6 +402,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) pf[t][e] = pack_f16x2(p[8 * t + 2 * e], p[8 * t + 2 * e + 1]);
+    convert_store(slot_v1);
   };
 
   // steps that need no mask: every column sees all 32 keys causally and
