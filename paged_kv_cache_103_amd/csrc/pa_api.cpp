@@ -316,7 +316,7 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
     p.window = sliding_window;
     p.scale_log2 = scale_log2;
     // bound on sum over sequences with q_len > 1 of ceil(q_len / TQ)
-    const long long tq = pa::prefill_tokens_per_tile(group);
+    const long long tq = pa::prefill_tokens_per_tile((int)cache_dtype, group);
     const long long long_seqs = std::min<long long>(num_seqs, num_q_tokens / 2);
     const long long bound_a = long_seqs + (num_q_tokens + tq - 1) / tq;
     const long long bound_b = long_seqs * ((max_q_len + tq - 1) / tq);

@@ -88,9 +88,12 @@ struct PrefillArgs {
   int num_tiles;  // grid bound on (sequence, query tile) pairs
   float scale_log2;
 };
-int prefill_tokens_per_tile(int group);
+// Query tokens per workgroup tile of the chunked-prefill kernel for a cache type.
+int prefill_tokens_per_tile(int cache_kind, int group);
+int prefill_bf16_tokens_per_tile(int group);
 hipError_t launch_prefill(const PrefillArgs& args, int cache_kind, int head_size, hipStream_t stream);
-// bf16 caches: the 32x32x16 MFMA kernel with direct global->LDS copies.
+// bf16 caches: the 32x32 MFMA kernel (bf16 scores, fp16 PV) with direct
+// global->LDS copies, 8 waves per workgroup.
 hipError_t launch_prefill_bf16(const PrefillArgs& args, int head_size, hipStream_t stream);
 bool prefill_supported(int q_kind, int cache_kind, int head_size, int group);
 

@@ -1,4 +1,5 @@
-// Chunked-prefill paged attention on gfx950 matrix cores (MFMA).
+// Chunked-prefill paged attention on gfx950 matrix cores (MFMA) for fp8
+// caches (bf16 caches take the kernel of prefill_bf16.hip).
 //
 // What it computes: every query row of a chunk longer than one token attends
 // causally to its sequence's cached keys, read through the block table: the
@@ -31,8 +32,6 @@
 // the most keys), and the KV head is the fastest-varying part of the
 // workgroup index so that the tiles of one head land on the same XCD.
 #include <math.h>
-#include <stdlib.h>
-#include <string.h>
 
 #include <type_traits>
 
@@ -443,7 +442,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------------------
-int prefill_tokens_per_tile(int group) { return 128 / group; }
+int prefill_tokens_per_tile(int cache_kind, int group) {
+  return cache_kind == KBF16 ? prefill_bf16_tokens_per_tile(group) : 128 / group;
+}
 
 bool prefill_supported(int q_kind, int cache_kind, int head_size, int group) {
   if (head_size != 64 && head_size != 128) return false;
@@ -474,10 +475,6 @@ static hipError_t run_prefill_g(const PrefillArgs& a, int G, hipStream_t st) {
 hipError_t launch_prefill(const PrefillArgs& a, int cache_kind, int head_size, hipStream_t stream) {
   const int G = a.num_heads / a.num_kv_heads;
   if (cache_kind == KBF16) {
-    if (getenv("PA_PREFILL_KERNEL") && strcmp(getenv("PA_PREFILL_KERNEL"), "mfma16") == 0) {
-      if (head_size == 64) return run_prefill_g<KBF16, 64>(a, G, stream);
-      if (head_size == 128) return run_prefill_g<KBF16, 128>(a, G, stream);
-    }
     return launch_prefill_bf16(a, head_size, stream);
   } else if (cache_kind == KFP8) {
     if (head_size == 64) return run_prefill_g<KFP8, 64>(a, G, stream);

@@ -10,8 +10,9 @@
 // Each cached K/V row serves many queries, so the work is a dense contraction
 // ("大模型推理优化学习笔记", "计算密集与访存密集") and runs on MFMA.
 //
-// Shape of the work (one workgroup = 4 waves = 128 query columns of one KV
-// head: 128/G tokens x the G query heads of the group):
+// Shape of the work (one workgroup = 8 waves = 256 query columns of one KV
+// head: 256/G tokens x the G query heads of the group; one workgroup per
+// CU, so that the staging of each K/V step is shared by 8 waves):
 //  * keys advance in steps of 32 (two 16-token blocks). A wave computes the
 //    32 x 32 score tile S^T = K Q^T of its 32 columns with head_size/16 MFMAs
 //    (queries are the B operand, kept in registers), then O^T += V^T P^T with
@@ -36,9 +37,9 @@
 //  * K and V reach LDS by direct global->LDS copies, issued three steps
 //    ahead, into rings of three (K) and five (V) 32-key slots, one barrier
 //    per step. A V slot is converted to fp16 in place two steps after its
-//    copy was issued and read by the PV product two steps later. The copies
-//    place 16-byte chunks so that the MFMA operand reads hit distinct LDS
-//    banks;
+//    copy was issued and read by the PV product two steps later (each
+//    thread converts one 16-byte chunk). The copies place 16-byte chunks so
+//    that the MFMA operand reads hit distinct LDS banks;
 //  * masks (causal edge, sliding window, context end) are evaluated only in
 //    the steps that cross an edge; values of keys past the context are
 //    zeroed in the last step, because the block of a partial last block may
@@ -83,9 +84,9 @@ struct PfShape {
   static constexpr int DT = D / 32;          // 32-row tiles of head_size in O^T
   static constexpr int KSLOT = STEP * D;     // bf16 elements of one K slot: [32][D]
   static constexpr int VSLOT = 2 * D * 16;   // one V slot: two [D][16] block tiles
-  static constexpr int KSLOTS = 3;
-  static constexpr int VSLOTS = 5;
-  static constexpr int COPIES = D / 64;      // 1 KiB copies per wave and operand per step
+  static constexpr int AHEAD = 3;            // steps a copy is issued ahead of its step
+  static constexpr int KSLOTS = AHEAD;
+  static constexpr int VSLOTS = AHEAD + 2;
   static constexpr int BLK_BYTES = 16 * D * 2;
 };
 
@@ -163,19 +164,23 @@ __device__ __forceinline__ void step_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
+constexpr int PF_NW = 8;             // waves per workgroup
+constexpr int PF_NT = 64 * PF_NW;    // threads per workgroup
+
 template <int D, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(PrefillArgs a) {
   using S = PfShape<D>;
-  constexpr int TQ = 128 / G;
+  constexpr int NW = PF_NW, NT = PF_NT;
+  constexpr int TQ = 32 * NW / G;
   __shared__ __attribute__((aligned(16))) uint16_t kring[S::KSLOTS * S::KSLOT];
   __shared__ __attribute__((aligned(16))) uint16_t vring[S::VSLOTS * S::VSLOT];
-  __shared__ int sh_scan[256];
+  __shared__ int sh_scan[NT];
   __shared__ int sh_found[3];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = blockIdx.x % a.num_kv_heads;
-  const PrefillTile tile = find_prefill_tile(a.cu_seqlens, a.num_seqs, TQ, blockIdx.x / a.num_kv_heads, sh_scan,
+  const PrefillTile tile = find_prefill_tile<NT>(a.cu_seqlens, a.num_seqs, TQ, blockIdx.x / a.num_kv_heads, sh_scan,
                                              sh_found);
   if (tile.seq < 0) return;
   const int s = tile.seq;
@@ -221,35 +226,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
-  // ---- global -> LDS copies (one 16-byte chunk per lane, lane i to byte
-  // 16 i of a 1 KiB region); wave w copies half of block w/2 of the step.
-  // Blocks past the context re-read the last block (masked, zeroed).
+  // ---- global -> LDS copies: a step's K slot and V slot are each written
+  // by D/16 copies of 1 KiB (one 16-byte chunk per lane, lane i to byte
+  // 16 i of the copy's region); wave w issues copies w + NW n, the first
+  // D/16 of them K, the rest V. Each lane fetches the global chunk that
+  // lands, swizzled, where the MFMA operand reads expect it. Blocks past the
+  // context re-read the last block (masked, zeroed).
+  constexpr int KCOPIES = D / 16;
+  constexpr int CPW = 2 * KCOPIES / NW;  // copies per wave per step
+  static_assert(CPW >= 1 && 2 * KCOPIES % NW == 0, "copy split");
   const uint32_t head_stride = (uint32_t)a.num_kv_heads * S::BLK_BYTES;
   const uint8_t* kcache = reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)g * S::BLK_BYTES;
   const uint8_t* vcache = reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * S::BLK_BYTES;
   const int b0 = jstart >> 4;
-  constexpr int CPR = D / 8;     // chunks per K row
-  constexpr int RPC = 64 / CPR;  // K rows per 1 KiB copy
-  uint32_t koff[S::COPIES], voff[S::COPIES];
+  constexpr int CPR = D / 8;  // chunks per K row
+  uint32_t cp_off[CPW];
 #pragma unroll
-  for (int n = 0; n < S::COPIES; ++n) {
-    const int row = 8 * (wave & 1) + n * RPC + lane / CPR;  // K row within the block
-    koff[n] = row * (2 * D) + 16 * ((lane % CPR) ^ k_swizzle<D>(16 * (wave >> 1) + row));
-    const int d = (D / 2) * (wave & 1) + 32 * n + lane / 2;  // V^T row within the block
-    voff[n] = d * 32 + 16 * ((lane & 1) ^ v_swizzle(d));
+  for (int n = 0; n < CPW; ++n) {
+    const int j = wave + NW * n;
+    const int p = 64 * (j < KCOPIES ? j : j - KCOPIES) + lane;  // 16-byte position in the slot
+    if (j < KCOPIES) {
+      const int key = p / CPR;
+      cp_off[n] = (key % 16) * (2 * D) + 16 * ((p % CPR) ^ k_swizzle<D>(key));
+    } else {
+      const int d = (p / 2) % D;
+      cp_off[n] = d * 32 + 16 * ((p % 2) ^ v_swizzle(d));
+    }
   }
+  const uint32_t kring_lds = lds_offset(kring), vring_lds = lds_offset(vring);
   // block ids are non-negative and a head's block stride is below 4 GiB
-  auto block_of = [&](int step) {
-    const int b = min(b0 + 2 * step + (wave >> 1), b_last);
-    return (uint64_t)(uint32_t)bt[b] * (uint32_t)head_stride;
-  };
-  const uint32_t kring_lds = lds_offset(kring) + 2 * (16 * (wave >> 1) + 8 * (wave & 1)) * D;
-  const uint32_t vring_lds = lds_offset(vring) + 2 * ((wave >> 1) * D * 16 + (D / 2) * (wave & 1) * 16);
-  auto copy_k = [&](int step, int slot) {
-    copy_to_lds<S::COPIES>(kcache + block_of(step), koff, kring_lds + slot * (2 * S::KSLOT));
-  };
-  auto copy_v = [&](int step, int slot) {
-    copy_to_lds<S::COPIES>(vcache + block_of(step), voff, vring_lds + slot * (2 * S::VSLOT));
+  auto copy_step = [&](int step, int kslot, int vslot) {
+#pragma unroll
+    for (int n = 0; n < CPW; ++n) {
+      const int j = wave + NW * n;
+      const bool isv = j >= KCOPIES;
+      const int jj = isv ? j - KCOPIES : j;
+      const int b = min(b0 + 2 * step + (64 * jj) / (2 * D), b_last);
+      const uint64_t off = (uint64_t)(uint32_t)bt[b] * head_stride;
+      const uint32_t lds = isv ? vring_lds + vslot * (2 * S::VSLOT) + 1024 * jj
+                               : kring_lds + kslot * (2 * S::KSLOT) + 1024 * jj;
+      copy_to_lds<1>((isv ? vcache : kcache) + off, &cp_off[n], lds);
+    }
   };
 
   // ---- per-lane LDS read offsets ----
@@ -300,61 +317,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         o[dt] = mfma32x32x16_f16(vf, pk[t], o[dt]);
       }
   };
-  // bf16 -> fp16 in place: thread tid owns the 16-byte chunks tid + 256 n of
-  // the slot (consecutive lanes, consecutive chunks: no bank conflicts).
-  // The chunks are read early in an iteration and written back at its end.
-  u32x4 cvt[D / 64];
+  // bf16 -> fp16 in place: thread tid owns the 16-byte chunk tid of the
+  // slot (4 D chunks; threads past them idle). The chunk is read early in an
+  // iteration and written back at its end.
+  constexpr int VCH = 4 * D;
+  static_assert(VCH <= NT, "one chunk per thread");
+  const bool converts = VCH == NT || tid < VCH;
+  u32x4 cvt = {0, 0, 0, 0};
   auto convert_load = [&](int slot) {
-    const u32x4* vp = reinterpret_cast<const u32x4*>(vring + slot * S::VSLOT) + tid;
-#pragma unroll
-    for (int n = 0; n < D / 64; ++n) cvt[n] = vp[256 * n];
+    if (converts) cvt = reinterpret_cast<const u32x4*>(vring + slot * S::VSLOT)[tid];
   };
   auto convert_store = [&](int slot) {
-    u32x4* vp = reinterpret_cast<u32x4*>(vring + slot * S::VSLOT) + tid;
-#pragma unroll
-    for (int n = 0; n < D / 64; ++n) {
-      u32x4 w = cvt[n];
+    if (converts) {
+      u32x4 w = cvt;
       w[0] = bf16x2_to_f16x2(w[0]); w[1] = bf16x2_to_f16x2(w[1]);
       w[2] = bf16x2_to_f16x2(w[2]); w[3] = bf16x2_to_f16x2(w[3]);
-      vp[256 * n] = w;
+      reinterpret_cast<u32x4*>(vring + slot * S::VSLOT)[tid] = w;
     }
   };
 
   // ---- prologue: K and V of steps 0..2; V of step 0 converted; the V slot
   // of step -1 (read with P = 0 by the first iteration) cleared ----
 #pragma unroll
-  for (int i = 0; i < 3; ++i) { copy_v(i, i); copy_k(i, i); }
+  for (int i = 0; i < S::AHEAD; ++i) copy_step(i, i, i);
   {
     u32x4* vz = reinterpret_cast<u32x4*>(vring + (S::VSLOTS - 1) * S::VSLOT);
-    for (int i = tid; i < S::VSLOT / 8; i += 256) vz[i] = u32x4{0, 0, 0, 0};
+    for (int i = tid; i < S::VSLOT / 8; i += NT) vz[i] = u32x4{0, 0, 0, 0};
   }
   wait_vmcnt<0>();
   __syncthreads();
   convert_load(0);
   convert_store(0);
   f32x16 sc = scores(0), sc2;
-  int krot = 0;  // step % 3 of the next iteration
-  int vrot = 0;  // step % 5 of the next iteration
+  int krot = 0;  // step % KSLOTS of the next iteration
+  int vrot = 0;  // step % VSLOTS of the next iteration
 
   // lane's keys in a step: key_off(v) + 8h, v = 0..15 (value v of the score
   // accumulator)
   auto iteration = [&](auto masked_tag, int st, f32x16& sc, f32x16& sn) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    wait_vmcnt<2 * S::COPIES>();  // copies issued two iterations ago have landed
+    wait_vmcnt<(S::AHEAD - 2) * CPW>();  // the copies of step st+1 have landed
     step_barrier();
     if (pending) {
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt) o[dt] *= alpha;
     }
-    const int slot_k3 = krot;                          // = st % 3: K of step st+3 replaces K of step st
-    const int slot_k1 = krot == 2 ? 0 : krot + 1;      // K of step st+1
+    constexpr int KS = S::KSLOTS, VS = S::VSLOTS;
+    const int slot_ka = krot;                               // K of step st+AHEAD replaces K of step st
+    const int slot_k1 = krot == KS - 1 ? 0 : krot + 1;      // K of step st+1
     krot = slot_k1;
-    const int slot_vp = vrot == 0 ? 4 : vrot - 1;      // V of step st-1
-    const int slot_v1 = vrot == 4 ? 0 : vrot + 1;      // V of step st+1
-    const int slot_v3 = vrot >= 2 ? vrot - 2 : vrot + 3;  // V of step st+3 replaces V of step st-2
+    const int slot_vp = vrot == 0 ? VS - 1 : vrot - 1;      // V of step st-1
+    const int slot_v1 = vrot == VS - 1 ? 0 : vrot + 1;      // V of step st+1
+    const int slot_va = vrot >= 2 ? vrot - 2 : vrot + VS - 2;  // V of step st+AHEAD replaces V of step st-2
     vrot = slot_v1;
-    copy_v(st + 3, slot_v3);
-    copy_k(st + 3, slot_k3);
+    copy_step(st + S::AHEAD, slot_ka, slot_va);
     convert_load(slot_v1);                  // converted below; read by the PV product two iterations on
     scores_load(slot_k1);
     __builtin_amdgcn_sched_barrier(0);
@@ -437,7 +453,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int kp = kb + 16 * t + 2 * e;
         vmask[t][e] = (kp < ctx ? 0x0000ffffu : 0u) | (kp + 1 < ctx ? 0xffff0000u : 0u);
       }
-    pv((nsteps + 4) % 5, pf, vmask);  // V of step nsteps-1
+    pv((nsteps - 1) % S::VSLOTS, pf, vmask);  // V of step nsteps-1
   }
 
   // ---- normalise and write: lane holds rows d = 32 dt + 8 i + 4 h + r of
@@ -466,7 +482,7 @@ template <int D, int G>
 static hipError_t run_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
   const unsigned blocks = (unsigned)a.num_tiles * (unsigned)a.num_kv_heads;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, G>), dim3(blocks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, G>), dim3(blocks), dim3(PF_NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -481,6 +497,8 @@ static hipError_t run_prefill_bf16_g(const PrefillArgs& a, int G, hipStream_t st
   }
   return hipErrorInvalidValue;
 }
+
+int prefill_bf16_tokens_per_tile(int group) { return 32 * PF_NW / group; }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_size, hipStream_t stream) {
   const int G = a.num_heads / a.num_kv_heads;

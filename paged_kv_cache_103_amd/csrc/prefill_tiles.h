@@ -14,14 +14,15 @@ struct PrefillTile {
   int tile;  // query tile within the sequence, heaviest (last) first
 };
 
-// Requires blockDim.x == 256; sh_scan holds 256 ints, sh_found 3.
+// Requires blockDim.x == NT; sh_scan holds NT ints, sh_found 3.
+template <int NT = 256>
 __device__ inline PrefillTile find_prefill_tile(const int* cu_seqlens, int num_seqs, int tokens_per_tile, int t,
                                                 int* sh_scan, int* sh_found) {
   const int tid = threadIdx.x;
   if (tid == 0) { sh_found[0] = -1; sh_found[1] = 0; sh_found[2] = 0; }
   __syncthreads();
   int running = 0;
-  for (int base = 0; base < num_seqs; base += 256) {
+  for (int base = 0; base < num_seqs; base += NT) {
     const int s = base + tid;
     int n = 0;
     if (s < num_seqs) {
@@ -30,7 +31,7 @@ __device__ inline PrefillTile find_prefill_tile(const int* cu_seqlens, int num_s
     }
     sh_scan[tid] = n;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
+    for (int off = 1; off < NT; off <<= 1) {
       const int v = tid >= off ? sh_scan[tid - off] : 0;
       __syncthreads();
       sh_scan[tid] += v;
@@ -42,7 +43,7 @@ __device__ inline PrefillTile find_prefill_tile(const int* cu_seqlens, int num_s
       sh_found[1] = t - (running + incl - n);
       sh_found[2] = n;
     }
-    running += sh_scan[255];
+    running += sh_scan[NT - 1];
     __syncthreads();
     if (sh_found[0] >= 0) break;
   }
