@@ -113,42 +113,43 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// N 16-byte global -> LDS copies per lane, from base + lane_offset[n] (base
-// uniform): lane i's chunk of copy n lands at byte lds_base + 1024 n + 16 i.
-// Written as inline assembly so that the compiler does not see an LDS store:
-// it would otherwise drain every outstanding copy before each LDS read of
-// the loop. Completion is tracked by the vector-memory counter (wait_vmcnt)
-// and made visible to the workgroup by a barrier. M0 holds the LDS base of
-// a copy (read when the copy issues) and is restored afterwards; a copy must
-// not directly follow a write of M0.
-template <int N>
-__device__ __forceinline__ void copy_to_lds(const void* base, const uint32_t* lane_offset, uint32_t lds_base) {
+// A 16-byte global -> LDS copy per lane, from base + lane_offset (base
+// uniform): lane i's chunk lands at byte lds_base + 16 i. Written as inline
+// assembly so that the compiler does not see an LDS store: it would
+// otherwise drain every outstanding copy before each LDS read of the loop.
+// Completion is tracked by the vector-memory counter (wait_vmcnt) and made
+// visible to the workgroup by a barrier. M0 holds the LDS base of a copy
+// (read when the copy issues) and is restored afterwards; a copy must not
+// directly follow a write of M0.
+__device__ __forceinline__ void copy_to_lds(const void* base, uint32_t lane_offset, uint32_t lds_base) {
   uint32_t saved;
-  if constexpr (N == 1) {
-    __asm__ volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(lane_offset[0]), "s"(base), "s"(lds_base)
-        : "memory");
-  } else {
-    static_assert(N == 2, "one or two copies");
-    __asm__ volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %4\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %3\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %2, %3\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(lane_offset[0]), "v"(lane_offset[1]), "s"(base), "s"(lds_base)
-        : "memory");
-  }
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(lane_offset), "s"(base), "s"(lds_base)
+      : "memory");
+}
+
+// One K and one V copy (as copy_to_lds, each from its own base).
+__device__ __forceinline__ void copy_kv_to_lds(const void* kbase, uint32_t koff, uint32_t klds, const void* vbase,
+                                               uint32_t voff, uint32_t vlds) {
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %4\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(koff), "s"(kbase), "v"(voff), "s"(vbase), "s"(klds), "s"(vlds)
+      : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_offset(const uint16_t* p) {
@@ -256,16 +257,22 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const uint32_t kring_lds = lds_offset(kring), vring_lds = lds_offset(vring);
   // block ids are non-negative and a head's block stride is below 4 GiB
   auto copy_step = [&](int step, int kslot, int vslot) {
-#pragma unroll
-    for (int n = 0; n < CPW; ++n) {
-      const int j = wave + NW * n;
-      const bool isv = j >= KCOPIES;
-      const int jj = isv ? j - KCOPIES : j;
+    if constexpr (CPW == 2) {
+      // one K and one V copy per wave, both of block wave / (2 D / 64) of
+      // the step
+      const int b = min(b0 + 2 * step + (64 * wave) / (2 * D), b_last);
+      const uint64_t off = (uint64_t)(uint32_t)bt[b] * head_stride;
+      copy_kv_to_lds(kcache + off, cp_off[0], kring_lds + kslot * (2 * S::KSLOT) + 1024 * wave,
+                     vcache + off, cp_off[1], vring_lds + vslot * (2 * S::VSLOT) + 1024 * wave);
+    } else {
+      static_assert(CPW == 1, "one or two copies per wave");
+      const bool isv = wave >= KCOPIES;
+      const int jj = isv ? wave - KCOPIES : wave;
       const int b = min(b0 + 2 * step + (64 * jj) / (2 * D), b_last);
       const uint64_t off = (uint64_t)(uint32_t)bt[b] * head_stride;
       const uint32_t lds = isv ? vring_lds + vslot * (2 * S::VSLOT) + 1024 * jj
                                : kring_lds + kslot * (2 * S::KSLOT) + 1024 * jj;
-      copy_to_lds<1>((isv ? vcache : kcache) + off, &cp_off[n], lds);
+      copy_to_lds((isv ? vcache : kcache) + off, cp_off[0], lds);
     }
   };
 
