@@ -264,6 +264,30 @@ def test_prefill_small(case):
     check_rows(b, out, range(b.num_seqs), f"prefill case {case}")
 
 
+@pytest.mark.parametrize("log2_scale", [13, -20])
+def test_prefill_values_across_fp16_range(log2_scale):
+    """The bf16-cache prefill kernel takes the values into its PV product as
+    fp16: exact for magnitudes in fp16's normal range, 2^-24 of absolute
+    resolution below it. Values scaled by 2^13 (up to ~4e4, inside the range)
+    must keep the bar scaled by the same factor; values scaled by 2^-20 (fp16
+    subnormals) must stay within 2^-24 absolute."""
+    ctx, ql = [700, 3000, 48], [300, 129, 48]
+    b = W.make_batch(f"vrange{log2_scale}", 400 + log2_scale, ctx, ql, 16, 4, 128, "bf16", "bf16",
+                     device=DEV, extra_blocks=3)
+    f = 2.0 ** log2_scale
+    b.v_cache.mul_(f)  # exact in bf16 (a power of two; NaN poison stays NaN)
+    assert torch.isfinite(b.v_cache[b.v_cache == b.v_cache]).all()
+    out = run_prefill(b)
+    torch.cuda.synchronize()
+    ref = oracle_rows(b, range(b.num_seqs))
+    got = out_f64(out)
+    cu = b.cu_seqlens
+    atol = 2e-3 * f if log2_scale > 0 else 2.0 ** -24
+    for s in range(b.num_seqs):
+        ma, mr = assert_close(got[cu[s]:cu[s + 1]], ref[s], f"values x 2^{log2_scale} seq {s}", atol=atol)
+        _log(f"values x 2^{log2_scale} seq {s}: max abs {ma:.3e} (bar {atol:.3e}), max rel {mr:.3e}")
+
+
 def test_random_shapes():
     """Seeded random small shapes over head size, group size, dtypes, context,
     chunk length and window (decode and prefill)."""
