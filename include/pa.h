@@ -1,7 +1,7 @@
 /*
  * pa.h — C ABI of libpa: attention over a paged KV cache on MI355X (gfx950).
  *
- * What the three calls compute (sources are the page titles and sections):
+ * What the calls compute (sources are the page titles and sections):
  *
  *  - pa_reshape_and_cache writes the new tokens' K and V into fixed-size
  *    physical blocks of 16 tokens through a per-token slot_mapping
@@ -15,6 +15,8 @@
  *    K/V by block table). Long contexts are split into key ranges whose
  *    partial softmax summaries are merged exactly ("宣稱省下 106 倍成本…",
  *    the online-softmax Q&A of "中：Kimi K3 的 DCP 選擇與 DEP 轉折").
+ *  - pa_decode_shared_prefix is pa_decode for batches whose sequences share
+ *    prefix blocks, reading each shared block once per group of sequences.
  *  - pa_prefill_chunk does the same for a flattened variable-length batch of
  *    causal query chunks (cu_seqlens), e.g. decode tokens and one chunk of a
  *    long prompt scheduled together under a token budget
@@ -131,6 +133,49 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
                     size_t workspace_bytes, pa_stream_t stream);
 
 /*
+ * Decode attention where runs of consecutive sequences share the physical
+ * blocks of a common prefix: a prefix cache points the block tables of
+ * sequences with identical leading content at the same refcounted blocks
+ * ("宣稱省下 106 倍成本…", "vLLM 的解法：統一分頁 + 共用池"), and agentic
+ * subagents fork from their parent's context, so most of a decode batch's
+ * keys can be shared ("Agentic Workload 為什麼難伺服：四個特徵與三個挑戰":
+ * prefix reuse above 96%). The result is exactly pa_decode's (the same
+ * attention, up to fp32 rounding order); what changes is that a group's
+ * shared blocks are read once per 16 query heads of its members instead of
+ * once per member, each member's own keys separately, and the partial softmax
+ * summaries merged exactly (the online-softmax Q&A of "中：Kimi K3 的 DCP
+ * 選擇與 DEP 轉折").
+ * num_groups: host scalar in [0, num_seqs].
+ * cu_groups: int32 [num_groups + 1], device: group k is the sequences
+ *   cu_groups[k] .. cu_groups[k+1]-1 (disjoint runs, non-decreasing,
+ *   cu_groups[num_groups] <= num_seqs); sequences outside every run, and
+ *   runs whose usable prefix (below) is shorter than one block, share
+ *   nothing. If the runs break these rules no group is used (checked on the
+ *   device; the result is pa_decode's either way).
+ * group_prefix_len: int32 [num_groups], device: tokens of group k's shared
+ *   prefix; every member's block table holds the same physical blocks for
+ *   logical blocks 0 .. group_prefix_len[k]/16 - 1 (the first member's table
+ *   is the one read). The kernel uses the length rounded down to whole blocks
+ *   and to at most every member's context length minus one (a member's own
+ *   newest token is never shared), so any value is memory-safe; values that
+ *   break the sharing precondition give wrong results, not faults.
+ * Other arguments, layouts and the workspace rules are pa_decode's; the
+ *   workspace must hold pa_decode_shared_prefix_workspace_bytes(...) bytes.
+ * The shared-block reading applies to (BF16, BF16) and (BF16, FP8_E4M3) with
+ *   sliding_window 0 and at most 3000 sequences; other requests (or
+ *   num_groups == 0) are served as pa_decode would serve them.
+ */
+pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_cache, const void* v_cache,
+                                  const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                  int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t max_context_len, const int32_t* cu_groups,
+                                  const int32_t* group_prefix_len, int32_t num_groups, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                  int32_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype, float scale,
+                                  int32_t sliding_window, void* workspace, size_t workspace_bytes,
+                                  pa_stream_t stream);
+
+/*
  * Causal attention for a flattened variable-length batch.
  * Sequence s owns query rows cu_seqlens[s] .. cu_seqlens[s+1]-1 (int32
  * [num_seqs+1]); context_lens[s] counts its cached tokens including this
@@ -157,6 +202,11 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
                                  int32_t num_kv_heads, int32_t head_size, pa_dtype cache_dtype,
                                  int32_t sliding_window);
+
+/* Workspace bytes pa_decode_shared_prefix needs for these sizes (0 if none). */
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_groups, int32_t max_context_len,
+                                               int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                               pa_dtype cache_dtype, int32_t sliding_window);
 
 /* Workspace bytes pa_prefill_chunk needs for these sizes (0 if none; the
  * one-token rows of a mixed batch use the decode plan). */

@@ -33,8 +33,10 @@ BLOCK_SIZE = 16
 EXPORTED = (
     "pa_reshape_and_cache",
     "pa_decode",
+    "pa_decode_shared_prefix",
     "pa_prefill_chunk",
     "pa_decode_workspace_bytes",
+    "pa_decode_shared_prefix_workspace_bytes",
     "pa_prefill_workspace_bytes",
     "pa_status_string",
     "pa_last_error",
@@ -66,6 +68,12 @@ def load() -> ctypes.CDLL:
     L.pa_decode.restype = ctypes.c_int
     L.pa_decode.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32,
                             ctypes.c_int, ctypes.c_int, ctypes.c_float, i32, vp, sz, vp]
+    L.pa_decode_shared_prefix.restype = ctypes.c_int
+    L.pa_decode_shared_prefix.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i32, vp, i32, i32, vp, vp, i32, i32,
+                                          i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_float, i32,
+                                          vp, sz, vp]
+    L.pa_decode_shared_prefix_workspace_bytes.restype = sz
+    L.pa_decode_shared_prefix_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
     L.pa_prefill_chunk.restype = ctypes.c_int
     L.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                    i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_float, i32,
@@ -144,6 +152,14 @@ def decode_workspace_bytes(num_seqs: int, max_context_len: int, num_heads: int, 
                                                 head_size, _cache_code(cache_dtype), sliding_window))
 
 
+def decode_shared_prefix_workspace_bytes(num_seqs: int, num_groups: int, max_context_len: int, num_heads: int,
+                                         num_kv_heads: int, head_size: int, cache_dtype="bf16",
+                                         sliding_window: int = 0) -> int:
+    return int(load().pa_decode_shared_prefix_workspace_bytes(num_seqs, num_groups, max_context_len, num_heads,
+                                                              num_kv_heads, head_size, _cache_code(cache_dtype),
+                                                              sliding_window))
+
+
 def prefill_workspace_bytes(num_seqs: int, num_q_tokens: int, max_q_len: int, max_context_len: int,
                             num_heads: int, num_kv_heads: int, head_size: int, cache_dtype="bf16",
                             sliding_window: int = 0) -> int:
@@ -180,6 +196,28 @@ def decode(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cach
                             S, int(max_context_len), Hq, Hkv, D, k_cache.shape[2], NB,
                             dtype_code(query.dtype), dtype_code(k_cache.dtype), float(scale),
                             int(sliding_window), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def decode_shared_prefix(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         block_table: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                         cu_groups: torch.Tensor, group_prefix_len: torch.Tensor, scale: float,
+                         k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                         sliding_window: int = 0, workspace: Optional[torch.Tensor] = None,
+                         stream=None) -> None:
+    """pa_decode_shared_prefix: pa_decode plus cu_groups int32 [G+1] (runs of
+    consecutive sequences) and group_prefix_len int32 [G] (shared tokens)."""
+    S, Hq, D = query.shape
+    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
+    NGr = group_prefix_len.numel()
+    assert cu_groups.dtype == torch.int32 and group_prefix_len.dtype == torch.int32
+    assert cu_groups.numel() == NGr + 1
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().pa_decode_shared_prefix(_ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                          _ptr(v_scale), _ptr(block_table), block_table.shape[1],
+                                          _ptr(context_lens), S, int(max_context_len), _ptr(cu_groups),
+                                          _ptr(group_prefix_len), NGr, Hq, Hkv, D, k_cache.shape[2], NB,
+                                          dtype_code(query.dtype), dtype_code(k_cache.dtype), float(scale),
+                                          int(sliding_window), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def prefill_chunk(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

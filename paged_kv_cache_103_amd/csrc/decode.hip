@@ -511,6 +511,15 @@ size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int num_head
   return slots * head_size * sizeof(float) + slots * 2 * sizeof(float);
 }
 
+size_t decode_shared_prefix_workspace_bytes(int num_seqs, int num_groups, int num_heads, int num_kv_heads,
+                                            int head_size) {
+  // records of 16 query columns; at most 2 * num_seqs streams per KV head
+  const size_t slots = (size_t)(8 * device_cu_count()) + (size_t)2 * num_seqs * num_kv_heads;
+  (void)num_heads;
+  return align256((size_t)shared_prefix_meta_ints(num_seqs, num_groups) * sizeof(int)) +
+         align256(slots * 16 * head_size * sizeof(float)) + slots * 16 * 2 * sizeof(float);
+}
+
 static bool group_ok(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
 bool decode_supported(int q_kind, int cache_kind, int head_size, int group) {

@@ -236,9 +236,9 @@ __device__ __forceinline__ void pair_step(WaveAcc<D>& acc, const PairRegs<CK, D>
 // (max, sum, unnormalised output) for the merge kernel.
 template <int D>
 __device__ __forceinline__ void wave_write(WaveAcc<D>& acc, const DecodeArgs& a, int slot, int qrow, int g, int G,
-                                           bool single, int c16, int q4) {
+                                           bool single, int c16, int q4, int ncols) {
   const float L = strided_sum<16>(acc.lsum);
-  if (c16 >= G) return;
+  if (c16 >= ncols) return;
   if (single) {
     const float inv = 1.f / L;
     uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * a.num_heads + g * G + c16) * D + 4 * q4;
@@ -250,7 +250,7 @@ __device__ __forceinline__ void wave_write(WaveAcc<D>& acc, const DecodeArgs& a,
       *reinterpret_cast<uint2*>(op + dt * 16) = w;
     }
   } else {
-    const size_t rec = (size_t)slot * G + c16;
+    const size_t rec = (size_t)slot * a.rec_cols + c16;
     float* op = a.part_o + rec * D + 4 * q4;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(op + dt * 16) = acc.o[dt];
@@ -299,15 +299,18 @@ __device__ __forceinline__ void wave_blocks(WaveAcc<D>& acc, const u32x4* qf, co
   }
 }
 
+// Query columns of a wave: column c16 < ncols is head g*G + c16 % G of query
+// row qrow + c16 / G (one row for a sequence's own keys; the rows of several
+// sequences for a shared prefix).
 template <int CK, int D>
 __device__ __forceinline__ void load_query(u32x4* qf, const DecodeArgs& a, int qrow, int g, int G, int c16,
-                                           int q4) {
+                                           int q4, int ncols) {
   constexpr int E = CacheElem<CK>::bytes;
 #pragma unroll
   for (int j = 0; j < D / 32; ++j) {
-    if (c16 < G) {
+    if (c16 < ncols) {
       const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) +
-                           ((size_t)qrow * a.num_heads + g * G + c16) * D + kstep_d0<E>(j, q4);
+                           ((size_t)(qrow + c16 / G) * a.num_heads + g * G + c16 % G) * D + kstep_d0<E>(j, q4);
       qf[j] = load16(qp);
     } else {
       qf[j] = u32x4{0, 0, 0, 0};
@@ -315,9 +318,10 @@ __device__ __forceinline__ void load_query(u32x4* qf, const DecodeArgs& a, int q
   }
 }
 
-// Blocks of sequence s's key range [lo, ctx) (0 for rows of longer chunks
-// in a mixed batch, which the prefill kernel serves).
-__device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int s, int& qrow, int& ctx, int& lo) {
+// Blocks of sequence s's own key range [lo, ctx) (0 for rows of longer
+// chunks in a mixed batch, which the prefill kernel serves); keys below
+// `shared` (a shared prefix read once for its group) are not its own.
+__device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int s, int& qrow, int& ctx, int& lo, int shared = 0) {
   qrow = s;
   ctx = 0;
   lo = 0;
@@ -327,23 +331,19 @@ __device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int s, int& qrow,
     qrow = q0;
   }
   ctx = a.context_lens[s];
-  lo = a.window > 0 ? max(0, ctx - a.window) : 0;
-  return ((ctx - 1) >> 4) - (lo >> 4) + 1;
+  lo = max(shared, a.window > 0 ? max(0, ctx - a.window) : 0);
+  return max(0, ((ctx - 1) >> 4) - (lo >> 4) + 1);
 }
 
-// Exclusive prefix sums of seq_blocks over the sequences, into psum[0..S]
-// (LDS), using 256 scan slots after them. Returns the total.
-__device__ __forceinline__ int block_prefix(const DecodeArgs& a, int* psum) {
-  int* scan = psum + a.num_seqs + 1;
+// Exclusive prefix sums of n(i), i < count, into out[0..count] (LDS), with a
+// 256-int scan scratch. Returns the total. Requires blockDim.x == 256.
+template <typename F>
+__device__ __forceinline__ int lds_exclusive_scan(int count, F n_of, int* out, int* scan) {
   const int tid = threadIdx.x;
   int running = 0;
-  for (int base = 0; base < a.num_seqs; base += 256) {
-    const int s = base + tid;
-    int n = 0;
-    if (s < a.num_seqs) {
-      int qr, cx, l0;
-      n = seq_blocks(a, s, qr, cx, l0);
-    }
+  for (int base = 0; base < count; base += 256) {
+    const int i = base + tid;
+    const int n = i < count ? n_of(i) : 0;
     scan[tid] = n;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
@@ -352,14 +352,70 @@ __device__ __forceinline__ int block_prefix(const DecodeArgs& a, int* psum) {
       scan[tid] += v;
       __syncthreads();
     }
-    if (s < a.num_seqs) psum[s] = running + scan[tid] - n;
+    if (i < count) out[i] = running + scan[tid] - n;
     running += scan[255];
     __syncthreads();
   }
-  if (tid == 0) psum[a.num_seqs] = running;
+  if (tid == 0) out[count] = running;
   __syncthreads();
   return running;
 }
+
+// Last index k in [0, n) with v[k] <= x (v non-decreasing, v[0] <= x).
+__device__ __forceinline__ int last_le(const int* v, int n, long long x, long long scale = 1) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((long long)v[mid] * scale <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Shared prefixes: sequences [cu_groups[k], cu_groups[k+1]) read the
+// physical blocks of their first `prefix` tokens in common. Fills, in LDS,
+// sg[s] = group of sequence s (-1: none), effp[k] = the prefix each member
+// can use (the given length, at most every member's context minus its own
+// new token, in whole blocks) and cbase = exclusive prefix sums of the
+// groups' column chunks (16/G members per chunk). Returns the chunk count.
+//
+// Groups must be disjoint ordered runs (0 <= cu_groups[k] <= cu_groups[k+1]
+// <= S); if they are not, no group is used and the result is plain decode
+// (the groups only change which reads are shared, never the result).
+__device__ __forceinline__ int shared_prefix_setup(const DecodeArgs& a, int G, int* sg, int* cbase, int* effp,
+                                                   int* scan) {
+  const int S = a.num_seqs, MPC = 16 / G;
+  int bad = 0;
+  for (int k = threadIdx.x; k < a.num_groups; k += 256) {
+    const int b = a.cu_groups[k], e = a.cu_groups[k + 1];
+    bad |= (b < 0) | (e < b) | (e > S);
+  }
+  const int NG = __syncthreads_or(bad) ? 0 : a.num_groups;
+  for (int s = threadIdx.x; s < S; s += 256) sg[s] = -1;
+  if (threadIdx.x == 0) cbase[0] = 0;
+  __syncthreads();
+  for (int k = threadIdx.x; k < NG; k += 256) {
+    const int b = min(max(a.cu_groups[k], 0), S), e = min(max(a.cu_groups[k + 1], b), S);
+    int minctx = 0x7fffffff;
+    for (int s = b; s < e; ++s) minctx = min(minctx, a.context_lens[s]);
+    const int p = e > b ? max(0, min(a.group_prefix_len[k], minctx - 1)) & ~15 : 0;
+    effp[k] = p;
+    if (p > 0)  // a group without a whole shared block shares nothing
+      for (int s = b; s < e; ++s) sg[s] = k;
+  }
+  __syncthreads();
+  return lds_exclusive_scan(
+      NG,
+      [&](int k) {
+        const int b = min(max(a.cu_groups[k], 0), S), e = min(max(a.cu_groups[k + 1], b), S);
+        return effp[k] > 0 ? (e - b + MPC - 1) / MPC : 0;
+      },
+      cbase, scan);
+}
+
+// Offsets into the meta buffer the split kernel leaves for the merge kernel.
+__host__ __device__ __forceinline__ int meta_sg(int S) { return 2 + 2 * S; }
+__host__ __device__ __forceinline__ int meta_cbase(int S) { return 2 + 3 * S; }
+int shared_prefix_meta_ints(int num_seqs, int num_groups) { return meta_cbase(num_seqs) + num_groups + 1; }
 
 // Blocks each wave takes: an even share of T block-heads, at least 8 and even.
 __device__ __forceinline__ int split_chunk(int total, int nwaves) {
@@ -375,23 +431,53 @@ __device__ __forceinline__ int split_chunk(int total, int nwaves) {
 // a stream covered by one segment is finished in place, others leave one
 // (max, sum, unnormalised output) summary per segment in slot wave + stream
 // for the merge kernel.
-template <int CK, int D>
+//
+// With shared prefixes (SHARED), the streams of the sequences cover only
+// their own keys after their group's prefix, and after them come one stream
+// per (column chunk of a group, KV head) over the prefix blocks: its MFMA
+// columns are the query heads of up to 16/G member sequences, so a shared
+// block is read once per chunk instead of once per member. Every member's
+// summaries (its own stream's and its chunk's) go to the merge kernel.
+template <int CK, int D, bool SHARED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mfma_split(
     DecodeArgs a) {
   using S = MfmaDecodeShape<CK, D>;
-  extern __shared__ int psum[];  // [num_seqs + 1] block prefix sums, then 256 scan slots
+  // LDS: [sg S][cbase NG+1][effp NG] (shared prefixes only), psum over the
+  // streams, 256 scan slots
+  extern __shared__ int lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15, q4 = lane >> 4;
   const int H = a.num_kv_heads;
   const int G = a.num_heads / H;
+  const int NSEQ = a.num_seqs;
+  const int NG = SHARED ? a.num_groups : 0;
+  int* sg = lds;
+  int* cbase = sg + NSEQ;
+  int* effp = cbase + NG + 1;
+  int* psum = SHARED ? effp + NG : lds;
+  int* scan = psum + (SHARED ? 2 * NSEQ + 1 : NSEQ + 1);
 
-  const int per_head = block_prefix(a, psum);
+  int nstreams = NSEQ;
+  if constexpr (SHARED) nstreams += shared_prefix_setup(a, G, sg, cbase, effp, scan);
+  const int per_head = lds_exclusive_scan(
+      nstreams,
+      [&](int i) {
+        int qr, cx, l0;
+        if (!SHARED) return seq_blocks(a, i, qr, cx, l0);
+        if (i < NSEQ) return seq_blocks(a, i, qr, cx, l0, sg[i] >= 0 ? effp[sg[i]] : 0);
+        return effp[last_le(cbase, NG, i - NSEQ)] >> 4;
+      },
+      psum, scan);
   const long long T = (long long)per_head * H;
   const int C = split_chunk((int)min<long long>(T, 0x7fffffff), a.split_waves);
   if (blockIdx.x == 0) {  // for the merge kernel
     if (tid == 0) a.meta[0] = C;
-    for (int s = tid; s <= a.num_seqs; s += 256) a.meta[1 + s] = psum[s];
+    for (int i = tid; i <= nstreams; i += 256) a.meta[1 + i] = psum[i];
+    if constexpr (SHARED) {
+      for (int i = tid; i < NSEQ; i += 256) a.meta[meta_sg(NSEQ) + i] = sg[i];
+      for (int i = tid; i <= NG; i += 256) a.meta[meta_cbase(NSEQ) + i] = cbase[i];
+    }
   }
 
   const int w = blockIdx.x * 4 + wave;
@@ -399,65 +485,104 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const size_t head_stride = (size_t)H * S::TILE;
   long long x = (long long)w * C;
   while (x < x_end) {
-    // stream containing block-head x: sequence = last s with psum[s]*H <= x
-    int lo_s = 0, hi_s = a.num_seqs;  // psum[lo_s]*H <= x < psum[hi_s]*H
-    while (hi_s - lo_s > 1) {
-      const int mid = (lo_s + hi_s) >> 1;
-      if ((long long)psum[mid] * H <= x) lo_s = mid; else hi_s = mid;
-    }
-    const int s = lo_s;
-    const int nb = psum[s + 1] - psum[s];
-    const long long base = (long long)psum[s] * H;
+    // stream containing block-head x: last i with psum[i]*H <= x
+    const int i = last_le(psum, nstreams, x, H);
+    const int nb = psum[i + 1] - psum[i];
+    const long long base = (long long)psum[i] * H;
     const int g = (int)((x - base) / nb);
     const long long sstart = base + (long long)g * nb;  // this stream's first block-head
     const long long seg_end = min(x_end, sstart + nb);
-    int qrow, ctx, lo;
-    seq_blocks(a, s, qrow, ctx, lo);
-    const int blk0 = (lo >> 4) + (int)(x - sstart);
-    const int blk1 = (lo >> 4) + (int)(seg_end - sstart);
-    const int kend = min(ctx, blk1 * 16);
-
+    const uint8_t* kcache = reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)g * S::TILE;
+    const uint8_t* vcache = reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * S::TILE;
+    const int slot = w + i * H + g;
     u32x4 qf[S::DS];
-    load_query<CK, D>(qf, a, qrow, g, G, c16, q4);
     WaveAcc<D> acc;
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt) acc.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     acc.m = -INFINITY;
     acc.lsum = 0.f;
-    const uint8_t* kcache = reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)g * S::TILE;
-    const uint8_t* vcache = reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * S::TILE;
-    wave_blocks<CK, D>(acc, qf, kcache, vcache, a.block_table + (size_t)s * a.bt_stride, blk0, 2, blk1, lo,
-                       kend, head_stride, a, c16, q4);
-    const int stream = s * H + g;
-    const bool single = (sstart / C) == ((sstart + nb - 1) / C);
-    wave_write<D>(acc, a, w + stream, qrow, g, G, single, c16, q4);
+    if (!SHARED || i < NSEQ) {
+      const int s = i;
+      const bool grouped = SHARED && sg[s] >= 0;
+      int qrow, ctx, lo;
+      seq_blocks(a, s, qrow, ctx, lo, grouped ? effp[sg[s]] : 0);
+      const int blk0 = (lo >> 4) + (int)(x - sstart);
+      const int blk1 = (lo >> 4) + (int)(seg_end - sstart);
+      const int kend = min(ctx, blk1 * 16);
+      load_query<CK, D>(qf, a, qrow, g, G, c16, q4, G);
+      wave_blocks<CK, D>(acc, qf, kcache, vcache, a.block_table + (size_t)s * a.bt_stride, blk0, 2, blk1, lo,
+                         kend, head_stride, a, c16, q4);
+      const bool single = !grouped && (sstart / C) == ((sstart + nb - 1) / C);
+      wave_write<D>(acc, a, slot, qrow, g, G, single, c16, q4, G);
+    } else {
+      // column chunk j of group k: members m0 .. m0 + nmem - 1, prefix blocks
+      // read through the first member's table
+      const int c = i - NSEQ;
+      const int k = last_le(cbase, NG, c);
+      const int MPC = 16 / G;
+      const int first = min(max(a.cu_groups[k], 0), NSEQ);
+      const int end = min(max(a.cu_groups[k + 1], first), NSEQ);
+      const int m0 = first + (c - cbase[k]) * MPC;
+      const int nmem = min(MPC, end - m0);
+      const int blk0 = (int)(x - sstart);
+      const int blk1 = (int)(seg_end - sstart);
+      load_query<CK, D>(qf, a, m0, g, G, c16, q4, nmem * G);
+      wave_blocks<CK, D>(acc, qf, kcache, vcache, a.block_table + (size_t)first * a.bt_stride, blk0, 2, blk1, 0,
+                         blk1 * 16, head_stride, a, c16, q4);
+      wave_write<D>(acc, a, slot, 0, g, G, false, c16, q4, nmem * G);
+    }
     x = seg_end;
   }
 }
 
-// Exact merge of one stream's segment summaries: one wave per (sequence,
-// query head); M = max m_i, L = sum l_i 2^(m_i - M), out = sum o_i 2^(m_i - M) / L.
-template <int D>
+// Exact merge of a (sequence, query head)'s summaries: one wave each;
+// M = max m_i, L = sum l_i 2^(m_i - M), out = sum o_i 2^(m_i - M) / L. The
+// summaries are the segments of the sequence's own stream and, with shared
+// prefixes, those of its group chunk's stream (column of the member).
+template <int D, bool SHARED>
 __global__ __launch_bounds__(256) void decode_split_merge(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (idx >= a.num_seqs * a.num_heads) return;
-  const int H = a.num_kv_heads, G = a.num_heads / H;
+  const int H = a.num_kv_heads, G = a.num_heads / H, NSEQ = a.num_seqs;
   const int s = idx / a.num_heads, hq = idx % a.num_heads, g = hq / G, h = hq % G;
   const int* psum = a.meta + 1;
-  const int nb = psum[s + 1] - psum[s];
-  if (nb == 0) return;
   const int C = a.meta[0];
+  // the sequence's own stream: segments w0..w1, summary slot w + stream
+  const int nb = psum[s + 1] - psum[s];
   const long long sstart = (long long)psum[s] * H + (long long)g * nb;
-  const int w0 = (int)(sstart / C), w1 = (int)((sstart + nb - 1) / C);
-  if (w0 == w1) return;  // finished in place
+  const int w0 = (int)(sstart / C), w1 = nb > 0 ? (int)((sstart + nb - 1) / C) : w0 - 1;
+  const int n1 = w1 - w0 + 1;
+  const int stream1 = s * H + g;
+  // its group chunk's stream, if any
+  int n2 = 0, w20 = 0, stream2 = 0, col2 = 0;
+  if constexpr (SHARED) {
+    const int k = a.meta[meta_sg(NSEQ) + s];
+    if (k >= 0) {
+      const int MPC = 16 / G;
+      const int mi = s - min(max(a.cu_groups[k], 0), NSEQ);
+      const int i2 = NSEQ + a.meta[meta_cbase(NSEQ) + k] + mi / MPC;
+      const int nb2 = psum[i2 + 1] - psum[i2];
+      if (nb2 > 0) {
+        const long long st2 = (long long)psum[i2] * H + (long long)g * nb2;
+        w20 = (int)(st2 / C);
+        n2 = (int)((st2 + nb2 - 1) / C) - w20 + 1;
+        stream2 = i2 * H + g;
+        col2 = (mi % MPC) * G + h;
+      }
+    }
+  }
+  if (n2 == 0 && n1 == 1) return;  // finished in place
   int qrow = s;
   if (a.cu_seqlens != nullptr) qrow = a.cu_seqlens[s];
-  const int stream = s * H + g;
-  const int n = w1 - w0 + 1;
-  // slot of segment i: w0 + i + stream
+  const int n = n1 + n2;
+  // record of summary i: (slot, column)
+  auto rec = [&](int i) -> size_t {
+    return i < n1 ? (size_t)(w0 + i + stream1) * a.rec_cols + h
+                  : (size_t)(w20 + (i - n1) + stream2) * a.rec_cols + col2;
+  };
   float M = -INFINITY;
-  for (int i = lane; i < n; i += 64) M = fmaxf(M, a.part_ml[((size_t)(w0 + i + stream) * G + h) * 2]);
+  for (int i = lane; i < n; i += 64) M = fmaxf(M, a.part_ml[rec(i) * 2]);
   M = strided_max<1>(M);
   constexpr int DL = D / 64;
   float o[DL];
@@ -466,17 +591,17 @@ __global__ __launch_bounds__(256) void decode_split_merge(DecodeArgs a) {
   float L = 0.f;
   for (int i0 = 0; i0 < n; i0 += 64) {
     const int i = i0 + lane;
-    const size_t slot = (size_t)(w0 + i + stream);
-    const float wgt = (i < n) ? __builtin_amdgcn_exp2f(a.part_ml[(slot * G + h) * 2] - M) : 0.f;
-    if (i < n) L += a.part_ml[(slot * G + h) * 2 + 1] * wgt;
+    const float wgt = (i < n) ? __builtin_amdgcn_exp2f(a.part_ml[rec(i) * 2] - M) : 0.f;
+    if (i < n) L += a.part_ml[rec(i) * 2 + 1] * wgt;
     const int cnt = min(64, n - i0);
     for (int j0 = 0; j0 < cnt; j0 += 8) {
       float v[8][DL];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const float* row = a.part_o + ((size_t)(w0 + i0 + j0 + u + stream) * G + h) * D;
+        const bool ok = j0 + u < cnt;
+        const float* row = a.part_o + (ok ? rec(i0 + j0 + u) : 0) * D;
 #pragma unroll
-        for (int k = 0; k < DL; ++k) v[u][k] = (j0 + u < cnt) ? row[k * 64 + lane] : 0.f;
+        for (int k = 0; k < DL; ++k) v[u][k] = ok ? row[k * 64 + lane] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -494,27 +619,31 @@ __global__ __launch_bounds__(256) void decode_split_merge(DecodeArgs a) {
         f32_to_bf16(o[k] * inv);
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int cache_kind, int head_size, hipStream_t st) {
+template <int CK, int D, bool SHARED>
+static hipError_t run_decode_mfma(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.split_waves / 4));
-  const size_t lds = (size_t)(a.num_seqs + 1 + 256) * sizeof(int);
-  if (cache_kind == KBF16 && head_size == 128)
-    hipLaunchKernelGGL((decode_mfma_split<KBF16, 128>), grid, dim3(256), lds, st, a);
-  else if (cache_kind == KBF16 && head_size == 64)
-    hipLaunchKernelGGL((decode_mfma_split<KBF16, 64>), grid, dim3(256), lds, st, a);
-  else if (cache_kind == KFP8 && head_size == 128)
-    hipLaunchKernelGGL((decode_mfma_split<KFP8, 128>), grid, dim3(256), lds, st, a);
-  else if (cache_kind == KFP8 && head_size == 64)
-    hipLaunchKernelGGL((decode_mfma_split<KFP8, 64>), grid, dim3(256), lds, st, a);
-  else
-    return hipErrorInvalidValue;
+  const size_t lds = SHARED ? (size_t)(3 * a.num_seqs + 2 * a.num_groups + 2 + 256) * sizeof(int)
+                            : (size_t)(a.num_seqs + 1 + 256) * sizeof(int);
+  hipLaunchKernelGGL((decode_mfma_split<CK, D, SHARED>), grid, dim3(256), lds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int waves = a.num_seqs * a.num_heads;
-  if (head_size == 128)
-    hipLaunchKernelGGL((decode_split_merge<128>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_split_merge<64>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_split_merge<D, SHARED>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+template <bool SHARED>
+static hipError_t run_decode_mfma_kind(const DecodeArgs& a, int cache_kind, int head_size, hipStream_t st) {
+  if (cache_kind == KBF16 && head_size == 128) return run_decode_mfma<KBF16, 128, SHARED>(a, st);
+  if (cache_kind == KBF16 && head_size == 64) return run_decode_mfma<KBF16, 64, SHARED>(a, st);
+  if (cache_kind == KFP8 && head_size == 128) return run_decode_mfma<KFP8, 128, SHARED>(a, st);
+  if (cache_kind == KFP8 && head_size == 64) return run_decode_mfma<KFP8, 64, SHARED>(a, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int cache_kind, int head_size, hipStream_t st) {
+  return a.num_groups > 0 ? run_decode_mfma_kind<true>(a, cache_kind, head_size, st)
+                          : run_decode_mfma_kind<false>(a, cache_kind, head_size, st);
 }
 
 }  // namespace pa

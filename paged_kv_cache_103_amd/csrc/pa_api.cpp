@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -153,6 +154,10 @@ static void bind_workspace(pa::DecodeArgs& a, const pa::DecodePlan& plan, void* 
   a.meta = nullptr;
   a.part_o = nullptr;
   a.part_ml = nullptr;
+  a.cu_groups = nullptr;
+  a.group_prefix_len = nullptr;
+  a.num_groups = 0;
+  a.rec_cols = num_heads / num_kv_heads;
   if (workspace == nullptr) return;
   char* ws = static_cast<char*>(workspace);
   if (plan.split_waves > 0) {
@@ -231,6 +236,92 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = pa::launch_decode(a, (int)q_dtype, (int)cache_dtype, head_size, (hipStream_t)stream);
   return hip_status(e, "decode launch");
+}
+
+// Whether pa_decode_shared_prefix reads shared blocks once (else it serves
+// the request as pa_decode).
+static bool shared_prefix_applies(int32_t num_seqs, int32_t num_groups, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_size, pa_dtype cache_dtype, int32_t sliding_window) {
+  if (num_groups <= 0 || num_seqs <= 0 || num_seqs > pa::kSharedPrefixMaxSeqs || sliding_window != 0) return false;
+  if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return false;
+  const pa::DecodePlan plan = make_plan(num_seqs, 1, num_heads, num_kv_heads, head_size, cache_dtype, 0);
+  return plan.split_waves > 0;
+}
+
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_groups, int32_t max_context_len,
+                                               int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                               pa_dtype cache_dtype, int32_t sliding_window) {
+  if (!shared_prefix_applies(num_seqs, num_groups, num_heads, num_kv_heads, head_size, cache_dtype,
+                             sliding_window))
+    return pa_decode_workspace_bytes(num_seqs, max_context_len, num_heads, num_kv_heads, head_size, cache_dtype,
+                                     sliding_window);
+  return pa::decode_shared_prefix_workspace_bytes(num_seqs, num_groups, num_heads, num_kv_heads, head_size);
+}
+
+pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_cache, const void* v_cache,
+                                  const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                  int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t max_context_len, const int32_t* cu_groups,
+                                  const int32_t* group_prefix_len, int32_t num_groups, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                  int32_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype, float scale,
+                                  int32_t sliding_window, void* workspace, size_t workspace_bytes,
+                                  pa_stream_t stream) {
+  if (num_groups < 0 || num_groups > std::max(num_seqs, 0))
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_groups must be in [0, num_seqs] (got %d for %d sequences)",
+                num_groups, num_seqs);
+  if (num_groups > 0 && (!cu_groups || !group_prefix_len))
+    return fail(PA_ERR_INVALID_ARGUMENT, "null device pointer (cu_groups / group_prefix_len)");
+  pa_status st = check_attention_common(out, query, k_cache, v_cache, k_scale, v_scale, block_table,
+                                        block_table_stride, context_lens, num_seqs, max_context_len,
+                                        num_heads, num_kv_heads, head_size, block_size, num_blocks,
+                                        q_dtype, cache_dtype, scale, sliding_window);
+  if (st != PA_OK) return st;
+  if (!shared_prefix_applies(num_seqs, num_groups, num_heads, num_kv_heads, head_size, cache_dtype,
+                             sliding_window))
+    return pa_decode(out, query, k_cache, v_cache, k_scale, v_scale, block_table, block_table_stride,
+                     context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_size, block_size,
+                     num_blocks, q_dtype, cache_dtype, scale, sliding_window, workspace, workspace_bytes,
+                     stream);
+  const size_t need = pa::decode_shared_prefix_workspace_bytes(num_seqs, num_groups, num_heads, num_kv_heads,
+                                                               head_size);
+  if (workspace_bytes < need || workspace == nullptr)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "shared-prefix decode needs %zu workspace bytes (got %zu)", need,
+                workspace_bytes);
+  const pa::DecodePlan plan = make_plan(num_seqs, max_context_len, num_heads, num_kv_heads, head_size,
+                                        cache_dtype, sliding_window);
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.query = query;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.cu_seqlens = nullptr;
+  a.pb = plan.pb;
+  a.max_parts = plan.max_parts;
+  a.split_waves = plan.split_waves;
+  char* ws = static_cast<char*>(workspace);
+  const size_t slots = (size_t)plan.split_waves + (size_t)2 * num_seqs * num_kv_heads;
+  a.meta = reinterpret_cast<int*>(ws);
+  ws += align256((size_t)pa::shared_prefix_meta_ints(num_seqs, num_groups) * sizeof(int));
+  a.part_o = reinterpret_cast<float*>(ws);
+  ws += align256(slots * 16 * head_size * sizeof(float));
+  a.part_ml = reinterpret_cast<float*>(ws);
+  a.cu_groups = cu_groups;
+  a.group_prefix_len = group_prefix_len;
+  a.num_groups = num_groups;
+  a.rec_cols = 16;
+  a.bt_stride = block_table_stride;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.window = 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pa::launch_decode(a, (int)q_dtype, (int)cache_dtype, head_size, (hipStream_t)stream);
+  return hip_status(e, "shared-prefix decode launch");
 }
 
 pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, const void* v_cache,

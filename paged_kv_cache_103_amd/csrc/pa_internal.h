@@ -37,6 +37,12 @@ DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num
                        int q_kind, int cache_kind, int sliding_window);
 size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int num_heads, int num_kv_heads,
                               int head_size);
+// Decode with groups of sequences sharing prefix blocks (matrix-core kernel
+// only): workspace, the largest batch it serves, and the launch.
+size_t decode_shared_prefix_workspace_bytes(int num_seqs, int num_groups, int num_heads, int num_kv_heads,
+                                            int head_size);
+constexpr int kSharedPrefixMaxSeqs = 3000;
+int shared_prefix_meta_ints(int num_seqs, int num_groups);
 bool decode_uses_mfma(int q_kind, int cache_kind, int group);
 int device_cu_count();
 
@@ -54,6 +60,11 @@ struct DecodeArgs {
                           // split plan: [slots][group][head_size]
   float* part_ml;         // running max (log2 units) and sum per summary
   int* meta;              // split plan: [0] = blocks per wave, [1 + s] = block prefix sums
+                          // (with shared prefixes: then group of each sequence and chunk bases)
+  const int* cu_groups;   // shared prefixes: group k = sequences [cu_groups[k], cu_groups[k+1])
+  const int* group_prefix_len;  // shared prefixes: tokens of group k's shared blocks (multiple of 16)
+  int num_groups;         // 0: no shared prefixes
+  int rec_cols;           // query columns per summary record (group size G, or 16 with shared prefixes)
   int bt_stride;
   int num_seqs;
   int num_heads;

@@ -66,6 +66,7 @@ class Batch:
     new_key: torch.Tensor             # [T][Hkv][D] (q dtype for fp8 pools, else cache dtype)
     new_value: torch.Tensor
     shared_groups: List[List[int]] = field(default_factory=list)
+    shared_prefix: Dict[int, int] = field(default_factory=dict)   # group index -> shared tokens
     device_meta: Dict[str, torch.Tensor] = field(default_factory=dict)
 
     # ---- derived sizes ----
@@ -98,6 +99,32 @@ class Batch:
                 "context_lens": torch.from_numpy(self.context_lens).to(device),
                 "cu_seqlens": torch.from_numpy(self.cu_seqlens).to(device),
                 "slot_mapping": torch.from_numpy(self.slot_mapping).to(device),
+            }
+        return self.device_meta[key]
+
+    def group_meta(self, device) -> Dict[str, torch.Tensor]:
+        """cu_groups int32 [G+1] and group_prefix_len int32 [G] of the shared
+        groups as the shared-prefix decode takes them: each group a run of
+        consecutive sequences, runs in order; sequences between runs are
+        given as runs of one with no shared prefix."""
+        key = "groups:" + str(device)
+        if key not in self.device_meta:
+            groups = sorted((sorted(g), self.shared_prefix.get(gi, 0)) for gi, g in enumerate(self.shared_groups))
+            cu, pl = [], []
+            nxt = groups[0][0][0] if groups else 0
+            for members, p in groups:
+                assert members == list(range(members[0], members[0] + len(members))), "groups must be runs"
+                while nxt < members[0]:
+                    cu.append(nxt)
+                    pl.append(0)
+                    nxt += 1
+                cu.append(members[0])
+                pl.append(p)
+                nxt = members[-1] + 1
+            cu.append(nxt)
+            self.device_meta[key] = {
+                "cu_groups": torch.tensor(cu, dtype=torch.int32).to(device),
+                "group_prefix_len": torch.tensor(pl, dtype=torch.int32).to(device),
             }
         return self.device_meta[key]
 
@@ -260,7 +287,8 @@ def make_batch(name: str, seed: int, ctx_lens: Sequence[int], q_lens: Sequence[i
                  q_lens=np.asarray(q_lens, dtype=np.int32), block_table=table, num_blocks=NB,
                  slot_mapping=slot_mapping, query=query, k_cache=k_cache, v_cache=v_cache,
                  k_scale=k_scale, v_scale=v_scale, new_key=new_key, new_value=new_value,
-                 shared_groups=[list(g) for g in shared_groups])
+                 shared_groups=[list(g) for g in shared_groups],
+                 shared_prefix=dict(shared_prefix or {}))
 
 
 # ----------------------------------------------------------------------------

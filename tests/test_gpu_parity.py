@@ -181,6 +181,62 @@ def test_decode_agentic_sampled():
         assert len({int(b.context_lens[s]) for s in grp}) == 1
 
 
+def run_decode_shared(b, out=None):
+    m = b.meta(DEV)
+    gm = b.group_meta(DEV)
+    out = torch.empty_like(b.query) if out is None else out
+    ng = gm["group_prefix_len"].numel()
+    ws_bytes = pa.decode_shared_prefix_workspace_bytes(b.num_seqs, ng, b.max_context_len, b.num_heads,
+                                                       b.num_kv_heads, b.head_size, b.cache_dtype,
+                                                       b.sliding_window)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=DEV)
+    pa.decode_shared_prefix(out, b.query, b.k_cache, b.v_cache, m["block_table"], m["context_lens"],
+                            b.max_context_len, gm["cu_groups"], gm["group_prefix_len"], b.scale, b.k_scale,
+                            b.v_scale, b.sliding_window, ws)
+    return out
+
+
+def test_decode_shared_prefix_agentic():
+    """The agentic batch through the shared-prefix decode (each group's
+    prefix blocks read once for its four members): the oracle on one member
+    of every group, and the plain decode's result within the same bar."""
+    b = W.make_config("agentic_decode", device=DEV)
+    out = run_decode_shared(b)
+    ref_plain = out_f64(run_decode(b))
+    torch.cuda.synchronize()
+    check_rows(b, out, [grp[i % len(grp)] for i, grp in enumerate(b.shared_groups)], "agentic shared-prefix")
+    got = out_f64(out)
+    ma, mr = assert_close(got, ref_plain, "agentic shared-prefix vs plain decode")
+    _log(f"agentic shared-prefix vs plain decode: max abs {ma:.2e}, max rel {mr:.2e}")
+
+
+SHARED_CASES = [
+    # (ctx lens, groups [(first, size, prefix tokens)], Hq, Hkv, D, cache dtype)
+    ([40, 40, 40, 40, 100, 7, 33, 33], [(0, 4, 32), (4, 1, 64), (6, 2, 32)], 16, 4, 128, "bf16"),
+    ([300, 310, 290, 305, 320, 299], [(0, 6, 288)], 32, 8, 128, "bf16"),         # 6 members > 16/G = 2
+    ([1000, 1017, 1001], [(0, 3, 1000)], 8, 8, 64, "bf16"),                      # G = 1: 16 members per chunk
+    ([5000, 4990, 17, 4999], [(0, 2, 4096), (3, 1, 4000)], 64, 4, 128, "bf16"),  # G = 16: one member per chunk
+    ([700, 650, 800, 720, 20], [(0, 4, 640), (4, 1, 0)], 16, 2, 64, "fp8_e4m3"),
+    ([129, 129, 129], [(0, 3, 4096)], 8, 2, 128, "bf16"),                         # prefix clamped to ctx - 1
+    ([64, 80, 96, 112, 128, 144, 160, 176, 192], [(1, 8, 48)], 32, 8, 128, "fp8_e4m3"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SHARED_CASES)))
+def test_decode_shared_prefix_small(case):
+    ctx, groups, Hq, Hkv, D, cd = SHARED_CASES[case]
+    sg = [list(range(f, f + n)) for f, n, _ in groups]
+    sp = {gi: p for gi, (_, _, p) in enumerate(groups)}
+    # blocks really shared only up to what every member can hold
+    sp_blocks = {gi: min(p, min(ctx[s] for s in sg[gi]) - 1) // 16 * 16 for gi, p in sp.items()}
+    b = W.make_batch(f"shared{case}", 500 + case, ctx, [1] * len(ctx), Hq, Hkv, D, "bf16", cd,
+                     shared_groups=sg, shared_prefix=sp_blocks, device=DEV, extra_blocks=3)
+    b.shared_prefix = sp  # the call gets the unclamped lengths
+    out = run_decode_shared(b)
+    torch.cuda.synchronize()
+    check_rows(b, out, range(b.num_seqs), f"shared-prefix case {case}")
+
+
 def test_decode_fp8_sampled():
     b = W.make_config("fp8_decode", device=DEV)
     out = run_decode(b)
