@@ -148,3 +148,34 @@ def test_workspace_queries(lib):
         lib.decode_workspace_bytes(193, 67584, 32, 8, 128, "bf16")
     # no one-token rows possible: no workspace
     assert lib.prefill_workspace_bytes(2, 600, 300, 5000, 32, 8, 128, "bf16") == 0
+
+
+def test_shared_prefix_rejects_bad_arguments(lib):
+    L = lib.load()
+
+    def call(**over):
+        a = dict(cu=1, plen=1, ng=1, num_seqs=4, q_dtype=1, cache_dtype=1, window=0, ws=1, ws_bytes=1 << 30)
+        a.update(over)
+        return L.pa_decode_shared_prefix(1, 1, 1, 1, None, None, 1, 8, 1, a["num_seqs"], 100, a["cu"], a["plen"],
+                                         a["ng"], 8, 2, 128, 16, 10, a["q_dtype"], a["cache_dtype"], 0.1,
+                                         a["window"], a["ws"], a["ws_bytes"], None)
+
+    assert call(ng=-1) == 1 and "num_groups" in lib.last_error()
+    assert call(ng=5) == 1 and "num_groups" in lib.last_error()      # more groups than sequences
+    assert call(cu=None) == 1 and "cu_groups" in lib.last_error()
+    assert call(plen=None) == 1 and "cu_groups" in lib.last_error()
+    assert call(block_size=16, ws_bytes=16) == 3 and "shared-prefix" in lib.last_error()
+    # the checks pa_decode makes apply too
+    assert call(q_dtype=2) == 2 and "fp8 queries" in lib.last_error()
+
+
+def test_shared_prefix_workspace_falls_back_to_decode(lib):
+    # sharing applies: its own (larger) workspace; otherwise pa_decode's
+    shared = lib.decode_shared_prefix_workspace_bytes(16, 4, 262144, 32, 8, 128, "bf16")
+    plain = lib.decode_workspace_bytes(16, 262144, 32, 8, 128, "bf16")
+    assert shared > plain > 0
+    assert lib.decode_shared_prefix_workspace_bytes(16, 0, 262144, 32, 8, 128, "bf16") == plain
+    assert lib.decode_shared_prefix_workspace_bytes(16, 4, 262144, 32, 8, 128, "bf16", 128) == \
+        lib.decode_workspace_bytes(16, 262144, 32, 8, 128, "bf16", 128)
+    assert lib.decode_shared_prefix_workspace_bytes(4, 2, 300, 8, 2, 64, "f32") == \
+        lib.decode_workspace_bytes(4, 300, 8, 2, 64, "f32")
