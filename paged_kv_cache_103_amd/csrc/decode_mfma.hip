@@ -152,9 +152,13 @@ __device__ __forceinline__ void pair_step(WaveAcc<D>& acc, const PairRegs<CK, D>
   // this lane's keys: b*16 + 8*q4 + 4*kt + r, all in block b + q4/2
   float ks = a.scale_log2, vs = 1.f;
   if constexpr (CK == KFP8) {
-  const size_t phys = (q4 >> 1) ? phys1 : phys0;
-  ks *= a.k_scale[phys];
-  vs = a.v_scale[phys];
+  // the pair's two blocks' scales by scalar loads (uniform ids), then per lane
+  typedef __attribute__((address_space(4))) const float cfloat;
+  const cfloat* kss = (const cfloat*)(a.k_scale);
+  const cfloat* vss = (const cfloat*)(a.v_scale);
+  const float k0 = kss[phys0], k1 = kss[phys1], v0 = vss[phys0], v1 = vss[phys1];
+  ks *= (q4 >> 1) ? k1 : k0;
+  vs = (q4 >> 1) ? v1 : v0;
   }
   const int key0 = b * 16 + 8 * q4;
   float x[2][4];
@@ -261,41 +265,60 @@ __device__ __forceinline__ void wave_write(WaveAcc<D>& acc, const DecodeArgs& a,
   }
 }
 
-// Blocks of one partition not taken by the wave: the running pair loop with
-// the next pair's loads in flight while one is computed.
+// The blocks [b, blk1) of one stream segment, in pairs, with the next pair's
+// loads in flight while one is computed. Only the first pair (a window
+// start) and the last (context or segment end) can need masks; the pairs in
+// between run in a loop whose loads are unconditional, so that the compiler
+// keeps one pair's loads outstanding across the other's arithmetic.
 template <int CK, int D>
 __device__ __forceinline__ void wave_blocks(WaveAcc<D>& acc, const u32x4* qf, const uint8_t* kcache,
-                                            const uint8_t* vcache, const int* bt, int b, int step, int blk1,
-                                            int lo, int ctx, size_t head_stride, const DecodeArgs& a, int c16,
-                                            int q4) {
-  auto run = [&](const PairRegs<CK, D>& r, size_t p0, size_t p1, int bb) {
+                                            const uint8_t* vcache, const int* bt, int b, int blk1, int lo,
+                                            int ctx, size_t head_stride, const DecodeArgs& a, int c16, int q4) {
+  const int np = (blk1 - b + 1) >> 1;
+  if (np <= 0) return;
+  // block ids are uniform over the wave and read-only here: scalar loads
+  // through the constant address space (a vector load would make the
+  // compiler wait for every outstanding K/V load before using the id)
+  typedef __attribute__((address_space(4))) const int cint;
+  const cint* btc = (const cint*)(bt);
+  auto ids = [&](int n, size_t& p0, size_t& p1) {
+    const int bb = b + 2 * n;
+    p0 = (size_t)btc[bb];
+    p1 = (bb + 1 < blk1) ? (size_t)btc[bb + 1] : p0;
+  };
+  auto run = [&](const PairRegs<CK, D>& r, size_t p0, size_t p1, int n) {
+    const int bb = b + 2 * n;
     if (bb * 16 < lo || bb * 16 + 32 > ctx) pair_step<CK, D, true>(acc, r, qf, p0, p1, bb, lo, ctx, a, c16, q4);
     else pair_step<CK, D, false>(acc, r, qf, p0, p1, bb, lo, ctx, a, c16, q4);
   };
+  auto run_interior = [&](const PairRegs<CK, D>& r, size_t p0, size_t p1, int n) {
+    pair_step<CK, D, false>(acc, r, qf, p0, p1, b + 2 * n, lo, ctx, a, c16, q4);
+  };
   PairRegs<CK, D> ra, rb;
-  size_t a0 = 0, a1 = 0, b0 = 0, b1 = 0;
-  if (b < blk1) {
-    a0 = (size_t)bt[b];
-    a1 = (b + 1 < blk1) ? (size_t)bt[b + 1] : a0;
-    load_pair<CK, D>(ra, kcache, vcache, a0, a1, head_stride, c16, q4);
+  size_t a0, a1, b0 = 0, b1 = 0;
+  ids(0, a0, a1);
+  load_pair<CK, D>(ra, kcache, vcache, a0, a1, head_stride, c16, q4);
+  if (np >= 2) {
+    ids(1, b0, b1);
+    load_pair<CK, D>(rb, kcache, vcache, b0, b1, head_stride, c16, q4);
   }
-  while (b < blk1) {
-    const int bn = b + step;
-    if (bn < blk1) {
-      b0 = (size_t)bt[bn];
-      b1 = (bn + 1 < blk1) ? (size_t)bt[bn + 1] : b0;
-      load_pair<CK, D>(rb, kcache, vcache, b0, b1, head_stride, c16, q4);
-    }
-    run(ra, a0, a1, b);
-    if (bn >= blk1) break;
-    const int bnn = bn + step;
-    if (bnn < blk1) {
-      a0 = (size_t)bt[bnn];
-      a1 = (bnn + 1 < blk1) ? (size_t)bt[bnn + 1] : a0;
+  run(ra, a0, a1, 0);
+  int n = 1;  // rb holds pair n
+  for (; n + 2 < np; n += 2) {  // pairs n and n + 1 are interior, n + 2 exists
+    ids(n + 1, a0, a1);
+    load_pair<CK, D>(ra, kcache, vcache, a0, a1, head_stride, c16, q4);
+    run_interior(rb, b0, b1, n);
+    ids(n + 2, b0, b1);
+    load_pair<CK, D>(rb, kcache, vcache, b0, b1, head_stride, c16, q4);
+    run_interior(ra, a0, a1, n + 1);
+  }
+  if (n < np) {
+    if (n + 1 < np) {
+      ids(n + 1, a0, a1);
       load_pair<CK, D>(ra, kcache, vcache, a0, a1, head_stride, c16, q4);
     }
-    run(rb, b0, b1, bn);
-    b = bnn;
+    run(rb, b0, b1, n);
+    if (n + 1 < np) run(ra, a0, a1, n + 1);
   }
 }
 
@@ -485,10 +508,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const size_t head_stride = (size_t)H * S::TILE;
   long long x = (long long)w * C;
   while (x < x_end) {
-    // stream containing block-head x: last i with psum[i]*H <= x
-    const int i = last_le(psum, nstreams, x, H);
-    const int nb = psum[i + 1] - psum[i];
-    const long long base = (long long)psum[i] * H;
+    // stream containing block-head x: last i with psum[i]*H <= x (uniform)
+    const int i = __builtin_amdgcn_readfirstlane(last_le(psum, nstreams, x, H));
+    const int nb = __builtin_amdgcn_readfirstlane(psum[i + 1] - psum[i]);
+    const long long base = (long long)__builtin_amdgcn_readfirstlane(psum[i]) * H;
     const int g = (int)((x - base) / nb);
     const long long sstart = base + (long long)g * nb;  // this stream's first block-head
     const long long seg_end = min(x_end, sstart + nb);
@@ -510,8 +533,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int blk1 = (lo >> 4) + (int)(seg_end - sstart);
       const int kend = min(ctx, blk1 * 16);
       load_query<CK, D>(qf, a, qrow, g, G, c16, q4, G);
-      wave_blocks<CK, D>(acc, qf, kcache, vcache, a.block_table + (size_t)s * a.bt_stride, blk0, 2, blk1, lo,
-                         kend, head_stride, a, c16, q4);
+      wave_blocks<CK, D>(acc, qf, kcache, vcache, a.block_table + (size_t)s * a.bt_stride, blk0, blk1, lo, kend,
+                         head_stride, a, c16, q4);
       const bool single = !grouped && (sstart / C) == ((sstart + nb - 1) / C);
       wave_write<D>(acc, a, slot, qrow, g, G, single, c16, q4, G);
     } else {
@@ -527,7 +550,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int blk0 = (int)(x - sstart);
       const int blk1 = (int)(seg_end - sstart);
       load_query<CK, D>(qf, a, m0, g, G, c16, q4, nmem * G);
-      wave_blocks<CK, D>(acc, qf, kcache, vcache, a.block_table + (size_t)first * a.bt_stride, blk0, 2, blk1, 0,
+      wave_blocks<CK, D>(acc, qf, kcache, vcache, a.block_table + (size_t)first * a.bt_stride, blk0, blk1, 0,
                          blk1 * 16, head_stride, a, c16, q4);
       wave_write<D>(acc, a, slot, 0, g, G, false, c16, q4, nmem * G);
     }
