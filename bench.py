@@ -207,6 +207,38 @@ def stored_traffic(profile="decode_mfma_split_llama8b_decode.md", files=DECODE_S
     return int(t["fetch_bytes_per_launch"]) + int(t["write_bytes_per_launch"])
 
 
+def measure_ceilings(torch):
+    """Achievable peaks on this GPU, measured with libpa_peaks next to the
+    path: HBM read rate of a paged gather (random 4 KiB tiles, one wave per
+    tile, 16-byte nontemporal loads; contiguous 1 KiB per instruction, and the
+    decode kernel's key pattern of 64 bytes from each of 16 rows) and the
+    back-to-back 32x32x16 bf16 / fp16 MFMA rate."""
+    from paged_kv_cache_103_amd import peaks
+
+    res = {}
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(0)
+    ids = torch.randperm(nbytes // 4096, generator=g).to(torch.int32).cuda()
+    sink = torch.empty(256 * 2048, dtype=torch.float32, device="cuda")
+    for mode, name in ((0, "hbm_tiles_contiguous_gbs"), (1, "hbm_tiles_decode_pattern_gbs")):
+        f = lambda: peaks.read_tiles(buf, ids, mode, 4096, sink)
+        _, ms, _ = time_steps(torch, lambda: None, f, 5, 2)
+        res[name] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del buf, ids
+    torch.cuda.empty_cache()
+    for kind, name in ((0, "mfma_bf16_tflops"), (1, "mfma_fp16_tflops")):
+        flops = [0.0]
+
+        def f():
+            flops[0] = peaks.mfma(kind, 2000, 2048, sink)
+
+        _, ms, _ = time_steps(torch, lambda: None, f, 5, 2)
+        res[name] = round(flops[0] / (ms * 1e-3) / 1e12, 1)
+    return res
+
+
 def chunk_of(mb):
     """The mixed step's last sequence (the 2048-token chunk on its 65,536-token
     prefix) as a batch of its own, sharing the mixed step's device buffers."""
@@ -249,6 +281,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--extra", action="store_true", help="also time the other named configurations (stderr)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the achievable-peak probes")
     ap.add_argument("--profile-pass", action="store_true",
                     help="only the kernels a counter run needs: a plain 1 GiB device copy (the "
                          "calibration kernel for FETCH_SIZE/WRITE_SIZE), a few decode and mixed steps, "
@@ -331,6 +364,9 @@ def main():
         del eb
         torch.cuda.empty_cache()
 
+    ceil = None if args.no_ceilings else measure_ceilings(torch)
+    if ceil:
+        log(f"measured ceilings: {ceil}")
     achieved = dec["kv_gbs_attend"]
     line = {
         "metric": METRIC,
@@ -352,7 +388,13 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "pa_decode call: decode_mfma_split + decode_split_merge",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(),
-                     "algorithmic_bytes_per_launch": dec["kv_bytes"]},
+                     "algorithmic_bytes_per_launch": dec["kv_bytes"],
+                     "measured_ceiling": None if not ceil else {
+                         "value": ceil["hbm_tiles_contiguous_gbs"], "unit": "GB/s",
+                         "frac": round(achieved / ceil["hbm_tiles_contiguous_gbs"], 4),
+                         "probe": "libpa_peaks: random 4 KiB tiles, a wave per tile, 16-byte nontemporal "
+                                  "loads, 1 KiB contiguous per instruction",
+                         "decode_key_pattern_gbs": ceil["hbm_tiles_decode_pattern_gbs"]}},
         "cpu_baseline": cpu,
         "mixed_step": {"value": round(mix["tokens_per_s"], 1), "unit": "tokens/s",
                        "ms_per_step": round(mix["step_ms"], 5),
@@ -365,7 +407,13 @@ def main():
                                             "unit": "TFLOP/s", "frac": round(pre_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                                             "traffic": stored_traffic("prefill_bf16_kernel_2048_chunk.md",
                                                                       PREFILL_SOURCES),
-                                            "algorithmic_flops_per_launch": flops}},
+                                            "algorithmic_flops_per_launch": flops,
+                                            "measured_ceiling": None if not ceil else {
+                                                "value": ceil["mfma_bf16_tflops"], "unit": "TFLOP/s",
+                                                "frac": round(pre_tflops / ceil["mfma_bf16_tflops"], 4),
+                                                "probe": "libpa_peaks: back-to-back independent 32x32x16 "
+                                                         "bf16 MFMAs, 8 waves per CU",
+                                                "fp16_tflops": ceil["mfma_fp16_tflops"]}}},
     }
     if extra:
         line["extra"] = extra

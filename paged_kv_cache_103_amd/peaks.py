@@ -1,0 +1,52 @@
+"""ctypes binding of libpa_peaks (include/pa_peaks.h): argument marshalling
+for the achievable-peak probes bench.py runs beside the attention path."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import _lib
+
+PEAKS_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpa_peaks.so")
+EXPORTED = ("pa_peak_read_tiles", "pa_peak_mfma")
+
+_L = None
+
+
+def load() -> ctypes.CDLL:
+    global _L
+    if _L is None:
+        if not os.path.exists(PEAKS_PATH):
+            raise RuntimeError(f"{PEAKS_PATH} is not built: run `python -m paged_kv_cache_103_amd.build`")
+        L = ctypes.CDLL(PEAKS_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        L.pa_peak_read_tiles.restype = i32
+        L.pa_peak_read_tiles.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+        L.pa_peak_mfma.restype = i32
+        L.pa_peak_mfma.argtypes = [i32, i32, i32, vp, vp]
+        _L = L
+    return _L
+
+
+def read_tiles(buf: torch.Tensor, tile_ids: torch.Tensor, mode: int, grid_blocks: int, sink: torch.Tensor) -> None:
+    """Gather the 4 KiB tiles tile_ids (int32) of buf; mode 0 contiguous 1 KiB
+    loads, 1 the decode kernel's key pattern."""
+    assert tile_ids.dtype == torch.int32
+    assert buf.numel() * buf.element_size() >= 4096 * (int(tile_ids.max()) + 1)
+    assert sink.numel() * sink.element_size() >= 4 * grid_blocks
+    st = load().pa_peak_read_tiles(buf.data_ptr(), tile_ids.data_ptr(), tile_ids.numel(), mode, grid_blocks,
+                                   sink.data_ptr(), _lib._stream(None))
+    if st != 0:
+        raise RuntimeError(f"pa_peak_read_tiles launch failed (HIP error {st})")
+
+
+def mfma(kind: int, iters: int, grid_blocks: int, sink: torch.Tensor) -> float:
+    """Back-to-back 32x32x16 MFMAs (kind 0 bf16, 1 fp16); returns the flops enqueued."""
+    assert sink.numel() * sink.element_size() >= 4 * 256 * grid_blocks
+    st = load().pa_peak_mfma(kind, iters, grid_blocks, sink.data_ptr(), _lib._stream(None))
+    if st != 0:
+        raise RuntimeError(f"pa_peak_mfma launch failed (HIP error {st})")
+    return 4.0 * 32768 * iters * grid_blocks * 4

@@ -494,3 +494,20 @@ def test_fp8_all_codes_decode_exactly():
     ref_bf16 = torch.from_numpy(ref).to(torch.bfloat16).to(torch.float64).numpy()
     for s in range(S):
         assert np.array_equal(got[s, :, :], np.broadcast_to(ref_bf16[s], (8, D)))
+
+
+def test_peak_probes_run():
+    """The achievable-peak probes bench.py reports beside the path launch and
+    write their sinks (a small gather and a short MFMA loop)."""
+    from paged_kv_cache_103_amd import peaks
+
+    buf = torch.ones(64 * 4096, dtype=torch.uint8, device=DEV)
+    ids = torch.randperm(64, device="cpu").to(torch.int32).to(DEV)
+    sink = torch.full((256 * 8,), -1.0, dtype=torch.float32, device=DEV)
+    for mode in (0, 1):
+        peaks.read_tiles(buf, ids, mode, 8, sink)
+    flops = peaks.mfma(0, 10, 8, sink)
+    peaks.mfma(1, 10, 8, sink)
+    torch.cuda.synchronize()
+    assert flops == 4.0 * 32768 * 10 * 8 * 4
+    assert torch.isfinite(sink).all()
