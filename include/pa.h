@@ -80,7 +80,8 @@ typedef enum {
   PA_ERR_INVALID_ARGUMENT = 1,   /* bad size, null pointer, inconsistent sizes */
   PA_ERR_UNSUPPORTED = 2,        /* valid request this build has no kernel for */
   PA_ERR_WORKSPACE_TOO_SMALL = 3,
-  PA_ERR_HIP = 4                 /* a HIP runtime call or launch failed */
+  PA_ERR_HIP = 4,                /* a HIP runtime call or launch failed */
+  PA_ERR_OUT_OF_BLOCKS = 5       /* block manager: too few free blocks (pa_blocks.h) */
 } pa_status;
 
 typedef enum {

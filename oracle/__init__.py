@@ -15,6 +15,9 @@ paging     block arithmetic and the KV write (``reshape_and_cache``): slot =
            physical block * block_size + offset, byte-exact scatter.
 attention  gather through the block table and exact softmax attention with
            causal / sliding-window masks; partial-softmax merge.
+blocks     plain model of the block manager's policy (refcounts, prefix reuse
+           over full blocks, LRU free queue, fork and copy-on-write), imported
+           on its own as ``oracle.blocks``.
 
 Every function names the page passage it follows in its docstring. Pins
 (page facts, closed forms, brute force) live in ``tests/test_oracle_*.py``.

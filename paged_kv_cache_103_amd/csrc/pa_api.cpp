@@ -3,6 +3,7 @@
 // arguments that can be checked on the host, sizes the split-K plan from host
 // scalars (never reading device memory), and enqueues the kernels.
 #include "pa.h"
+#include "pa_blocks.h"
 
 #include <hip/hip_runtime.h>
 
@@ -419,6 +420,32 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
   return PA_OK;
 }
 
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale, const int32_t* pairs,
+                         int32_t num_pairs, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_size, pa_dtype cache_dtype, pa_stream_t stream) {
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_pairs must be >= 0 (got %d)", num_pairs);
+  if (block_size != PA_BLOCK_SIZE)
+    return fail(PA_ERR_UNSUPPORTED, "block_size must be %d (got %d)", PA_BLOCK_SIZE, block_size);
+  if (head_size != 64 && head_size != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_size must be 64 or 128 (got %d)", head_size);
+  if (num_kv_heads < 1 || num_blocks < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_kv_heads and num_blocks must be >= 1 (got %d, %d)", num_kv_heads,
+                num_blocks);
+  if (!known_dtype(cache_dtype)) return fail(PA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)cache_dtype);
+  if (num_pairs == 0) {
+    g_last_error.clear();
+    return PA_OK;
+  }
+  if (!k_cache || !v_cache || !pairs) return fail(PA_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale))
+    return fail(PA_ERR_INVALID_ARGUMENT, "fp8 cache needs k_scale and v_scale");
+  const size_t tile = (size_t)PA_BLOCK_SIZE * head_size * elem_bytes(cache_dtype);
+  hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, cache_dtype == PA_FP8_E4M3 ? k_scale : nullptr,
+                                        cache_dtype == PA_FP8_E4M3 ? v_scale : nullptr, pairs, num_pairs, tile,
+                                        num_kv_heads, num_blocks, (hipStream_t)stream);
+  return hip_status(e, "copy_blocks launch");
+}
+
 const char* pa_status_string(pa_status s) {
   switch (s) {
     case PA_OK: return "PA_OK";
@@ -426,12 +453,22 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
     case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
     case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_OUT_OF_BLOCKS: return "PA_ERR_OUT_OF_BLOCKS";
   }
   return "PA_ERR_UNKNOWN";
 }
 
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
+
 int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
 
 }  // extern "C"
+
+namespace pa {
+pa_status set_error(pa_status st, const char* msg) {
+  if (st == PA_OK) g_last_error.clear();
+  else g_last_error = msg;
+  return st;
+}
+}  // namespace pa

@@ -6,7 +6,16 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
+
+// Sets (or, for PA_OK, clears) the thread's pa_last_error() text; returns st.
+pa_status set_error(pa_status st, const char* msg);
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale, const int32_t* pairs,
+                              int num_pairs, size_t tile_bytes, int num_kv_heads, int num_blocks,
+                              hipStream_t stream);
 
 // e4m3fn saturation before the hardware conversion: finite values are clamped
 // to +-448, NaN stays NaN.
