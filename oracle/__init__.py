@@ -14,7 +14,8 @@ formats    exact decoding of stored element bits (fp32, bf16, OCP e4m3fn) to
 paging     block arithmetic and the KV write (``reshape_and_cache``): slot =
            physical block * block_size + offset, byte-exact scatter.
 attention  gather through the block table and exact softmax attention with
-           causal / sliding-window masks; partial-softmax merge.
+           causal / sliding-window masks; sparse decode over chosen blocks;
+           partial-softmax merge.
 blocks     plain model of the block manager's policy (refcounts, prefix reuse
            over full blocks, LRU free queue, fork and copy-on-write), imported
            on its own as ``oracle.blocks``.
@@ -39,6 +40,8 @@ from .attention import (  # noqa: F401
     gather_kv,
     paged_attention,
     attend_sequence,
+    attend_selected_blocks,
+    selected_positions,
     partial_softmax,
     merge_partials,
 )

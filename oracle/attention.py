@@ -117,6 +117,53 @@ def paged_attention(query, q_dtype: str, k_pool, v_pool, cache_dtype: str, k_sca
     return out
 
 
+def selected_positions(ctx: int, selected, block_size: int = 16) -> np.ndarray:
+    """Key positions a sparse decode query reads: every position < ctx inside
+    the chosen logical blocks, in ascending order.
+
+    Sparse attention looks only at the top-k positions an indexer picks out
+    of the history ("宣稱省下 106 倍成本…", "下：DeepSeek V4 的挑戰與 PCP/DEP 方案",
+    "背景：什麼是稀疏注意力"); the candidates here are whole blocks (reading).
+    Readings: an entry outside [0, newest block) is ignored, order and
+    repeats do not matter, and the block holding the newest token is always
+    read, so the query always sees itself.
+    """
+    nbk = -(-ctx // block_size)
+    keep = {int(e) for e in np.asarray(selected, dtype=np.int64).ravel() if 0 <= int(e) < nbk - 1}
+    keep.add(nbk - 1)
+    pos = [b * block_size + o for b in sorted(keep) for o in range(block_size) if b * block_size + o < ctx]
+    return np.asarray(pos, dtype=np.int64)
+
+
+def attend_selected_blocks(q_f64, k_pool, v_pool, cache_dtype: str, k_scale, v_scale,
+                           block_table_row, ctx: int, selected, num_kv_heads: int, scale: float,
+                           block_size: int = 16):
+    """Sparse decode of one sequence, float64: the query of its newest token
+    (position ctx - 1, q_f64 [1][Hq][D]) attends to the keys at
+    ``selected_positions(ctx, selected)`` only, with the same softmax as
+    ``attend_sequence`` (all of them precede the query, so none is masked).
+    The selection is one list for the whole sequence, shared by every head:
+    the indexer hands over one global top-k list ("三個讓 TP 更不划算的原因",
+    second reason), and fetching the chosen entries is the work that stays
+    ("真正貴的部分…", third reason; the DeepSeek-V4.1 write-up,
+    "三、第二招：把能合的内核全合成一个", sparse MQA logits: only candidates
+    are scored, so the cost stops growing with the context).
+    """
+    assert q_f64.shape[0] == 1 and ctx >= 1
+    Hq = q_f64.shape[1]
+    G = Hq // num_kv_heads
+    k_pos = selected_positions(ctx, selected, block_size)
+    out = np.full(q_f64.shape, np.nan)
+    for g in range(num_kv_heads):
+        K, V = gather_kv(k_pool, v_pool, cache_dtype, k_scale, v_scale, block_table_row, g, k_pos,
+                         block_size)
+        for h in range(g * G, (g + 1) * G):
+            s = scale * (K @ q_f64[0, h, :])
+            p = np.exp(s - s.max())
+            out[0, h, :] = (p @ V) / p.sum()
+    return out
+
+
 def partial_softmax(scores, values):
     """Summary of one key range: (m, l, o) = (max s, sum e^(s-m), sum e^(s-m) v).
 

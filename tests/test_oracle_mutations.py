@@ -142,3 +142,66 @@ def test_slot_math_mistake_is_caught(monkeypatch, golden):
     monkeypatch.undo()
     monkeypatch.setattr(oracle, "blocks_needed", lambda n, B=16: n // B)
     _expect_failure(TP.test_allocate_slots, golden)
+
+
+# ---------------------------------------------------------------------------
+# sparse decode over chosen blocks
+# ---------------------------------------------------------------------------
+from tests import test_oracle_sparse as TS  # noqa: E402
+
+SPARSE_CASES = [
+    (17, [0, 2], 4, 2),
+    (23, [5, 1, 1, 9, -3], 2, 1),
+    (40, [], 4, 4),
+    (8, [0, 1], 3, 1),
+]
+
+
+def _sparse_pins_fail():
+    failures = 0
+    for case in SPARSE_CASES:
+        try:
+            TS.test_sparse_matches_brute_force(*case)
+        except AssertionError:
+            failures += 1
+    for fn in (TS.test_nothing_chosen_with_one_token_in_the_newest_block_returns_its_v,
+               TS.test_every_block_chosen_is_dense_decode):
+        try:
+            fn()
+        except (AssertionError, IndexError, ValueError):
+            failures += 1
+    assert failures > 0, "the planted mistake passed every sparse pin"
+
+
+def _positions(keep, ctx, B):
+    return np.asarray([b * B + o for b in sorted(keep) for o in range(B) if b * B + o < ctx], dtype=np.int64)
+
+
+def test_sparse_without_the_newest_block_is_caught(monkeypatch):
+    def mutant(ctx, selected, block_size=16):
+        nbk = -(-ctx // block_size)
+        keep = {int(e) for e in np.asarray(selected).ravel() if 0 <= int(e) < nbk}
+        return _positions(keep or {nbk - 1}, ctx, block_size)
+
+    monkeypatch.setattr(A, "selected_positions", mutant)
+    _sparse_pins_fail()
+
+
+def test_sparse_reading_past_the_context_is_caught(monkeypatch):
+    def mutant(ctx, selected, block_size=16):
+        nbk = -(-ctx // block_size)
+        keep = {int(e) for e in np.asarray(selected).ravel() if 0 <= int(e) < nbk - 1} | {nbk - 1}
+        return np.asarray([b * block_size + o for b in sorted(keep) for o in range(block_size)], dtype=np.int64)
+
+    monkeypatch.setattr(A, "selected_positions", mutant)
+    _sparse_pins_fail()
+
+
+def test_sparse_newest_block_off_by_one_is_caught(monkeypatch):
+    def mutant(ctx, selected, block_size=16):
+        nbk = ctx // block_size  # should round up
+        keep = {int(e) for e in np.asarray(selected).ravel() if 0 <= int(e) < nbk - 1} | {max(nbk - 1, 0)}
+        return _positions(keep, ctx, block_size)
+
+    monkeypatch.setattr(A, "selected_positions", mutant)
+    _sparse_pins_fail()
