@@ -177,6 +177,42 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_ca
                                   pa_stream_t stream);
 
 /*
+ * Sparse decode: the newest token of each sequence attends only to the keys
+ * of a chosen set of its logical blocks. Sparse attention looks at the top-k
+ * history positions an indexer picks instead of all of them; the indexer
+ * hands over one list per sequence for every head, and the work that remains
+ * is fetching the chosen entries ("宣稱省下 106 倍成本…", "下：DeepSeek V4 的
+ * 挑戰與 PCP/DEP 方案": "背景：什麼是稀疏注意力" and the three reasons that
+ * follow), so the bytes read stop growing with the context (DeepSeek-V4.1
+ * write-up, "三、第二招：把能合的内核全合成一个", sparse MQA logits). Candidates
+ * here are whole 16-token blocks.
+ * selected_blocks: int32 [num_seqs][selected_stride], device: logical block
+ *   ids (position / 16) chosen for sequence s; its first num_selected[s]
+ *   entries (clamped to [0, max_selected]) are read. Entries outside
+ *   [0, newest block) are ignored, order and repeats do not matter, and the
+ *   newest block (holding position context_lens[s] - 1) is always read, so
+ *   the query always sees itself. Keys at positions >= context_lens[s] are
+ *   never read.
+ * num_selected: int32 [num_seqs], device. Both may be NULL when
+ *   max_selected == 0 (every sequence reads its newest block only).
+ * max_selected: host scalar in [0, 2^22]; selected_stride >= max_selected.
+ * The result is pa_decode's over exactly those keys; choosing every block
+ *   gives pa_decode's result. Other arguments and layouts are pa_decode's
+ *   (no sliding window); max_context_len up to 8,257,536 (PA_ERR_UNSUPPORTED
+ *   beyond: the block bitmap lives in 64 KiB of LDS). The workspace must
+ *   hold pa_decode_sparse_workspace_bytes(...) bytes: it keeps the compacted
+ *   block table ([num_seqs][max_selected + 1] int32) the decode then reads.
+ */
+pa_status pa_decode_sparse(void* out, const void* query, const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale, const int32_t* block_table,
+                           int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                           int32_t max_context_len, const int32_t* selected_blocks, int32_t selected_stride,
+                           const int32_t* num_selected, int32_t max_selected, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_size, int32_t block_size, int32_t num_blocks,
+                           pa_dtype q_dtype, pa_dtype cache_dtype, float scale, void* workspace,
+                           size_t workspace_bytes, pa_stream_t stream);
+
+/*
  * Causal attention for a flattened variable-length batch.
  * Sequence s owns query rows cu_seqlens[s] .. cu_seqlens[s+1]-1 (int32
  * [num_seqs+1]); context_lens[s] counts its cached tokens including this
@@ -208,6 +244,11 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len, int3
 size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_groups, int32_t max_context_len,
                                                int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
                                                pa_dtype cache_dtype, int32_t sliding_window);
+
+/* Workspace bytes pa_decode_sparse needs for these sizes (0 if arguments are
+ * out of range). */
+size_t pa_decode_sparse_workspace_bytes(int32_t num_seqs, int32_t max_selected, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_size, pa_dtype cache_dtype);
 
 /* Workspace bytes pa_prefill_chunk needs for these sizes (0 if none; the
  * one-token rows of a mixed batch use the decode plan). */

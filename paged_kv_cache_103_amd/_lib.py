@@ -34,9 +34,11 @@ EXPORTED = (
     "pa_reshape_and_cache",
     "pa_decode",
     "pa_decode_shared_prefix",
+    "pa_decode_sparse",
     "pa_prefill_chunk",
     "pa_decode_workspace_bytes",
     "pa_decode_shared_prefix_workspace_bytes",
+    "pa_decode_sparse_workspace_bytes",
     "pa_prefill_workspace_bytes",
     "pa_status_string",
     "pa_last_error",
@@ -74,6 +76,11 @@ def load() -> ctypes.CDLL:
                                           vp, sz, vp]
     L.pa_decode_shared_prefix_workspace_bytes.restype = sz
     L.pa_decode_shared_prefix_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
+    L.pa_decode_sparse.restype = ctypes.c_int
+    L.pa_decode_sparse.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i32, vp, i32, i32, vp, i32, vp, i32, i32, i32,
+                                   i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, sz, vp]
+    L.pa_decode_sparse_workspace_bytes.restype = sz
+    L.pa_decode_sparse_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
     L.pa_prefill_chunk.restype = ctypes.c_int
     L.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                    i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_float, i32,
@@ -218,6 +225,36 @@ def decode_shared_prefix(out: torch.Tensor, query: torch.Tensor, k_cache: torch.
                                           _ptr(group_prefix_len), NGr, Hq, Hkv, D, k_cache.shape[2], NB,
                                           dtype_code(query.dtype), dtype_code(k_cache.dtype), float(scale),
                                           int(sliding_window), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def decode_sparse_workspace_bytes(num_seqs: int, max_selected: int, num_heads: int, num_kv_heads: int,
+                                  head_size: int, cache_dtype="bf16") -> int:
+    """Bytes of device workspace pa_decode_sparse needs."""
+    return int(load().pa_decode_sparse_workspace_bytes(num_seqs, max_selected, num_heads, num_kv_heads, head_size,
+                                                       _cache_code(cache_dtype)))
+
+
+def decode_sparse(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  block_table: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                  selected_blocks: torch.Tensor, num_selected: torch.Tensor, scale: float,
+                  k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """pa_decode_sparse: pa_decode over the keys of chosen logical blocks only;
+    selected_blocks int32 [S][max_selected], num_selected int32 [S]."""
+    S, Hq, D = query.shape
+    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
+    assert selected_blocks.dtype == torch.int32 and selected_blocks.dim() == 2
+    assert num_selected.dtype == torch.int32 and num_selected.numel() == S
+    assert selected_blocks.shape[1] == 0 or selected_blocks.stride(1) == 1
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ms = selected_blocks.shape[1]
+    _check(load().pa_decode_sparse(_ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                   _ptr(v_scale), _ptr(block_table), block_table.shape[1], _ptr(context_lens), S,
+                                   int(max_context_len), _ptr(selected_blocks) if ms else None,
+                                   selected_blocks.stride(0) if ms else 0, _ptr(num_selected) if ms else None, ms,
+                                   Hq, Hkv, D, k_cache.shape[2], NB, dtype_code(query.dtype),
+                                   dtype_code(k_cache.dtype), float(scale), _ptr(workspace), ws_bytes,
+                                   _stream(stream)))
 
 
 def prefill_chunk(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -325,6 +325,96 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_ca
   return hip_status(e, "shared-prefix decode launch");
 }
 
+static size_t sparse_table_bytes(int32_t num_seqs, int32_t max_selected) {
+  return align256((size_t)num_seqs * (size_t)(max_selected + 1) * sizeof(int)) +
+         align256((size_t)num_seqs * sizeof(int));
+}
+
+size_t pa_decode_sparse_workspace_bytes(int32_t num_seqs, int32_t max_selected, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_size, pa_dtype cache_dtype) {
+  if (num_seqs <= 0 || max_selected < 0 || max_selected > pa::kSparseMaxSelected || num_heads <= 0 ||
+      num_kv_heads <= 0 || head_size <= 0)
+    return 0;
+  return sparse_table_bytes(num_seqs, max_selected) +
+         pa_decode_workspace_bytes(num_seqs, 16 * (max_selected + 1), num_heads, num_kv_heads, head_size,
+                                   cache_dtype, 0);
+}
+
+pa_status pa_decode_sparse(void* out, const void* query, const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale, const int32_t* block_table,
+                           int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                           int32_t max_context_len, const int32_t* selected_blocks, int32_t selected_stride,
+                           const int32_t* num_selected, int32_t max_selected, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_size, int32_t block_size, int32_t num_blocks,
+                           pa_dtype q_dtype, pa_dtype cache_dtype, float scale, void* workspace,
+                           size_t workspace_bytes, pa_stream_t stream) {
+  if (max_selected < 0 || max_selected > pa::kSparseMaxSelected)
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_selected must be in [0, %d] (got %d)", pa::kSparseMaxSelected,
+                max_selected);
+  if (max_selected > 0 && (!selected_blocks || !num_selected))
+    return fail(PA_ERR_INVALID_ARGUMENT, "null device pointer (selected_blocks / num_selected)");
+  if (max_selected > 0 && selected_stride < max_selected)
+    return fail(PA_ERR_INVALID_ARGUMENT, "selected_stride (%d) is smaller than max_selected (%d)",
+                selected_stride, max_selected);
+  pa_status st = check_attention_common(out, query, k_cache, v_cache, k_scale, v_scale, block_table,
+                                        block_table_stride, context_lens, num_seqs, max_context_len,
+                                        num_heads, num_kv_heads, head_size, block_size, num_blocks,
+                                        q_dtype, cache_dtype, scale, 0);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) {
+    g_last_error.clear();
+    return PA_OK;
+  }
+  if (pa::sparse_select_lds_bytes(max_context_len) > pa::kSparseMaxLds)
+    return fail(PA_ERR_UNSUPPORTED, "max_context_len %d is beyond the sparse decode's block bitmap",
+                max_context_len);
+  const size_t need = pa_decode_sparse_workspace_bytes(num_seqs, max_selected, num_heads, num_kv_heads, head_size,
+                                                       cache_dtype);
+  if (workspace_bytes < need || workspace == nullptr)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "sparse decode needs %zu workspace bytes (got %zu)", need,
+                workspace_bytes);
+  char* ws = static_cast<char*>(workspace);
+  pa::SparseSelectArgs sa{};
+  sa.block_table = block_table;
+  sa.bt_stride = block_table_stride;
+  sa.context_lens = context_lens;
+  sa.selected = selected_blocks;
+  sa.sel_stride = selected_stride;
+  sa.num_selected = max_selected > 0 ? num_selected : nullptr;
+  sa.max_selected = max_selected;
+  sa.blocks_max = (max_context_len + 15) / 16;
+  sa.words_max = (sa.blocks_max + 31) / 32;
+  sa.cbt = reinterpret_cast<int*>(ws);
+  sa.cbt_stride = max_selected + 1;
+  sa.eff_ctx = reinterpret_cast<int*>(ws + align256((size_t)num_seqs * (size_t)(max_selected + 1) * sizeof(int)));
+  hipError_t e = pa::launch_sparse_select(sa, num_seqs, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "sparse block selection launch");
+
+  const int32_t eff_max = 16 * (max_selected + 1);
+  const pa::DecodePlan plan = make_plan(num_seqs, eff_max, num_heads, num_kv_heads, head_size, cache_dtype, 0);
+  const size_t dec_need = pa::decode_workspace_bytes(plan, num_seqs, num_heads, num_kv_heads, head_size);
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.query = query;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = sa.cbt;
+  a.context_lens = sa.eff_ctx;
+  a.cu_seqlens = nullptr;
+  bind_workspace(a, plan, dec_need ? ws + sparse_table_bytes(num_seqs, max_selected) : nullptr, num_seqs,
+                 num_heads, num_kv_heads, head_size);
+  a.bt_stride = sa.cbt_stride;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.window = 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  e = pa::launch_decode(a, (int)q_dtype, (int)cache_dtype, head_size, (hipStream_t)stream);
+  return hip_status(e, "sparse decode launch");
+}
+
 pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, const void* v_cache,
                            const float* k_scale, const float* v_scale, const int32_t* block_table,
                            int32_t block_table_stride, const int32_t* cu_seqlens,

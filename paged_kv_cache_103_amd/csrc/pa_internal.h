@@ -90,6 +90,27 @@ hipError_t launch_decode(const DecodeArgs& args, int q_kind, int cache_kind, int
                          hipStream_t stream);
 bool decode_supported(int q_kind, int cache_kind, int head_size, int group);
 
+// Sparse decode: compaction of each sequence's chosen blocks into a block
+// table of its own (cbt [num_seqs][cbt_stride]) and key counts (eff_ctx).
+struct SparseSelectArgs {
+  const int* block_table;
+  int bt_stride;
+  const int* context_lens;
+  const int* selected;      // [num_seqs][sel_stride] logical block ids
+  int sel_stride;
+  const int* num_selected;  // [num_seqs]; null when max_selected == 0
+  int max_selected;
+  int blocks_max;           // ceil(max_context_len / 16)
+  int words_max;            // ceil(blocks_max / 32): bitmap words in LDS
+  int* cbt;
+  int cbt_stride;           // max_selected + 1
+  int* eff_ctx;
+};
+constexpr int kSparseMaxSelected = 1 << 22;
+constexpr size_t kSparseMaxLds = 64 * 1024;  // bitmap + scan: contexts up to 8,257,536 tokens
+size_t sparse_select_lds_bytes(int max_context_len);
+hipError_t launch_sparse_select(const SparseSelectArgs& a, int num_seqs, hipStream_t stream);
+
 struct PrefillArgs {
   void* out;
   const void* query;

@@ -1,0 +1,78 @@
+// Sparse decode, first kernel (pa_decode_sparse, include/pa.h): turns each
+// sequence's list of chosen logical blocks into a compact block table of the
+// physical blocks it will read, in ascending logical order, with the newest
+// block always last, and the number of keys that leaves. The decode kernels
+// then run on that table unchanged: positions are already encoded in Q and K,
+// so only which keys are read matters, and every chosen key precedes the
+// query. Sparse attention reads only the top-k positions an indexer picks
+// ("宣稱省下 106 倍成本…", "背景：什麼是稀疏注意力"), so the bytes read stop growing
+// with the context (DeepSeek-V4.1 write-up, "三、第二招：把能合的内核全合成一个",
+// sparse MQA logits).
+//
+// One workgroup per sequence. The chosen entries set bits of a per-sequence
+// bitmap of its logical blocks in LDS (so order and repeats do not matter,
+// and entries outside [0, newest block) are dropped); the set bits are then
+// compacted in ascending order by a workgroup scan of per-word popcounts.
+#include <hip/hip_runtime.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+__global__ __launch_bounds__(256) void sparse_select_kernel(SparseSelectArgs a) {
+  extern __shared__ unsigned int lds_bits[];
+  int* scan = reinterpret_cast<int*>(lds_bits + a.words_max);
+  const int s = blockIdx.x, tid = threadIdx.x;
+  const int ctx = a.context_lens[s];
+  const int nbk = min(ctx > 0 ? (ctx + 15) >> 4 : 0, a.blocks_max);
+  const int W = (nbk + 31) >> 5;
+  for (int w = tid; w < W; w += 256) lds_bits[w] = 0u;
+  __syncthreads();
+  if (nbk == 0) {  // uniform over the workgroup
+    if (tid == 0) a.eff_ctx[s] = 0;
+    return;
+  }
+  const int n = min(max(a.num_selected != nullptr ? a.num_selected[s] : 0, 0), a.max_selected);
+  const int* sel = a.selected + (size_t)s * a.sel_stride;
+  for (int i = tid; i < n; i += 256) {
+    const int e = sel[i];
+    if (e >= 0 && e < nbk - 1) atomicOr(&lds_bits[e >> 5], 1u << (e & 31));
+  }
+  if (tid == 0) atomicOr(&lds_bits[(nbk - 1) >> 5], 1u << ((nbk - 1) & 31));
+  __syncthreads();
+  const int* bt = a.block_table + (size_t)s * a.bt_stride;
+  int* out = a.cbt + (size_t)s * a.cbt_stride;
+  int base = 0;
+  for (int w0 = 0; w0 < W; w0 += 256) {
+    const int w = w0 + tid;
+    const unsigned int v = w < W ? lds_bits[w] : 0u;
+    const int c = __popc(v);
+    scan[tid] = c;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int t = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += t;
+      __syncthreads();
+    }
+    int pos = base + scan[tid] - c;
+    for (unsigned int m = v; m != 0u; m &= m - 1u) out[pos++] = bt[w * 32 + __builtin_ctz(m)];
+    base += scan[255];
+    __syncthreads();
+  }
+  if (tid == 0) a.eff_ctx[s] = 16 * (base - 1) + min(16, ctx - 16 * (nbk - 1));
+}
+
+size_t sparse_select_lds_bytes(int max_context_len) {
+  const int blocks = (max_context_len + 15) / 16;
+  return ((size_t)(blocks + 31) / 32 + 256) * sizeof(int);
+}
+
+hipError_t launch_sparse_select(const SparseSelectArgs& a, int num_seqs, hipStream_t stream) {
+  if (num_seqs == 0) return hipSuccess;
+  const size_t lds = (size_t)(a.words_max + 256) * sizeof(int);
+  hipLaunchKernelGGL(sparse_select_kernel, dim3((unsigned)num_seqs), dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -220,6 +220,16 @@ def make_batch(name: str, seed: int, ctx_lens: Sequence[int], q_lens: Sequence[i
     assert all(1 <= q <= c for q, c in zip(q_lens, ctx_lens))
     table, NB, used = _assign_blocks(rng, ctx_lens, shared_groups, shared_prefix or {}, extra_blocks,
                                      pool_blocks)
+    return _finish_batch(name, seed, ctx_lens, q_lens, num_heads, num_kv_heads, head_size, q_dtype, cache_dtype,
+                         sliding_window, scale, device, table, NB, used, chunk_blocks, shared_groups,
+                         shared_prefix)
+
+
+def _finish_batch(name, seed, ctx_lens, q_lens, num_heads, num_kv_heads, head_size, q_dtype, cache_dtype,
+                  sliding_window, scale, device, table, NB, used, chunk_blocks, shared_groups=(),
+                  shared_prefix=None) -> Batch:
+    """Draws the pool, poisons what no sequence owns, draws the queries and
+    the new tokens' rows, for a given block assignment."""
     H, D = num_kv_heads, head_size
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
@@ -289,6 +299,83 @@ def make_batch(name: str, seed: int, ctx_lens: Sequence[int], q_lens: Sequence[i
                  k_scale=k_scale, v_scale=v_scale, new_key=new_key, new_value=new_value,
                  shared_groups=[list(g) for g in shared_groups],
                  shared_prefix=dict(shared_prefix or {}))
+
+
+@dataclass
+class SparseChoice:
+    """Chosen logical blocks per sequence as pa_decode_sparse takes them."""
+    selected: np.ndarray      # int32 [S][width] (entries past num_selected are -1)
+    num_selected: np.ndarray  # int32 [S]
+    chosen: List[List[int]]   # per sequence: the distinct valid blocks, ascending, newest last
+
+    def device(self, device) -> Dict[str, torch.Tensor]:
+        return {"selected": torch.from_numpy(self.selected).to(device),
+                "num_selected": torch.from_numpy(self.num_selected).to(device)}
+
+
+def make_sparse_batch(name: str, seed: int, ctx_lens: Sequence[int], k_blocks: int, num_heads: int,
+                      num_kv_heads: int, head_size: int, q_dtype: str = "bf16", cache_dtype: str = "bf16",
+                      device="cpu", noise: bool = False, chunk_blocks: int = 16384):
+    """A decode batch where each sequence's indexer picked k_blocks of its
+    earlier blocks (distinct, uniform over [0, newest block), listed in a
+    random order). Only the chosen blocks and the newest block own physical
+    blocks with data; every other logical block points at one shared block
+    of NaN, so a read of an unchosen block shows in the output. With
+    ``noise`` the lists also carry repeats, the newest block, ids past it
+    and negative ids (to be ignored), and a tail past num_selected that names
+    unchosen blocks (never to be read). Returns (Batch, SparseChoice)."""
+    rng = np.random.default_rng(seed)
+    ctx_lens = [int(c) for c in ctx_lens]
+    S = len(ctx_lens)
+    lists, chosen = [], []
+    for c in ctx_lens:
+        nbk = -(-c // BLOCK)
+        k = min(k_blocks, nbk - 1)
+        pick = rng.choice(nbk - 1, size=k, replace=False).astype(np.int64) if k > 0 else np.zeros(0, np.int64)
+        lst = pick.tolist()
+        if noise:
+            lst += [int(x) for x in rng.choice(pick, size=min(3, k))] if k else []
+            lst += [nbk - 1, nbk, nbk + 7, -1, -5]
+        rng.shuffle(lst)
+        lists.append(lst)
+        chosen.append(sorted(int(x) for x in pick) + [nbk - 1])
+    tail = 2 if noise else 0
+    width = max(1, max(len(x) for x in lists) + tail)
+    selected = np.full((S, width), -1, dtype=np.int32)
+    num_selected = np.zeros(S, dtype=np.int32)
+    for s, lst in enumerate(lists):
+        selected[s, :len(lst)] = lst
+        num_selected[s] = len(lst)
+        nbk = -(-ctx_lens[s] // BLOCK)
+        unchosen = sorted(set(range(nbk - 1)) - set(chosen[s]))
+        for t in range(tail):
+            if unchosen:
+                selected[s, len(lst) + t] = unchosen[t % len(unchosen)]
+    total = sum(len(x) for x in chosen)
+    NB = total + 1
+    perm = rng.permutation(NB).astype(np.int32)
+    poison_block = int(perm[-1])
+    stride = max(-(-c // BLOCK) for c in ctx_lens)
+    table = np.full((S, stride), poison_block, dtype=np.int32)
+    nxt = 0
+    for s, blks in enumerate(chosen):
+        for b in blks:
+            table[s, b] = perm[nxt]
+            nxt += 1
+    used = perm[:nxt]
+    batch = _finish_batch(name, seed, ctx_lens, [1] * S, num_heads, num_kv_heads, head_size, q_dtype, cache_dtype,
+                          0, None, device, table, NB, used, chunk_blocks)
+    return batch, SparseChoice(selected, num_selected, chosen)
+
+
+def make_sparse_config(device="cpu"):
+    """Long-context sparse decode: 64 sequences, contexts U{32768..524288},
+    128 chosen blocks (2048 keys) plus the newest block each, 32/8 heads,
+    d 128, bf16; the Llama-shaped decode's heads at the long contexts where
+    sparse attention pays."""
+    rng = np.random.default_rng(6)
+    ctx = rng.integers(32768, 524289, 64).tolist()
+    return make_sparse_batch("sparse_decode", 6, ctx, 128, 32, 8, 128, "bf16", "bf16", device=device)
 
 
 # ----------------------------------------------------------------------------

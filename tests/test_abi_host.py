@@ -228,3 +228,37 @@ def test_copy_blocks_rejects_bad_arguments(lib):
     assert call(k=None) == 1
     assert call(dt=2) == 1  # fp8 without scales
     assert call(n=0, pairs=None, k=None, v=None) == 0  # nothing to do, nothing launched
+
+
+def test_sparse_decode_rejects_bad_arguments(lib):
+    L = lib.load()
+
+    def call(**over):
+        a = dict(out=1, query=1, k=1, v=1, ks=None, vs=None, bt=1, bt_stride=8, ctx=1, S=2, max_ctx=100, sel=1,
+                 sel_stride=4, nsel=1, max_sel=4, Hq=8, Hkv=2, D=128, B=16, NB=10, qd=1, cd=1, scale=0.1, ws=1,
+                 ws_bytes=1 << 30)
+        a.update(over)
+        return L.pa_decode_sparse(a["out"], a["query"], a["k"], a["v"], a["ks"], a["vs"], a["bt"], a["bt_stride"],
+                                  a["ctx"], a["S"], a["max_ctx"], a["sel"], a["sel_stride"], a["nsel"], a["max_sel"],
+                                  a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"], a["qd"], a["cd"], a["scale"], a["ws"],
+                                  a["ws_bytes"], None)
+
+    assert call(max_sel=-1) == 1
+    assert call(max_sel=(1 << 22) + 1) == 1
+    assert call(sel=None) == 1
+    assert call(nsel=None) == 1
+    assert call(sel_stride=3) == 1
+    assert call(B=32) == 2
+    assert call(Hq=6, Hkv=4) == 1
+    assert call(bt_stride=2) == 1
+    assert call(ws_bytes=16) == 3
+    assert call(ws=None) == 3
+    assert call(max_ctx=1 << 25, bt_stride=1 << 21) == 2  # beyond the block bitmap
+    assert call(S=0) == 0
+    # nothing chosen: the lists may be absent
+    need = L.pa_decode_sparse_workspace_bytes(2, 0, 8, 2, 128, 1)
+    assert need > 0
+    assert call(sel=None, nsel=None, max_sel=0, sel_stride=0, ws_bytes=need - 1) == 3
+    assert L.pa_decode_sparse_workspace_bytes(2, -1, 8, 2, 128, 1) == 0
+    assert (L.pa_decode_sparse_workspace_bytes(64, 128, 32, 8, 128, 1)
+            >= 64 * 129 * 4 + lib.decode_workspace_bytes(64, 16 * 129, 32, 8, 128, "bf16"))
