@@ -11,7 +11,8 @@ value = algorithmic K+V bytes read per step / step time.
 Beside it in the same line: the mixed chunked-prefill step (192 decode rows +
 one 2048-token chunk on a 65536-token prefix, 2240 new tokens written first)
 in new tokens/s, the roofline of the decode kernel, the prefill chunk's
-MFMA throughput, and the CPU oracle timed on a bounded sample.
+MFMA throughput, the sparse decode over chosen blocks at 32K..512K-token
+contexts, and the CPU oracle timed on a bounded sample.
 Everything is one attention layer.
 """
 
@@ -83,6 +84,55 @@ def shared_prefix_step_fns(pa, torch, b):
                                 b.v_scale, b.sliding_window, ws)
 
     return write, attend
+
+
+def sparse_step_fns(pa, torch, b, choice):
+    """Decode through pa_decode_sparse over each sequence's chosen blocks."""
+    m = b.meta("cuda")
+    c = choice.device("cuda")
+    out = torch.empty_like(b.query)
+    ms = choice.selected.shape[1]
+    n = pa.decode_sparse_workspace_bytes(b.num_seqs, ms, b.num_heads, b.num_kv_heads, b.head_size, b.cache_dtype)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+
+    def write():
+        pa.reshape_and_cache(b.new_key, b.new_value, b.k_cache, b.v_cache, m["slot_mapping"], b.k_scale,
+                             b.v_scale)
+
+    def attend():
+        pa.decode_sparse(out, b.query, b.k_cache, b.v_cache, m["block_table"], m["context_lens"],
+                         b.max_context_len, c["selected"], c["num_selected"], b.scale, b.k_scale, b.v_scale, ws)
+
+    return write, attend
+
+
+def sparse_kv_bytes(b, choice):
+    """K+V bytes a sparse decode reads: the keys of every chosen block (the
+    newest block up to the context end)."""
+    toks = 0
+    for ctx, blks in zip(b.context_lens.tolist(), choice.chosen):
+        nbk = -(-ctx // 16)
+        toks += 16 * (len(blks) - 1) + ctx - 16 * (nbk - 1)
+    e = {"bf16": 2, "f32": 4, "fp8_e4m3": 1}[b.cache_dtype]
+    return toks * b.num_kv_heads * b.head_size * 2 * e
+
+
+def run_sparse(pa, torch, W, steps, warmup, ctx=None):
+    """The long-context sparse batch (or, with ctx, 64 sequences of ctx tokens
+    each with the same 128-block choice size)."""
+    if ctx is None:
+        b, choice = W.make_sparse_config(device="cuda")
+    else:
+        b, choice = W.make_sparse_batch(f"sparse_ctx{ctx}", 60, [ctx] * 64, 128, 32, 8, 128, device="cuda")
+    torch.cuda.synchronize()
+    write, attend = sparse_step_fns(pa, torch, b, choice)
+    step_ms, attend_ms, wall = time_steps(torch, write, attend, steps, warmup)
+    kv = sparse_kv_bytes(b, choice)
+    dense = b.kv_bytes_read()
+    res = {"step_ms": step_ms, "attend_ms": attend_ms, "kv_bytes": kv, "dense_kv_bytes": dense,
+           "kv_gbs_attend": kv / (attend_ms * 1e-3) / 1e9, "mean_context": float(b.context_lens.mean()),
+           "chosen_blocks_per_seq": 128}
+    return b, res
 
 
 def prefill_step_fns(pa, torch, b):
@@ -285,7 +335,7 @@ def main():
     ap.add_argument("--profile-pass", action="store_true",
                     help="only the kernels a counter run needs: a plain 1 GiB device copy (the "
                          "calibration kernel for FETCH_SIZE/WRITE_SIZE), a few decode and mixed steps, "
-                         "and the mixed step's chunk alone")
+                         "the mixed step's chunk alone and a few sparse decode calls")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
@@ -322,6 +372,12 @@ def main():
             torch.cuda.synchronize()
             del b
             torch.cuda.empty_cache()
+        sb, choice = W.make_sparse_config(device="cuda")
+        _, sp_attend = sparse_step_fns(pa, torch, sb, choice)
+        for _ in range(3):
+            sp_attend()
+        torch.cuda.synchronize()
+        del sb
         log("profile pass done")
         return
 
@@ -347,8 +403,24 @@ def main():
     del mb, chunk
     torch.cuda.empty_cache()
 
+    # ---- sparse decode over chosen blocks, long contexts ----
+    sb, sp = run_sparse(pa, torch, W, max(10, args.steps // 2), args.warmup)
+    log(f"sparse_decode: pa_decode_sparse {sp['attend_ms']*1e3:.1f} us, {sp['kv_gbs_attend']:.0f} GB/s of chosen "
+        f"K/V ({sp['kv_bytes']/1e6:.0f} MB of {sp['dense_kv_bytes']/1e9:.1f} GB in the contexts)")
+    del sb
+    torch.cuda.empty_cache()
+
     extra = {}
     if args.extra:
+        # the sparse decode's time against the context length at a fixed choice
+        sweep = {}
+        for ctx in (8192, 65536, 524288):
+            sb, r = run_sparse(pa, torch, W, max(10, args.steps // 2), args.warmup, ctx=ctx)
+            sweep[str(ctx)] = round(r["attend_ms"] * 1e3, 2)
+            log(f"sparse decode, 64 x {ctx} tokens, 128 blocks chosen: {r['attend_ms']*1e3:.1f} us")
+            del sb
+            torch.cuda.empty_cache()
+        extra["sparse_decode_us_by_context"] = sweep
         for name in ("tiny_decode", "agentic_decode", "fp8_decode", "fp8_swa128"):
             eb, r = run_config(pa, torch, W, name, max(5, args.steps // 2), args.warmup)
             extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
@@ -414,6 +486,14 @@ def main():
                                                 "probe": "libpa_peaks: back-to-back independent 32x32x16 "
                                                          "bf16 MFMAs, 8 waves per CU",
                                                 "fp16_tflops": ceil["mfma_fp16_tflops"]}}},
+        "sparse_decode": {"value": round(sp["kv_gbs_attend"], 2), "unit": "GB/s", "attend_ms": round(sp["attend_ms"], 5),
+                          "step_ms": round(sp["step_ms"], 5),
+                          "workload": "64 sequences, context U{32768..524288}, 128 chosen blocks (2048 keys) + "
+                                      "the newest block each, 32/8 heads, d128, bf16; pa_decode_sparse",
+                          "kv_bytes_per_call": sp["kv_bytes"], "dense_kv_bytes": sp["dense_kv_bytes"],
+                          "roofline": {"bound": "hbm", "achieved": round(sp["kv_gbs_attend"], 2),
+                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": round(sp["kv_gbs_attend"] / HBM_PEAK_GBS, 4)}},
     }
     if extra:
         line["extra"] = extra
