@@ -44,4 +44,6 @@ from .attention import (  # noqa: F401
     selected_positions,
     partial_softmax,
     merge_partials,
+    normalized_partial,
+    merge_normalized,
 )

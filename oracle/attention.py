@@ -178,6 +178,30 @@ def partial_softmax(scores, values):
     return m, w.sum(), w @ v
 
 
+def normalized_partial(scores, values):
+    """One key range's result in the form a context-parallel rank hands over:
+    (o, lse) = (sum e^s v / sum e^s, ln sum e^s), computed as
+    o = o_i / l_i and lse = m_i + ln l_i from ``partial_softmax``.
+
+    Decode context parallelism splits a sequence's cached positions into
+    contiguous ranges, one per GPU; each attends over its own range and the
+    ranges' results are combined by the online-softmax correction
+    ("宣稱省下 106 倍成本…", "DCP 的切法：照「序列位置」切，不照「頭」切" and the
+    online-softmax Q&A of "中：Kimi K3 的 DCP 選擇與 DEP 轉折").
+    """
+    m, l, o = partial_softmax(scores, values)
+    return np.asarray(o, dtype=np.float64) / l, m + np.log(l)
+
+
+def merge_normalized(parts):
+    """Exact result from per-range (o_r, lse_r): with M = max_r lse_r,
+    out = sum_r e^(lse_r - M) o_r / sum_r e^(lse_r - M). A range with no keys
+    (lse = -inf) weighs nothing."""
+    M = max(p[1] for p in parts)
+    w = [np.exp(p[1] - M) for p in parts]
+    return sum(wi * np.asarray(p[0], dtype=np.float64) for wi, p in zip(w, parts)) / sum(w)
+
+
 def merge_partials(parts):
     """Exact softmax output from per-range summaries (m_i, l_i, o_i).
 

@@ -205,3 +205,17 @@ def test_sparse_newest_block_off_by_one_is_caught(monkeypatch):
 
     monkeypatch.setattr(A, "selected_positions", mutant)
     _sparse_pins_fail()
+
+
+def test_lse_merge_without_correction_is_caught(monkeypatch):
+    from tests import test_oracle_dcp as TD
+
+    def mutant(parts):  # plain average of the ranges' results
+        return sum(np.asarray(p[0], dtype=np.float64) for p in parts) / len(parts)
+
+    monkeypatch.setattr(oracle, "merge_normalized", mutant)
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "weighted_average_merge.json")) as f:
+        g = json.load(f)
+    _expect_failure(TD.test_weighted_average_example_in_normalized_form, lambda name: g)
