@@ -213,6 +213,45 @@ pa_status pa_decode_sparse(void* out, const void* query, const void* k_cache, co
                            size_t workspace_bytes, pa_stream_t stream);
 
 /*
+ * One rank's share of decode context parallelism: the KV cache of every
+ * sequence is split by position into contiguous ranges, one per GPU, each
+ * GPU attends over its own range only, and the ranges' results are combined
+ * with the online-softmax correction ("宣稱省下 106 倍成本…", "DCP 的切法：
+ * 照「序列位置」切，不照「頭」切" and the online-softmax Q&A of "中：Kimi K3
+ * 的 DCP 選擇與 DEP 轉折"). This call is pa_decode over the local range
+ * (context_lens[s] = the tokens of sequence s this rank holds, which may be
+ * 0; every one is visible to the query) that also writes
+ *   lse: fp32 [num_seqs][num_heads], device: ln of the softmax denominator,
+ *        ln sum_j exp(scale <q_h, K_j>) over the local keys (-inf, with a
+ *        zero output row, when the range is empty).
+ * The output is normalised over the local keys, in the query's type. No
+ * sliding window. Needs the matrix-core decode (BF16 queries, BF16 or
+ * FP8_E4M3 cache): PA_ERR_UNSUPPORTED otherwise. Workspace as pa_decode
+ * (pa_decode_workspace_bytes with sliding_window 0).
+ */
+pa_status pa_decode_partial(void* out, float* lse, const void* query, const void* k_cache, const void* v_cache,
+                            const float* k_scale, const float* v_scale, const int32_t* block_table,
+                            int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                            int32_t block_size, int32_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype,
+                            float scale, void* workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/*
+ * Combines num_parts results over disjoint key ranges of the same queries
+ * (after the ranks' results are gathered onto one GPU):
+ *   out[i] = sum_r e^(lse_r[i] - M) parts[r][i] / sum_r e^(lse_r[i] - M),
+ *   M = max_r lse_r[i]; lse_out[i] = M + ln sum_r e^(lse_r[i] - M)
+ * (same source as pa_decode_partial; the weighted-average example there).
+ * parts: [num_parts][num_rows][head_size] in dtype (F32 or BF16), device;
+ * parts_lse: fp32 [num_parts][num_rows], device; out: [num_rows][head_size]
+ * in dtype; lse_out: fp32 [num_rows] or NULL. A row is one (token, head);
+ * head_size 64, 128 or 512. Ranges with lse = -inf weigh nothing; a row with
+ * every lse = -inf gets zeros and -inf.
+ */
+pa_status pa_merge_partials(void* out, float* lse_out, const void* parts, const float* parts_lse, int32_t num_parts,
+                            int32_t num_rows, int32_t head_size, pa_dtype dtype, pa_stream_t stream);
+
+/*
  * Causal attention for a flattened variable-length batch.
  * Sequence s owns query rows cu_seqlens[s] .. cu_seqlens[s+1]-1 (int32
  * [num_seqs+1]); context_lens[s] counts its cached tokens including this

@@ -35,6 +35,8 @@ EXPORTED = (
     "pa_decode",
     "pa_decode_shared_prefix",
     "pa_decode_sparse",
+    "pa_decode_partial",
+    "pa_merge_partials",
     "pa_prefill_chunk",
     "pa_decode_workspace_bytes",
     "pa_decode_shared_prefix_workspace_bytes",
@@ -81,6 +83,11 @@ def load() -> ctypes.CDLL:
                                    i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, sz, vp]
     L.pa_decode_sparse_workspace_bytes.restype = sz
     L.pa_decode_sparse_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
+    L.pa_decode_partial.restype = ctypes.c_int
+    L.pa_decode_partial.argtypes = [vp, vp, vp, vp, vp, f32p, f32p, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, sz, vp]
+    L.pa_merge_partials.restype = ctypes.c_int
+    L.pa_merge_partials.argtypes = [vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp]
     L.pa_prefill_chunk.restype = ctypes.c_int
     L.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                    i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_float, i32,
@@ -255,6 +262,37 @@ def decode_sparse(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
                                    Hq, Hkv, D, k_cache.shape[2], NB, dtype_code(query.dtype),
                                    dtype_code(k_cache.dtype), float(scale), _ptr(workspace), ws_bytes,
                                    _stream(stream)))
+
+
+def decode_partial(out: torch.Tensor, lse: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
+                   v_cache: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor,
+                   max_context_len: int, scale: float, k_scale: Optional[torch.Tensor] = None,
+                   v_scale: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+    """pa_decode_partial: pa_decode over a rank's key range that also writes
+    lse fp32 [S][Hq] (ln of the softmax denominator)."""
+    S, Hq, D = query.shape
+    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
+    assert lse.dtype == torch.float32 and lse.numel() == S * Hq
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().pa_decode_partial(_ptr(out), _ptr(lse), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                    _ptr(v_scale), _ptr(block_table), block_table.shape[1], _ptr(context_lens), S,
+                                    int(max_context_len), Hq, Hkv, D, k_cache.shape[2], NB, dtype_code(query.dtype),
+                                    dtype_code(k_cache.dtype), float(scale), _ptr(workspace), ws_bytes,
+                                    _stream(stream)))
+
+
+def merge_partials(out: torch.Tensor, parts: torch.Tensor, parts_lse: torch.Tensor,
+                   lse_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """pa_merge_partials: parts [R][rows...][D] and parts_lse fp32 [R][rows...]
+    into out [rows...][D] (and lse_out [rows...])."""
+    R, D = parts.shape[0], parts.shape[-1]
+    rows = parts[0].numel() // D
+    assert parts.is_contiguous() and parts_lse.is_contiguous() and out.is_contiguous()
+    assert parts_lse.dtype == torch.float32 and parts_lse.numel() == R * rows
+    assert out.numel() == rows * D and out.dtype == parts.dtype
+    _check(load().pa_merge_partials(_ptr(out), _ptr(lse_out), _ptr(parts), _ptr(parts_lse), R, rows, D,
+                                    dtype_code(parts.dtype), _stream(stream)))
 
 
 def prefill_chunk(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

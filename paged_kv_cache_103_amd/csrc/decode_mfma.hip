@@ -245,6 +245,7 @@ __device__ __forceinline__ void wave_write(WaveAcc<D>& acc, const DecodeArgs& a,
   if (c16 >= ncols) return;
   if (single) {
     const float inv = 1.f / L;
+    if (a.lse != nullptr && q4 == 0) a.lse[(size_t)qrow * a.num_heads + g * G + c16] = (acc.m + log2f(L)) * kLn2;
     uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * a.num_heads + g * G + c16) * D + 4 * q4;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
@@ -635,7 +636,9 @@ __global__ __launch_bounds__(256) void decode_split_merge(DecodeArgs a) {
     }
   }
   L = strided_sum<1>(L);
-  const float inv = 1.f / L;
+  // no keys at all (an empty context range): zero output, lse = -inf
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  if (a.lse != nullptr && lane == 0) a.lse[(size_t)qrow * a.num_heads + hq] = (M + log2f(L)) * kLn2;
 #pragma unroll
   for (int k = 0; k < DL; ++k)
     reinterpret_cast<uint16_t*>(a.out)[((size_t)qrow * a.num_heads + hq) * D + k * 64 + lane] =

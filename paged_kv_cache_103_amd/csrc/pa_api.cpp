@@ -196,13 +196,14 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_
                                    cache_dtype, sliding_window);
 }
 
-pa_status pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
-                    const float* k_scale, const float* v_scale, const int32_t* block_table,
-                    int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
-                    int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
-                    int32_t head_size, int32_t block_size, int32_t num_blocks, pa_dtype q_dtype,
-                    pa_dtype cache_dtype, float scale, int32_t sliding_window, void* workspace,
-                    size_t workspace_bytes, pa_stream_t stream) {
+// pa_decode, and pa_decode_partial when lse is given.
+static pa_status decode_impl(void* out, float* lse, const void* query, const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale, const int32_t* block_table,
+                             int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                             int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_size, int32_t block_size, int32_t num_blocks, pa_dtype q_dtype,
+                             pa_dtype cache_dtype, float scale, int32_t sliding_window, void* workspace,
+                             size_t workspace_bytes, pa_stream_t stream) {
   pa_status st = check_attention_common(out, query, k_cache, v_cache, k_scale, v_scale, block_table,
                                         block_table_stride, context_lens, num_seqs, max_context_len,
                                         num_heads, num_kv_heads, head_size, block_size, num_blocks,
@@ -214,6 +215,9 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
   }
   const pa::DecodePlan plan = make_plan(num_seqs, max_context_len, num_heads, num_kv_heads, head_size,
                                         cache_dtype, sliding_window);
+  if (lse != nullptr && plan.split_waves <= 0)
+    return fail(PA_ERR_UNSUPPORTED, "partial decode needs the matrix-core kernel (bf16 queries, bf16 or fp8 "
+                "cache, at most 16000 sequences)");
   const size_t need = pa::decode_workspace_bytes(plan, num_seqs, num_heads, num_kv_heads, head_size);
   if (workspace_bytes < need || (need > 0 && workspace == nullptr))
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes (got %zu)", need,
@@ -235,8 +239,51 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
   a.num_kv_heads = num_kv_heads;
   a.window = sliding_window;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.lse = lse;
   hipError_t e = pa::launch_decode(a, (int)q_dtype, (int)cache_dtype, head_size, (hipStream_t)stream);
   return hip_status(e, "decode launch");
+}
+
+pa_status pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
+                    const float* k_scale, const float* v_scale, const int32_t* block_table,
+                    int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_size, int32_t block_size, int32_t num_blocks, pa_dtype q_dtype,
+                    pa_dtype cache_dtype, float scale, int32_t sliding_window, void* workspace,
+                    size_t workspace_bytes, pa_stream_t stream) {
+  return decode_impl(out, nullptr, query, k_cache, v_cache, k_scale, v_scale, block_table, block_table_stride,
+                     context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_size, block_size,
+                     num_blocks, q_dtype, cache_dtype, scale, sliding_window, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_partial(void* out, float* lse, const void* query, const void* k_cache, const void* v_cache,
+                            const float* k_scale, const float* v_scale, const int32_t* block_table,
+                            int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                            int32_t block_size, int32_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype,
+                            float scale, void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  if (lse == nullptr && num_seqs > 0) return fail(PA_ERR_INVALID_ARGUMENT, "null device pointer (lse)");
+  return decode_impl(out, lse, query, k_cache, v_cache, k_scale, v_scale, block_table, block_table_stride,
+                     context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_size, block_size,
+                     num_blocks, q_dtype, cache_dtype, scale, 0, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_merge_partials(void* out, float* lse_out, const void* parts, const float* parts_lse, int32_t num_parts,
+                            int32_t num_rows, int32_t head_size, pa_dtype dtype, pa_stream_t stream) {
+  if (num_parts < 1) return fail(PA_ERR_INVALID_ARGUMENT, "num_parts must be >= 1 (got %d)", num_parts);
+  if (num_rows < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_rows must be >= 0 (got %d)", num_rows);
+  if (head_size != 64 && head_size != 128 && head_size != 512)
+    return fail(PA_ERR_UNSUPPORTED, "head_size must be 64, 128 or 512 (got %d)", head_size);
+  if (dtype != PA_F32 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "merge dtype must be f32 or bf16 (got %d)", (int)dtype);
+  if (num_rows == 0) {
+    g_last_error.clear();
+    return PA_OK;
+  }
+  if (!out || !parts || !parts_lse) return fail(PA_ERR_INVALID_ARGUMENT, "null device pointer");
+  hipError_t e = pa::launch_merge_lse(out, lse_out, parts, parts_lse, num_parts, num_rows, head_size, (int)dtype,
+                                      (hipStream_t)stream);
+  return hip_status(e, "merge launch");
 }
 
 // Whether pa_decode_shared_prefix reads shared blocks once (else it serves

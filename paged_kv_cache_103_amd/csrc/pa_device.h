@@ -134,5 +134,6 @@ __device__ __forceinline__ u32x2 load8_stream(const void* p) {
 
 // log2(e): scores are kept premultiplied by scale*log2(e) so that exp2 is used.
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 }  // namespace pa

@@ -83,6 +83,7 @@ struct DecodeArgs {
   int max_parts;
   int split_waves;
   float scale_log2;  // softmax scale * log2(e)
+  float* lse;        // optional [rows][num_heads]: ln of the softmax denominator (matrix-core kernel)
 };
 
 // q_kind / cache_kind: 0 = f32, 1 = bf16, 2 = fp8 e4m3fn.
@@ -110,6 +111,10 @@ constexpr int kSparseMaxSelected = 1 << 22;
 constexpr size_t kSparseMaxLds = 64 * 1024;  // bitmap + scan: contexts up to 8,257,536 tokens
 size_t sparse_select_lds_bytes(int max_context_len);
 hipError_t launch_sparse_select(const SparseSelectArgs& a, int num_seqs, hipStream_t stream);
+
+// Merge of per-range attention results (o_r, lse_r) into one.
+hipError_t launch_merge_lse(void* out, float* lse_out, const void* parts, const float* parts_lse, int num_parts,
+                            int num_rows, int head_size, int kind, hipStream_t stream);
 
 struct PrefillArgs {
   void* out;

@@ -262,3 +262,35 @@ def test_sparse_decode_rejects_bad_arguments(lib):
     assert L.pa_decode_sparse_workspace_bytes(2, -1, 8, 2, 128, 1) == 0
     assert (L.pa_decode_sparse_workspace_bytes(64, 128, 32, 8, 128, 1)
             >= 64 * 129 * 4 + lib.decode_workspace_bytes(64, 16 * 129, 32, 8, 128, "bf16"))
+
+
+def test_partial_decode_and_merge_reject_bad_arguments(lib):
+    L = lib.load()
+
+    def partial(**over):
+        a = dict(out=1, lse=1, query=1, k=1, v=1, ks=None, vs=None, bt=1, bt_stride=8, ctx=1, S=2, max_ctx=100,
+                 Hq=8, Hkv=2, D=128, B=16, NB=10, qd=1, cd=1, scale=0.1, ws=1, ws_bytes=1 << 30)
+        a.update(over)
+        return L.pa_decode_partial(a["out"], a["lse"], a["query"], a["k"], a["v"], a["ks"], a["vs"], a["bt"],
+                                   a["bt_stride"], a["ctx"], a["S"], a["max_ctx"], a["Hq"], a["Hkv"], a["D"], a["B"],
+                                   a["NB"], a["qd"], a["cd"], a["scale"], a["ws"], a["ws_bytes"], None)
+
+    assert partial(lse=None) == 1
+    assert partial(qd=0, cd=0) == 2  # fp32 caches take the VALU kernel: no partial results
+    assert partial(B=8) == 2
+    assert partial(ws_bytes=8) == 3
+    assert partial(S=0, lse=None) == 0
+
+    def merge(**over):
+        a = dict(out=1, lse_out=None, parts=1, parts_lse=1, R=2, rows=10, D=128, dt=1)
+        a.update(over)
+        return L.pa_merge_partials(a["out"], a["lse_out"], a["parts"], a["parts_lse"], a["R"], a["rows"], a["D"],
+                                   a["dt"], None)
+
+    assert merge(R=0) == 1
+    assert merge(rows=-1) == 1
+    assert merge(D=96) == 2
+    assert merge(dt=2) == 2
+    assert merge(parts=None) == 1
+    assert merge(parts_lse=None) == 1
+    assert merge(rows=0, out=None, parts=None, parts_lse=None) == 0
