@@ -135,6 +135,52 @@ def run_sparse(pa, torch, W, steps, warmup, ctx=None):
     return b, res
 
 
+def run_context_parallel(pa, torch, W, ranks, steps, warmup):
+    """The Llama-shaped decode batch as `ranks` context-parallel ranks would
+    run it: every sequence cut into `ranks` contiguous block-aligned ranges,
+    each rank's pa_decode_partial over its ranges (timed one after another on
+    this GPU), then pa_merge_partials of the gathered results."""
+    import numpy as np
+    b = W.make_config("llama8b_decode", device="cuda")
+    S, Hq, D = b.query.shape
+    calls = []
+    for r in range(ranks):
+        ctx, rows = [], []
+        for s in range(S):
+            nb = -(-int(b.context_lens[s]) // 16)
+            a0, a1 = nb * r // ranks, nb * (r + 1) // ranks
+            ctx.append(max(0, min(int(b.context_lens[s]), a1 * 16) - a0 * 16))
+            rows.append(b.block_table[s, a0:a1])
+        stride = max(1, max(len(x) for x in rows))
+        tab = np.zeros((S, stride), dtype=np.int32)
+        for s, x in enumerate(rows):
+            tab[s, :len(x)] = x
+        mc = max(1, max(ctx))
+        ws = torch.empty(max(pa.decode_workspace_bytes(S, mc, Hq, b.num_kv_heads, D), 1), dtype=torch.uint8,
+                         device="cuda")
+        calls.append((torch.from_numpy(tab).to("cuda"), torch.tensor(ctx, dtype=torch.int32, device="cuda"), mc, ws))
+    parts = torch.empty((ranks, S, Hq, D), dtype=b.query.dtype, device="cuda")
+    lses = torch.empty((ranks, S, Hq), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(b.query)
+
+    def ranks_fn():
+        for r, (tab, ctx, mc, ws) in enumerate(calls):
+            pa.decode_partial(parts[r], lses[r], b.query, b.k_cache, b.v_cache, tab, ctx, mc, b.scale, workspace=ws)
+
+    def merge_fn():
+        pa.merge_partials(out, parts, lses)
+
+    _, ranks_ms, _ = time_steps(torch, lambda: None, ranks_fn, steps, warmup)
+    _, merge_ms, _ = time_steps(torch, lambda: None, merge_fn, steps, warmup)
+    res = {"ranks": ranks, "all_ranks_ms": round(ranks_ms, 5), "per_rank_ms": round(ranks_ms / ranks, 5),
+           "merge_ms": round(merge_ms, 5), "merge_bytes": parts.numel() * parts.element_size() + lses.numel() * 4
+           + out.numel() * out.element_size()}
+    log(f"context parallel ({ranks} ranks, one GPU): all ranks {ranks_ms*1e3:.1f} us, merge {merge_ms*1e3:.1f} us")
+    del b
+    torch.cuda.empty_cache()
+    return res
+
+
 def prefill_step_fns(pa, torch, b):
     m = b.meta("cuda")
     out = torch.empty_like(b.query)
@@ -421,6 +467,8 @@ def main():
             del sb
             torch.cuda.empty_cache()
         extra["sparse_decode_us_by_context"] = sweep
+        extra["context_parallel_llama8b"] = run_context_parallel(pa, torch, W, 8, max(10, args.steps // 2),
+                                                                 args.warmup)
         for name in ("tiny_decode", "agentic_decode", "fp8_decode", "fp8_swa128"):
             eb, r = run_config(pa, torch, W, name, max(5, args.steps // 2), args.warmup)
             extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
