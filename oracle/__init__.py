@@ -16,6 +16,9 @@ paging     block arithmetic and the KV write (``reshape_and_cache``): slot =
 attention  gather through the block table and exact softmax attention with
            causal / sliding-window masks; sparse decode over chosen blocks;
            partial-softmax merge.
+mla        decode over a paged latent (MLA) cache: one shared row per token,
+           absorbed queries, values from the row's first dv elements;
+           imported on its own as ``oracle.mla``.
 blocks     plain model of the block manager's policy (refcounts, prefix reuse
            over full blocks, LRU free queue, fork and copy-on-write), imported
            on its own as ``oracle.blocks``.

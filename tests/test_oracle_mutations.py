@@ -219,3 +219,48 @@ def test_lse_merge_without_correction_is_caught(monkeypatch):
     with open(os.path.join(os.path.dirname(__file__), "golden", "weighted_average_merge.json")) as f:
         g = json.load(f)
     _expect_failure(TD.test_weighted_average_example_in_normalized_form, lambda name: g)
+
+
+# ---------------------------------------------------------------------------
+# latent-cache (MLA) decode
+# ---------------------------------------------------------------------------
+def _mla_pins_fail():
+    from tests import test_oracle_mla as TM
+
+    failures = 0
+    for case in [(1, 1, 6, 4), (20, 3, 10, 8), (33, 2, 7, 7)]:
+        try:
+            TM.test_brute_force_with_positional_part(*case)
+        except AssertionError:
+            failures += 1
+    try:
+        TM.test_equals_gqa_oracle_with_one_kv_head()
+    except AssertionError:
+        failures += 1
+    assert failures > 0, "the planted mistake passed every latent-decode pin"
+
+
+def test_mla_values_from_the_wrong_end_are_caught(monkeypatch):
+    from oracle import mla as M
+
+    def mutant(q_f64, pool, cache_dtype, row, ctx, scale, dv, block_size=16):
+        C = M.latent_rows(pool, cache_dtype, row, np.arange(ctx), block_size)
+        s = scale * (q_f64 @ C.T)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        return (p @ C[:, C.shape[1] - dv:]) / p.sum(axis=1, keepdims=True)
+
+    monkeypatch.setattr(M, "mla_decode_sequence", mutant)
+    _mla_pins_fail()
+
+
+def test_mla_scores_without_the_positional_part_are_caught(monkeypatch):
+    from oracle import mla as M
+
+    def mutant(q_f64, pool, cache_dtype, row, ctx, scale, dv, block_size=16):
+        C = M.latent_rows(pool, cache_dtype, row, np.arange(ctx), block_size)
+        s = scale * (q_f64[:, :dv] @ C[:, :dv].T)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        return (p @ C[:, :dv]) / p.sum(axis=1, keepdims=True)
+
+    monkeypatch.setattr(M, "mla_decode_sequence", mutant)
+    _mla_pins_fail()
