@@ -252,6 +252,35 @@ pa_status pa_merge_partials(void* out, float* lse_out, const void* parts, const 
                             int32_t num_rows, int32_t head_size, pa_dtype dtype, pa_stream_t stream);
 
 /*
+ * Decode over a paged latent (multi-head latent attention, MLA) cache: one
+ * cached row per token shared by every head instead of a K and a V per head.
+ * The heads' up-projections are folded into their queries (matrix
+ * absorption), so head h scores its absorbed query directly against the rows
+ * and takes the attention-weighted sum of the rows' first 512 elements (its
+ * value up-projection is applied to that sum afterwards, outside this call)
+ * ("宣稱省下 106 倍成本…", "MLA(Multi-head Latent Attention)是什麼、為什麼讓 TP
+ * 沒效率" and its two Q&As):
+ *   out[s][h][:] = sum_j softmax_j(scale <query[s][h], c_j>) c_j[0:512]
+ * over the context_lens[s] rows c_j of sequence s (the newest included).
+ * latent_cache: bf16 [num_blocks][16][head_dim_k]; row j of sequence s is
+ *   latent_cache[block_table[s][j / 16]][j % 16]. head_dim_k is 512 (the
+ *   latent alone, K = V = c) or 576 (512 latent elements and 64 more that
+ *   take part in the scores only, such as a positional part).
+ * query: bf16 [num_seqs][num_heads][head_dim_k]; out: bf16
+ *   [num_seqs][num_heads][512]; head_dim_v must be 512.
+ * num_heads: 16, 32, 64 or 128; num_seqs at most 2048; context_lens[s] >= 1.
+ * workspace: pa_mla_decode_workspace_bytes(num_seqs, num_heads) bytes.
+ */
+pa_status pa_mla_decode(void* out, const void* query, const void* latent_cache, const int32_t* block_table,
+                        int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                        int32_t max_context_len, int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+                        int32_t block_size, int32_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype, float scale,
+                        void* workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/* Workspace bytes pa_mla_decode needs (0 if arguments are out of range). */
+size_t pa_mla_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads);
+
+/*
  * Causal attention for a flattened variable-length batch.
  * Sequence s owns query rows cu_seqlens[s] .. cu_seqlens[s+1]-1 (int32
  * [num_seqs+1]); context_lens[s] counts its cached tokens including this

@@ -37,6 +37,8 @@ EXPORTED = (
     "pa_decode_sparse",
     "pa_decode_partial",
     "pa_merge_partials",
+    "pa_mla_decode",
+    "pa_mla_decode_workspace_bytes",
     "pa_prefill_chunk",
     "pa_decode_workspace_bytes",
     "pa_decode_shared_prefix_workspace_bytes",
@@ -88,6 +90,11 @@ def load() -> ctypes.CDLL:
                                     ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, sz, vp]
     L.pa_merge_partials.restype = ctypes.c_int
     L.pa_merge_partials.argtypes = [vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp]
+    L.pa_mla_decode.restype = ctypes.c_int
+    L.pa_mla_decode.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_float, vp, sz, vp]
+    L.pa_mla_decode_workspace_bytes.restype = sz
+    L.pa_mla_decode_workspace_bytes.argtypes = [i32, i32]
     L.pa_prefill_chunk.restype = ctypes.c_int
     L.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                    i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_float, i32,
@@ -293,6 +300,25 @@ def merge_partials(out: torch.Tensor, parts: torch.Tensor, parts_lse: torch.Tens
     assert out.numel() == rows * D and out.dtype == parts.dtype
     _check(load().pa_merge_partials(_ptr(out), _ptr(lse_out), _ptr(parts), _ptr(parts_lse), R, rows, D,
                                     dtype_code(parts.dtype), _stream(stream)))
+
+
+def mla_decode_workspace_bytes(num_seqs: int, num_heads: int) -> int:
+    return int(load().pa_mla_decode_workspace_bytes(num_seqs, num_heads))
+
+
+def mla_decode(out: torch.Tensor, query: torch.Tensor, latent_cache: torch.Tensor, block_table: torch.Tensor,
+               context_lens: torch.Tensor, max_context_len: int, scale: float,
+               workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """pa_mla_decode: query bf16 [S][H][dk], latent_cache bf16 [NB][16][dk],
+    out bf16 [S][H][512]."""
+    S, H, DK = query.shape
+    NB = latent_cache.shape[0]
+    assert latent_cache.shape[1] == 16 and latent_cache.shape[2] == DK and out.shape == (S, H, 512)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().pa_mla_decode(_ptr(out), _ptr(query), _ptr(latent_cache), _ptr(block_table), block_table.shape[1],
+                                _ptr(context_lens), S, int(max_context_len), H, DK, 512, 16, NB,
+                                dtype_code(query.dtype), dtype_code(latent_cache.dtype), float(scale),
+                                _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def prefill_chunk(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -1,0 +1,464 @@
+// Decode over a paged latent (MLA) cache on matrix cores (pa_mla_decode,
+// include/pa.h).
+//
+// Multi-head latent attention keeps one row c per token for every head; with
+// the up-projections folded into the queries each head scores its absorbed
+// query directly against c, and the values are the rows' first 512 elements
+// ("宣稱省下 106 倍成本…", "MLA(Multi-head Latent Attention)是什麼、為什麼讓 TP
+// 沒效率" and its Q&As). One row read from memory therefore serves all H
+// heads: per 32 keys the work is an (H x dk)(dk x 32) score product and an
+// (H x 32)(32 x 512) value product, dense enough that the rows have to be
+// read once per workgroup and shared through LDS.
+//
+// Workgroup: 8 waves, one per CU (the LDS holds a 3-slot ring of 32-key row
+// tiles plus a transposed value tile). Wave w serves the 16 heads of head
+// group w / NDP and the 512 / NDP output dims of part w % NDP (NDP = 128 / H:
+// with fewer heads the value dims are split so that every wave has work;
+// the score product is then repeated by the waves of a head group).
+// Per step of 32 keys (two blocks):
+//  * the tile arrives by global->LDS copies issued two steps ahead, row
+//    major with a per-row XOR swizzle of its 16-byte chunks (conflict-free
+//    score-operand reads);
+//  * one pass by all 512 threads writes the value part again, transposed and
+//    converted to fp16 ([512 dims][32 keys], 80-byte rows), zeroing keys past
+//    the context: the value product needs 8 consecutive keys of one dim per
+//    lane, the score product 8 consecutive dims of one key;
+//  * scores S^T = C Q^T on 16x16x32 bf16 MFMAs (queries held in registers as
+//    the B operand, keys in the permuted row order that makes each lane's
+//    score accumulator its own P^T operand), online softmax with lazy
+//    rescaling, O^T += V^T P^T on 16x16x32 fp16 MFMAs with P scaled by 2^7.
+// The concatenated (sequence, pair of blocks) streams are split evenly over
+// the workgroups; a sequence covered by one workgroup is finished in place,
+// others leave (max, sum, unnormalised output) summaries that a second kernel
+// merges exactly.
+#include <hip/hip_runtime.h>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int MLA_NW = 8;
+constexpr int MLA_NT = 64 * MLA_NW;
+constexpr int MLA_DV = 512;
+constexpr int MLA_VT_ROW = 80;  // bytes per transposed value row (64 data + 16 pad)
+
+__device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                  0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                 0, 0);
+}
+__device__ __forceinline__ uint32_t f16x2_bits(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
+}
+
+// Chunk swizzle of a tile row (key 0..31 of the step): 16 lanes reading one
+// chunk column of 16 permuted keys hit 16 distinct 16-byte bank groups.
+template <int DK>
+__device__ __forceinline__ int row_swizzle(int key) {
+  if constexpr (DK == 576) return ((key >> 1) & 1) | (((key >> 3) & 3) << 1);  // rows of 72 chunks
+  else return (key & 3) | (((key >> 3) & 3) << 2);                              // rows of 64 chunks
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void barrier_keep_loads() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// 16-byte global -> LDS copy per lane (lane i lands at lds_base + 16 i); see
+// the prefill kernel for why this is inline assembly. M0 is restored.
+__device__ __forceinline__ void dma16(const void* base, uint32_t lane_offset, uint32_t lds_base) {
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(lane_offset), "s"(base), "s"(lds_base)
+      : "memory");
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  typedef __attribute__((address_space(3))) const T lds_t;
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_t*)p);
+}
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+  typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+  return *(const lds_u32x4*)(uintptr_t)addr;
+}
+__device__ __forceinline__ void lds_write8(uint32_t addr, uint32_t lo, uint32_t hi) {
+  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+  *(lds_u32x2*)(uintptr_t)addr = u32x2{lo, hi};
+}
+
+}  // namespace
+
+template <int DK>
+struct MlaShape {
+  static constexpr int ROWB = DK * 2;            // bytes of one cached row
+  static constexpr int BLKB = 16 * ROWB;         // bytes of one block
+  static constexpr int TILEB = 32 * ROWB;        // bytes of one 32-key tile
+  static constexpr int PIECES = TILEB / 1024;    // 1 KiB copies per tile (36 or 32)
+  static constexpr int MAXP = (PIECES + MLA_NW - 1) / MLA_NW;  // copies per wave (5 or 4)
+  static constexpr int KS = DK / 32;             // score k-steps
+  static constexpr int SLOTS = 3;
+};
+
+constexpr int kMlaMaxSeqs = 2048;
+
+template <int DK, int H>
+__global__ __launch_bounds__(MLA_NT) void mla_decode_split(MlaArgs a) {
+  using S = MlaShape<DK>;
+  constexpr int NHG = H / 16;          // head groups
+  constexpr int NDP = MLA_NW / NHG;    // value-dim parts
+  constexpr int DVW = MLA_DV / NDP;    // value dims per wave
+  constexpr int DTW = DVW / 16;        // 16-dim output tiles per wave
+  __shared__ __attribute__((aligned(16))) uint8_t ring[S::SLOTS * S::TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t vt[MLA_DV * MLA_VT_ROW];
+  __shared__ int psum[kMlaMaxSeqs + 1];
+  __shared__ int scan[MLA_NT];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, q4 = lane >> 4;
+  const int hg = wave / NDP, dp = wave % NDP;
+  const int NS = a.num_seqs;
+
+  // ---- pairs of blocks per sequence, prefix sums (all threads) ----
+  {
+    int running = 0;
+    for (int base = 0; base < NS; base += MLA_NT) {
+      const int i = base + tid;
+      const int ctx = i < NS ? a.context_lens[i] : 0;
+      const int n = ctx > 0 ? (((ctx + 15) >> 4) + 1) >> 1 : 0;
+      scan[tid] = n;
+      __syncthreads();
+      for (int off = 1; off < MLA_NT; off <<= 1) {
+        const int v = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+      }
+      if (i < NS) psum[i] = running + scan[tid] - n;
+      running += scan[MLA_NT - 1];
+      __syncthreads();
+    }
+    if (tid == 0) psum[NS] = running;
+    __syncthreads();
+  }
+  const int T = psum[NS];
+  const int C = max(1, (T + (int)gridDim.x - 1) / (int)gridDim.x);
+  if (blockIdx.x == 0) {
+    if (tid == 0) a.meta[0] = C;
+    for (int i = tid; i <= NS; i += MLA_NT) a.meta[1 + i] = psum[i];
+  }
+
+  // ---- per-lane constant offsets ----
+  // copies: piece k of a tile = bytes [1024 k, 1024 k + 1024), wholly inside
+  // block k / (PIECES / 2); this lane's source offset inside that block
+  auto src_off = [&](int k) {
+    const int P = 1024 * k + 16 * lane;
+    const int row = P / S::ROWB, pch = (P % S::ROWB) / 16;
+    return (uint32_t)((row & 15) * S::ROWB + 16 * (pch ^ row_swizzle<DK>(row)));
+  };
+  const int npieces = (S::PIECES - wave + MLA_NW - 1) / MLA_NW;  // 5 or 4 (uniform per wave)
+  const uint32_t ring_lds = lds_addr(ring), vt_lds = lds_addr(vt);
+  // score operand rows: tile kt, MFMA row c16 holds key 8 (c16 / 4) + 4 kt + c16 % 4
+  int qk_row[2], qk_swz[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = 8 * (c16 >> 2) + 4 * kt + (c16 & 3);
+    qk_row[kt] = key * S::ROWB;
+    qk_swz[kt] = row_swizzle<DK>(key);
+  }
+  // transposition pass: thread = (key quad kq, value chunk c)
+  const int tq = lane & 7, tc = 8 * wave + (lane >> 3);
+  // value operand rows: dim dp * DVW + 16 dt + c16, keys 8 q4 .. 8 q4 + 7
+  const uint32_t pv_base = vt_lds + (uint32_t)((dp * DVW + c16) * MLA_VT_ROW + 16 * q4);
+
+  const uint8_t* cache = reinterpret_cast<const uint8_t*>(a.cache);
+  const long long x_end = min<long long>((long long)(blockIdx.x + 1) * C, T);
+  long long x = (long long)blockIdx.x * C;
+  while (x < x_end) {
+    // sequence holding pair x: last s with psum[s] <= x (uniform)
+    int lo = 0, hi = NS - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (psum[mid] <= x) lo = mid;
+      else hi = mid - 1;
+    }
+    const int s = __builtin_amdgcn_readfirstlane(lo);
+    const int sp0 = __builtin_amdgcn_readfirstlane(psum[s]);
+    const int np = psum[s + 1] - sp0;
+    const int p0 = (int)(x - sp0);
+    const int p1 = (int)(min<long long>(x_end, (long long)sp0 + np) - sp0);
+    const int n = p1 - p0;
+    // uniform metadata by scalar loads (constant address space): a vector
+    // load would make the compiler wait for every copy in flight
+    typedef __attribute__((address_space(4))) const int cint;
+    const int ctx = ((const cint*)a.context_lens)[s];
+    const int nblk = (ctx + 15) >> 4;
+    const cint* bt = (const cint*)(a.block_table + (size_t)s * a.bt_stride);
+
+    // queries of this wave's 16 heads (B operand of the score product)
+    u32x4 qf[S::KS];
+    {
+      const uint8_t* qp =
+          reinterpret_cast<const uint8_t*>(a.query) + ((size_t)s * H + 16 * hg + c16) * S::ROWB + 16 * q4;
+#pragma unroll
+      for (int j = 0; j < S::KS; ++j) qf[j] = load16(qp + 64 * j);
+    }
+    f32x4 o[DTW];
+#pragma unroll
+    for (int t = 0; t < DTW; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.f;
+
+    auto issue = [&](int i) {  // copies of the segment's pair i into slot i % 3
+      const int pb = 2 * (p0 + i);
+      const int b0 = bt[pb];
+      const int b1 = pb + 1 < nblk ? bt[pb + 1] : b0;
+      const uint32_t slot = ring_lds + (uint32_t)((i % S::SLOTS) * S::TILEB);
+#pragma unroll
+      for (int c = 0; c < S::MAXP; ++c) {
+        if (c < npieces) {
+          const int k = wave + MLA_NW * c;
+          const int blk = k < S::PIECES / 2 ? b0 : b1;
+          dma16(cache + (size_t)(uint32_t)blk * S::BLKB, src_off(k), slot + 1024u * (uint32_t)k);
+        }
+      }
+    };
+    issue(0);
+    if (n > 1) issue(1);
+
+    for (int i = 0; i < n; ++i) {
+      // the copies of pair i have landed (those of pair i + 1 may be in flight)
+      if (i + 1 < n) {
+        if (npieces == S::MAXP) wait_vm<S::MAXP>();
+        else wait_vm<S::MAXP - 1>();
+      } else {
+        wait_vm<0>();
+      }
+      barrier_keep_loads();  // every wave is done with pair i - 1
+      if (i + 2 < n) issue(i + 2);
+      const int key0 = 32 * (p0 + i);
+      const int kend = ctx - key0;  // keys of this tile at or past kend are masked
+      const uint32_t slot = ring_lds + (uint32_t)((i % S::SLOTS) * S::TILEB);
+
+      // ---- transposed fp16 value tile ----
+      {
+        u32x4 h[4];  // h[t][w]: bf16, then fp16, pair (dims 2w, 2w+1) of key 4 tq + t
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int key = 4 * tq + t;
+          h[t] = lds_read16(slot + (uint32_t)(key * S::ROWB + 16 * (tc ^ row_swizzle<DK>(key))));
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bool ok = 4 * tq + t < kend;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t b = h[t][w];
+            h[t][w] = ok ? f16x2_bits(__uint_as_float(b << 16), __uint_as_float(b & 0xffff0000u)) : 0u;
+          }
+        }
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          // dim 8 tc + d: keys 4 tq .. 4 tq + 3
+          const int w = d >> 1;
+          const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+          const uint32_t lo = __builtin_amdgcn_perm(h[1][w], h[0][w], sel);
+          const uint32_t hi = __builtin_amdgcn_perm(h[3][w], h[2][w], sel);
+          lds_write8(vt_lds + (uint32_t)((8 * tc + d) * MLA_VT_ROW + 8 * tq), lo, hi);
+        }
+      }
+
+      // ---- scores S^T: 2 tiles of 16 permuted keys x 16 heads ----
+      f32x4 st[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t rb = slot + (uint32_t)qk_row[kt];
+#pragma unroll
+        for (int j = 0; j < S::KS; ++j) {
+          const u32x4 kf = lds_read16(rb + (uint32_t)(16 * ((4 * j + q4) ^ qk_swz[kt])));
+          st[kt] = mfma_bf16(kf, qf[j], st[kt]);
+        }
+      }
+      // this lane's keys: 8 q4 + 4 kt + r of the tile
+      float xv[2][4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = st[kt][r] * a.scale_log2;
+          v = (8 * q4 + 4 * kt + r < kend) ? v : -INFINITY;
+          xv[kt][r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = strided_max<16>(tmax);  // over the 32 keys of the head (key 0 of the tile is always valid)
+      const bool up = tmax > m + 8.f;
+      if (__any(up)) {
+        const float alpha = up ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;
+        m = up ? tmax : m;
+        lsum *= alpha;
+#pragma unroll
+        for (int t = 0; t < DTW; ++t) {
+          o[t][0] *= alpha; o[t][1] *= alpha; o[t][2] *= alpha; o[t][3] *= alpha;
+        }
+      }
+      // p scaled by 2^7 (at most 2^15): fp16 keeps small weights normal
+      const float mb = m - 7.f;
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = __builtin_amdgcn_exp2f(xv[e >> 2][e & 3] - mb);
+        lsum += pv[e];
+      }
+      u32x4 pf;
+      pf[0] = f16x2_bits(pv[0], pv[1]);
+      pf[1] = f16x2_bits(pv[2], pv[3]);
+      pf[2] = f16x2_bits(pv[4], pv[5]);
+      pf[3] = f16x2_bits(pv[6], pv[7]);
+
+      barrier_keep_loads();  // the transposed value tile is complete
+      // ---- O^T += V^T P^T ----
+#pragma unroll
+      for (int t = 0; t < DTW; ++t) {
+        const u32x4 vf = lds_read16(pv_base + (uint32_t)(16 * t * MLA_VT_ROW));
+        o[t] = mfma_f16(vf, pf, o[t]);
+      }
+    }
+    // ---- result of the segment ----
+    const float L = strided_sum<16>(lsum);
+    const bool single = (sp0 / C) == ((sp0 + np - 1) / C);
+    const int head = 16 * hg + c16;
+    if (single) {
+      const float inv = 1.f / L;
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)s * H + head) * MLA_DV + dp * DVW + 4 * q4;
+#pragma unroll
+      for (int t = 0; t < DTW; ++t) {
+        uint2 w;
+        w.x = pack_bf16x2(o[t][0] * inv, o[t][1] * inv);
+        w.y = pack_bf16x2(o[t][2] * inv, o[t][3] * inv);
+        *reinterpret_cast<uint2*>(op + 16 * t) = w;
+      }
+    } else {
+      const size_t rec = (size_t)(blockIdx.x + s) * H + head;
+      float* op = a.part_o + rec * MLA_DV + dp * DVW + 4 * q4;
+#pragma unroll
+      for (int t = 0; t < DTW; ++t) *reinterpret_cast<f32x4*>(op + 16 * t) = o[t];
+      if (dp == 0 && q4 == 0) {
+        a.part_ml[rec * 2] = m - 7.f;
+        a.part_ml[rec * 2 + 1] = L;
+      }
+    }
+    barrier_keep_loads();  // the ring is reused by the next segment
+    x = (long long)sp0 + p1;
+  }
+}
+
+// Exact merge of a (sequence, head)'s summaries, one wave each: the
+// workgroups w0..w1 covering the sequence left theirs in slot w + s.
+template <int H>
+__global__ __launch_bounds__(256) void mla_merge(MlaArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (idx >= a.num_seqs * H) return;
+  const int s = idx / H, h = idx % H;
+  const int C = a.meta[0];
+  const int* psum = a.meta + 1;
+  const int np = psum[s + 1] - psum[s];
+  if (np == 0) {
+    for (int d = lane; d < MLA_DV; d += 64) reinterpret_cast<uint16_t*>(a.out)[((size_t)s * H + h) * MLA_DV + d] = 0;
+    return;
+  }
+  const int w0 = psum[s] / C, w1 = (psum[s] + np - 1) / C;
+  if (w0 == w1) return;  // finished in place
+  const int n = w1 - w0 + 1;
+  auto rec = [&](int i) { return (size_t)(w0 + i + s) * H + h; };
+  float M = -INFINITY;
+  for (int i = lane; i < n; i += 64) M = fmaxf(M, a.part_ml[rec(i) * 2]);
+  M = strided_max<1>(M);
+  float acc[MLA_DV / 64];
+#pragma unroll
+  for (int k = 0; k < MLA_DV / 64; ++k) acc[k] = 0.f;
+  float L = 0.f;
+  for (int i = 0; i < n; ++i) {
+    const float w = __builtin_amdgcn_exp2f(a.part_ml[rec(i) * 2] - M);
+    L += w * a.part_ml[rec(i) * 2 + 1];
+    const float* row = a.part_o + rec(i) * MLA_DV;
+#pragma unroll
+    for (int k = 0; k < MLA_DV / 64; ++k) acc[k] = fmaf(w, row[64 * k + lane], acc[k]);
+  }
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int k = 0; k < MLA_DV / 64; ++k)
+    reinterpret_cast<uint16_t*>(a.out)[((size_t)s * H + h) * MLA_DV + 64 * k + lane] = f32_to_bf16(acc[k] * inv);
+}
+
+size_t mla_workspace_bytes(int num_seqs, int num_heads, int grid) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t slots = (size_t)grid + (size_t)num_seqs;
+  return al((size_t)(num_seqs + 2) * sizeof(int)) + al(slots * num_heads * MLA_DV * sizeof(float)) +
+         al(slots * num_heads * 2 * sizeof(float));
+}
+
+void mla_bind_workspace(MlaArgs& a, void* workspace, int num_seqs, int num_heads, int grid) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t slots = (size_t)grid + (size_t)num_seqs;
+  char* ws = static_cast<char*>(workspace);
+  a.meta = reinterpret_cast<int*>(ws);
+  ws += al((size_t)(num_seqs + 2) * sizeof(int));
+  a.part_o = reinterpret_cast<float*>(ws);
+  ws += al(slots * num_heads * MLA_DV * sizeof(float));
+  a.part_ml = reinterpret_cast<float*>(ws);
+}
+
+int mla_max_seqs() { return kMlaMaxSeqs; }
+
+template <int DK, int H>
+static hipError_t run_mla(const MlaArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((mla_decode_split<DK, H>), dim3((unsigned)grid), dim3(MLA_NT), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((mla_merge<H>), dim3((unsigned)((a.num_seqs * H + 3) / 4)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_decode(const MlaArgs& a, int head_dim_k, int grid, hipStream_t st) {
+  const int H = a.num_heads;
+  if (head_dim_k == 576) {
+    if (H == 16) return run_mla<576, 16>(a, grid, st);
+    if (H == 32) return run_mla<576, 32>(a, grid, st);
+    if (H == 64) return run_mla<576, 64>(a, grid, st);
+    if (H == 128) return run_mla<576, 128>(a, grid, st);
+  } else if (head_dim_k == 512) {
+    if (H == 16) return run_mla<512, 16>(a, grid, st);
+    if (H == 32) return run_mla<512, 32>(a, grid, st);
+    if (H == 64) return run_mla<512, 64>(a, grid, st);
+    if (H == 128) return run_mla<512, 128>(a, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

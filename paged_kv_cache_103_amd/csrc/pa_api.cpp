@@ -268,6 +268,60 @@ pa_status pa_decode_partial(void* out, float* lse, const void* query, const void
                      num_blocks, q_dtype, cache_dtype, scale, 0, workspace, workspace_bytes, stream);
 }
 
+size_t pa_mla_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads) {
+  if (num_seqs <= 0 || num_heads <= 0) return 0;
+  return pa::mla_workspace_bytes(num_seqs, num_heads, pa::device_cu_count());
+}
+
+pa_status pa_mla_decode(void* out, const void* query, const void* latent_cache, const int32_t* block_table,
+                        int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                        int32_t max_context_len, int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+                        int32_t block_size, int32_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype, float scale,
+                        void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  if (num_seqs < 0 || num_seqs > pa::mla_max_seqs())
+    return fail(PA_ERR_UNSUPPORTED, "num_seqs must be in [0, %d] (got %d)", pa::mla_max_seqs(), num_seqs);
+  if (block_size != PA_BLOCK_SIZE)
+    return fail(PA_ERR_UNSUPPORTED, "block_size must be %d (got %d)", PA_BLOCK_SIZE, block_size);
+  if (head_dim_v != 512) return fail(PA_ERR_UNSUPPORTED, "head_dim_v must be 512 (got %d)", head_dim_v);
+  if (head_dim_k != 512 && head_dim_k != 576)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim_k must be 512 or 576 (got %d)", head_dim_k);
+  if (num_heads != 16 && num_heads != 32 && num_heads != 64 && num_heads != 128)
+    return fail(PA_ERR_UNSUPPORTED, "num_heads must be 16, 32, 64 or 128 (got %d)", num_heads);
+  if (q_dtype != PA_BF16 || cache_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "latent decode takes bf16 queries and a bf16 cache");
+  if (!(scale > 0.0f) || scale != scale) return fail(PA_ERR_INVALID_ARGUMENT, "scale must be a positive number");
+  if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks must be > 0 (got %d)", num_blocks);
+  if (num_seqs == 0) {
+    g_last_error.clear();
+    return PA_OK;
+  }
+  if (max_context_len <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_context_len must be > 0 (got %d)", max_context_len);
+  if (block_table_stride < (max_context_len + 15) / 16)
+    return fail(PA_ERR_INVALID_ARGUMENT, "block_table_stride (%d) is smaller than ceil(max_context_len/16) (%d)",
+                block_table_stride, (max_context_len + 15) / 16);
+  if (!out || !query || !latent_cache || !block_table || !context_lens)
+    return fail(PA_ERR_INVALID_ARGUMENT, "null device pointer");
+  const int grid = pa::device_cu_count();
+  const size_t need = pa::mla_workspace_bytes(num_seqs, num_heads, grid);
+  if (workspace_bytes < need || workspace == nullptr)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "latent decode needs %zu workspace bytes (got %zu)", need,
+                workspace_bytes);
+  pa::MlaArgs a{};
+  a.out = out;
+  a.query = query;
+  a.cache = latent_cache;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  pa::mla_bind_workspace(a, workspace, num_seqs, num_heads, grid);
+  a.bt_stride = block_table_stride;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pa::launch_mla_decode(a, head_dim_k, grid, (hipStream_t)stream);
+  return hip_status(e, "latent decode launch");
+}
+
 pa_status pa_merge_partials(void* out, float* lse_out, const void* parts, const float* parts_lse, int32_t num_parts,
                             int32_t num_rows, int32_t head_size, pa_dtype dtype, pa_stream_t stream) {
   if (num_parts < 1) return fail(PA_ERR_INVALID_ARGUMENT, "num_parts must be >= 1 (got %d)", num_parts);

@@ -112,6 +112,27 @@ constexpr size_t kSparseMaxLds = 64 * 1024;  // bitmap + scan: contexts up to 8,
 size_t sparse_select_lds_bytes(int max_context_len);
 hipError_t launch_sparse_select(const SparseSelectArgs& a, int num_seqs, hipStream_t stream);
 
+// Decode over a paged latent (MLA) cache: [num_blocks][16][head_dim_k] bf16
+// rows shared by all heads; values are the rows' first 512 elements.
+struct MlaArgs {
+  void* out;            // bf16 [num_seqs][num_heads][512]
+  const void* query;    // bf16 [num_seqs][num_heads][head_dim_k]
+  const void* cache;
+  const int* block_table;
+  const int* context_lens;
+  float* part_o;        // [grid + num_seqs][num_heads][512]
+  float* part_ml;       // [grid + num_seqs][num_heads][2]
+  int* meta;            // [0] = pairs per workgroup, [1 + s] = pair prefix sums
+  int bt_stride;
+  int num_seqs;
+  int num_heads;
+  float scale_log2;
+};
+size_t mla_workspace_bytes(int num_seqs, int num_heads, int grid);
+void mla_bind_workspace(MlaArgs& a, void* workspace, int num_seqs, int num_heads, int grid);
+int mla_max_seqs();
+hipError_t launch_mla_decode(const MlaArgs& a, int head_dim_k, int grid, hipStream_t stream);
+
 // Merge of per-range attention results (o_r, lse_r) into one.
 hipError_t launch_merge_lse(void* out, float* lse_out, const void* parts, const float* parts_lse, int num_parts,
                             int num_rows, int head_size, int kind, hipStream_t stream);

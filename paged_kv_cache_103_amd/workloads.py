@@ -368,6 +368,67 @@ def make_sparse_batch(name: str, seed: int, ctx_lens: Sequence[int], k_blocks: i
     return batch, SparseChoice(selected, num_selected, chosen)
 
 
+@dataclass
+class MlaBatch:
+    """Decode batch over a paged latent (MLA) cache."""
+    name: str
+    num_heads: int
+    head_dim_k: int
+    scale: float
+    context_lens: np.ndarray   # int32 [S]
+    block_table: np.ndarray    # int32 [S][stride]
+    query: torch.Tensor        # bf16 [S][H][dk]
+    cache: torch.Tensor        # bf16 [NB][16][dk]
+
+    @property
+    def num_seqs(self) -> int:
+        return int(len(self.context_lens))
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max())
+
+    def latent_bytes_read(self) -> int:
+        """Algorithmic bytes one decode reads: every cached row once (shared by
+        all heads), plus the queries."""
+        return int(self.context_lens.sum()) * self.head_dim_k * 2 + self.query.numel() * 2
+
+
+def make_mla_batch(name: str, seed: int, ctx_lens: Sequence[int], num_heads: int, head_dim_k: int,
+                   device="cpu", extra_blocks: int = 0, scale: Optional[float] = None,
+                   chunk_blocks: int = 16384) -> MlaBatch:
+    """Latent rows and absorbed queries ~ N(0, 1) rounded to bf16; block ids a
+    seeded permutation of the pool; every slot no sequence owns is NaN."""
+    rng = np.random.default_rng(seed)
+    ctx_lens = [int(c) for c in ctx_lens]
+    table, NB, used = _assign_blocks(rng, ctx_lens, (), {}, extra_blocks, None)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    cache = torch.empty((NB, BLOCK, head_dim_k), dtype=torch.bfloat16, device=device)
+    for b0 in range(0, NB, chunk_blocks):
+        b1 = min(NB, b0 + chunk_blocks)
+        cache[b0:b1] = torch.randn((b1 - b0, BLOCK, head_dim_k), generator=gen, device=device).to(torch.bfloat16)
+    owned = torch.zeros((NB, BLOCK), dtype=torch.bool)
+    owned[torch.from_numpy(np.asarray(used, dtype=np.int64))] = True
+    for s, c in enumerate(ctx_lens):
+        if c % BLOCK:
+            owned[int(table[s, (c - 1) // BLOCK]), c % BLOCK:] = False
+    cache.masked_fill_(~owned.to(device)[:, :, None], float("nan"))
+    query = torch.randn((len(ctx_lens), num_heads, head_dim_k), generator=gen, device=device).to(torch.bfloat16)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim_k)
+    return MlaBatch(name, num_heads, head_dim_k, float(scale), np.asarray(ctx_lens, dtype=np.int32), table, query,
+                    cache)
+
+
+def make_mla_config(device="cpu") -> MlaBatch:
+    """Latent-cache decode shaped like the pages' MLA models: 64 sequences,
+    contexts U{4096..32768}, 128 heads, rows of 576 (512 latent + 64), bf16."""
+    rng = np.random.default_rng(7)
+    ctx = rng.integers(4096, 32769, 64).tolist()
+    return make_mla_batch("mla_decode", 7, ctx, 128, 576, device=device)
+
+
 def make_sparse_config(device="cpu"):
     """Long-context sparse decode: 64 sequences, contexts U{32768..524288},
     128 chosen blocks (2048 keys) plus the newest block each, 32/8 heads,

@@ -294,3 +294,29 @@ def test_partial_decode_and_merge_reject_bad_arguments(lib):
     assert merge(parts=None) == 1
     assert merge(parts_lse=None) == 1
     assert merge(rows=0, out=None, parts=None, parts_lse=None) == 0
+
+
+def test_mla_decode_rejects_bad_arguments(lib):
+    L = lib.load()
+
+    def call(**over):
+        a = dict(out=1, query=1, cache=1, bt=1, bt_stride=8, ctx=1, S=2, max_ctx=100, H=128, dk=576, dv=512, B=16,
+                 NB=10, qd=1, cd=1, scale=0.1, ws=1, ws_bytes=1 << 30)
+        a.update(over)
+        return L.pa_mla_decode(a["out"], a["query"], a["cache"], a["bt"], a["bt_stride"], a["ctx"], a["S"],
+                               a["max_ctx"], a["H"], a["dk"], a["dv"], a["B"], a["NB"], a["qd"], a["cd"], a["scale"],
+                               a["ws"], a["ws_bytes"], None)
+
+    assert call(H=48) == 2
+    assert call(dk=640) == 2
+    assert call(dv=256) == 2
+    assert call(cd=2) == 2
+    assert call(B=32) == 2
+    assert call(S=4096) == 2
+    assert call(bt_stride=2) == 1
+    assert call(cache=None) == 1
+    assert call(scale=0.0) == 1
+    assert call(ws_bytes=64) == 3
+    assert call(S=0) == 0
+    assert L.pa_mla_decode_workspace_bytes(0, 128) == 0
+    assert L.pa_mla_decode_workspace_bytes(64, 128) > 64 * 128 * 512 * 4
