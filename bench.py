@@ -181,6 +181,36 @@ def run_context_parallel(pa, torch, W, ranks, steps, warmup):
     return res
 
 
+def run_mla(pa, torch, W, steps, warmup, num_heads=128, head_dim_k=576):
+    """Latent-cache (MLA) decode: 64 sequences, contexts U{4096..32768}."""
+    import numpy as np
+    if num_heads == 128 and head_dim_k == 576:
+        b = W.make_mla_config(device="cuda")
+    else:
+        ctx = np.random.default_rng(7).integers(4096, 32769, 64).tolist()
+        b = W.make_mla_batch(f"mla_{num_heads}_{head_dim_k}", 7, ctx, num_heads, head_dim_k, device="cuda")
+    S, H = b.num_seqs, b.num_heads
+    out = torch.empty((S, H, 512), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(pa.mla_decode_workspace_bytes(S, H), 1), dtype=torch.uint8, device="cuda")
+    bt = torch.from_numpy(b.block_table).to("cuda")
+    cl = torch.from_numpy(b.context_lens).to("cuda")
+    torch.cuda.synchronize()
+
+    def attend():
+        pa.mla_decode(out, b.query, b.cache, bt, cl, b.max_context_len, b.scale, ws)
+
+    _, ms, _ = time_steps(torch, lambda: None, attend, steps, warmup)
+    keys = int(b.context_lens.sum())
+    nbytes = b.latent_bytes_read()
+    flops = 2.0 * H * (b.head_dim_k + 512) * keys
+    res = {"attend_ms": round(ms, 5), "bytes_per_call": nbytes, "flops_per_call": flops,
+           "gbs": round(nbytes / (ms * 1e-3) / 1e9, 2), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+           "num_heads": H, "head_dim_k": b.head_dim_k}
+    del b
+    torch.cuda.empty_cache()
+    return res
+
+
 def prefill_step_fns(pa, torch, b):
     m = b.meta("cuda")
     out = torch.empty_like(b.query)
@@ -456,8 +486,18 @@ def main():
     del sb
     torch.cuda.empty_cache()
 
+    # ---- decode over a paged latent (MLA) cache ----
+    ml = run_mla(pa, torch, W, max(10, args.steps // 2), args.warmup)
+    log(f"mla_decode (128 heads, rows of 576): {ml['attend_ms']*1e3:.1f} us, {ml['gbs']:.0f} GB/s of latent rows, "
+        f"{ml['tflops']:.0f} TFLOP/s")
+
     extra = {}
     if args.extra:
+        for h, dk in ((64, 576), (128, 512), (16, 576)):
+            r = run_mla(pa, torch, W, max(10, args.steps // 2), args.warmup, h, dk)
+            extra[f"mla_decode_{h}h_{dk}"] = r
+            log(f"mla_decode ({h} heads, rows of {dk}): {r['attend_ms']*1e3:.1f} us, {r['gbs']:.0f} GB/s, "
+                f"{r['tflops']:.0f} TFLOP/s")
         # the sparse decode's time against the context length at a fixed choice
         sweep = {}
         for ctx in (8192, 65536, 524288):
@@ -534,6 +574,14 @@ def main():
                                                 "probe": "libpa_peaks: back-to-back independent 32x32x16 "
                                                          "bf16 MFMAs, 8 waves per CU",
                                                 "fp16_tflops": ceil["mfma_fp16_tflops"]}}},
+        "mla_decode": {"value": ml["gbs"], "unit": "GB/s", "attend_ms": ml["attend_ms"],
+                       "workload": "64 sequences, context U{4096..32768}, 128 heads sharing one latent row per "
+                                   "token (512 latent + 64, bf16), absorbed queries; pa_mla_decode",
+                       "bytes_per_call": ml["bytes_per_call"], "flops_per_call": ml["flops_per_call"],
+                       "roofline": {"bound": "hbm", "achieved": ml["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(ml["gbs"] / HBM_PEAK_GBS, 4),
+                                    "mfma_tflops": ml["tflops"],
+                                    "mfma_frac": round(ml["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)}},
         "sparse_decode": {"value": round(sp["kv_gbs_attend"], 2), "unit": "GB/s", "attend_ms": round(sp["attend_ms"], 5),
                           "step_ms": round(sp["step_ms"], 5),
                           "workload": "64 sequences, context U{32768..524288}, 128 chosen blocks (2048 keys) + "

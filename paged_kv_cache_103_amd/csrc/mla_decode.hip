@@ -44,8 +44,6 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int MLA_NW = 8;
-constexpr int MLA_NT = 64 * MLA_NW;
 constexpr int MLA_DV = 512;
 constexpr int MLA_VT_ROW = 80;  // bytes per transposed value row (64 data + 16 pad)
 
@@ -112,30 +110,36 @@ __device__ __forceinline__ void lds_write8(uint32_t addr, uint32_t lo, uint32_t 
 
 }  // namespace
 
-template <int DK>
+template <int DK, int NW>
 struct MlaShape {
+  static constexpr int NT = 64 * NW;
   static constexpr int ROWB = DK * 2;            // bytes of one cached row
   static constexpr int BLKB = 16 * ROWB;         // bytes of one block
   static constexpr int TILEB = 32 * ROWB;        // bytes of one 32-key tile
   static constexpr int PIECES = TILEB / 1024;    // 1 KiB copies per tile (36 or 32)
-  static constexpr int MAXP = (PIECES + MLA_NW - 1) / MLA_NW;  // copies per wave (5 or 4)
+  static constexpr int MAXP = (PIECES + NW - 1) / NW;  // copies per wave
   static constexpr int KS = DK / 32;             // score k-steps
   static constexpr int SLOTS = 3;
+  static constexpr int TITEMS = 8 * (MLA_DV / 8);  // transposition items: (key quad, 8-dim chunk)
 };
 
 constexpr int kMlaMaxSeqs = 2048;
 
-template <int DK, int H>
-__global__ __launch_bounds__(MLA_NT) void mla_decode_split(MlaArgs a) {
-  using S = MlaShape<DK>;
-  constexpr int NHG = H / 16;          // head groups
-  constexpr int NDP = MLA_NW / NHG;    // value-dim parts
+// NW waves; each wave serves HG groups of 16 heads (the groups share every
+// LDS operand fragment) and DVW of the 512 value dims.
+template <int DK, int H, int NW, int HG>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void mla_decode_split(MlaArgs a) {
+  using S = MlaShape<DK, NW>;
+  constexpr int NT = S::NT;
+  constexpr int NHG = H / (16 * HG);   // head groups of the workgroup
+  static_assert(NHG >= 1 && NW % NHG == 0, "waves must cover the heads");
+  constexpr int NDP = NW / NHG;        // value-dim parts
   constexpr int DVW = MLA_DV / NDP;    // value dims per wave
   constexpr int DTW = DVW / 16;        // 16-dim output tiles per wave
   __shared__ __attribute__((aligned(16))) uint8_t ring[S::SLOTS * S::TILEB];
   __shared__ __attribute__((aligned(16))) uint8_t vt[MLA_DV * MLA_VT_ROW];
   __shared__ int psum[kMlaMaxSeqs + 1];
-  __shared__ int scan[MLA_NT];
+  __shared__ int scan[NT];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -146,20 +150,20 @@ __global__ __launch_bounds__(MLA_NT) void mla_decode_split(MlaArgs a) {
   // ---- pairs of blocks per sequence, prefix sums (all threads) ----
   {
     int running = 0;
-    for (int base = 0; base < NS; base += MLA_NT) {
+    for (int base = 0; base < NS; base += NT) {
       const int i = base + tid;
       const int ctx = i < NS ? a.context_lens[i] : 0;
       const int n = ctx > 0 ? (((ctx + 15) >> 4) + 1) >> 1 : 0;
       scan[tid] = n;
       __syncthreads();
-      for (int off = 1; off < MLA_NT; off <<= 1) {
+      for (int off = 1; off < NT; off <<= 1) {
         const int v = tid >= off ? scan[tid - off] : 0;
         __syncthreads();
         scan[tid] += v;
         __syncthreads();
       }
       if (i < NS) psum[i] = running + scan[tid] - n;
-      running += scan[MLA_NT - 1];
+      running += scan[NT - 1];
       __syncthreads();
     }
     if (tid == 0) psum[NS] = running;
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(MLA_NT) void mla_decode_split(MlaArgs a) {
   const int C = max(1, (T + (int)gridDim.x - 1) / (int)gridDim.x);
   if (blockIdx.x == 0) {
     if (tid == 0) a.meta[0] = C;
-    for (int i = tid; i <= NS; i += MLA_NT) a.meta[1 + i] = psum[i];
+    for (int i = tid; i <= NS; i += NT) a.meta[1 + i] = psum[i];
   }
 
   // ---- per-lane constant offsets ----
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(MLA_NT) void mla_decode_split(MlaArgs a) {
     const int row = P / S::ROWB, pch = (P % S::ROWB) / 16;
     return (uint32_t)((row & 15) * S::ROWB + 16 * (pch ^ row_swizzle<DK>(row)));
   };
-  const int npieces = (S::PIECES - wave + MLA_NW - 1) / MLA_NW;  // 5 or 4 (uniform per wave)
+  const int npieces = (S::PIECES - wave + NW - 1) / NW;  // uniform per wave
   const uint32_t ring_lds = lds_addr(ring), vt_lds = lds_addr(vt);
   // score operand rows: tile kt, MFMA row c16 holds key 8 (c16 / 4) + 4 kt + c16 % 4
   int qk_row[2], qk_swz[2];
@@ -190,8 +194,6 @@ __global__ __launch_bounds__(MLA_NT) void mla_decode_split(MlaArgs a) {
     qk_row[kt] = key * S::ROWB;
     qk_swz[kt] = row_swizzle<DK>(key);
   }
-  // transposition pass: thread = (key quad kq, value chunk c)
-  const int tq = lane & 7, tc = 8 * wave + (lane >> 3);
   // value operand rows: dim dp * DVW + 16 dt + c16, keys 8 q4 .. 8 q4 + 7
   const uint32_t pv_base = vt_lds + (uint32_t)((dp * DVW + c16) * MLA_VT_ROW + 16 * q4);
 
@@ -219,18 +221,26 @@ __global__ __launch_bounds__(MLA_NT) void mla_decode_split(MlaArgs a) {
     const int nblk = (ctx + 15) >> 4;
     const cint* bt = (const cint*)(a.block_table + (size_t)s * a.bt_stride);
 
-    // queries of this wave's 16 heads (B operand of the score product)
-    u32x4 qf[S::KS];
-    {
-      const uint8_t* qp =
-          reinterpret_cast<const uint8_t*>(a.query) + ((size_t)s * H + 16 * hg + c16) * S::ROWB + 16 * q4;
+    // queries of this wave's heads (B operand of the score product)
+    u32x4 qf[HG][S::KS];
 #pragma unroll
-      for (int j = 0; j < S::KS; ++j) qf[j] = load16(qp + 64 * j);
+    for (int g = 0; g < HG; ++g) {
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.query) +
+                          ((size_t)s * H + 16 * (HG * hg + g) + c16) * S::ROWB + 16 * q4;
+#pragma unroll
+      for (int j = 0; j < S::KS; ++j) qf[g][j] = load16(qp + 64 * j);
     }
-    f32x4 o[DTW];
+    f32x4 o[HG][DTW];
 #pragma unroll
-    for (int t = 0; t < DTW; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, lsum = 0.f;
+    for (int g = 0; g < HG; ++g)
+#pragma unroll
+      for (int t = 0; t < DTW; ++t) o[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m[HG], lsum[HG];
+#pragma unroll
+    for (int g = 0; g < HG; ++g) {
+      m[g] = -INFINITY;
+      lsum[g] = 0.f;
+    }
 
     auto issue = [&](int i) {  // copies of the segment's pair i into slot i % 3
       const int pb = 2 * (p0 + i);
@@ -240,7 +250,7 @@ __global__ __launch_bounds__(MLA_NT) void mla_decode_split(MlaArgs a) {
 #pragma unroll
       for (int c = 0; c < S::MAXP; ++c) {
         if (c < npieces) {
-          const int k = wave + MLA_NW * c;
+          const int k = wave + NW * c;
           const int blk = k < S::PIECES / 2 ? b0 : b1;
           dma16(cache + (size_t)(uint32_t)blk * S::BLKB, src_off(k), slot + 1024u * (uint32_t)k);
         }
@@ -263,8 +273,10 @@ __global__ __launch_bounds__(MLA_NT) void mla_decode_split(MlaArgs a) {
       const int kend = ctx - key0;  // keys of this tile at or past kend are masked
       const uint32_t slot = ring_lds + (uint32_t)((i % S::SLOTS) * S::TILEB);
 
-      // ---- transposed fp16 value tile ----
-      {
+      // ---- transposed fp16 value tile: item = (key quad tq, 8-dim chunk tc) ----
+#pragma unroll
+      for (int it = tid; it < S::TITEMS; it += NT) {
+        const int tq = it & 7, tc = it >> 3;
         u32x4 h[4];  // h[t][w]: bf16, then fp16, pair (dims 2w, 2w+1) of key 4 tq + t
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -285,91 +297,100 @@ __global__ __launch_bounds__(MLA_NT) void mla_decode_split(MlaArgs a) {
           // dim 8 tc + d: keys 4 tq .. 4 tq + 3
           const int w = d >> 1;
           const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
-          const uint32_t lo = __builtin_amdgcn_perm(h[1][w], h[0][w], sel);
-          const uint32_t hi = __builtin_amdgcn_perm(h[3][w], h[2][w], sel);
-          lds_write8(vt_lds + (uint32_t)((8 * tc + d) * MLA_VT_ROW + 8 * tq), lo, hi);
+          const uint32_t lo2 = __builtin_amdgcn_perm(h[1][w], h[0][w], sel);
+          const uint32_t hi2 = __builtin_amdgcn_perm(h[3][w], h[2][w], sel);
+          lds_write8(vt_lds + (uint32_t)((8 * tc + d) * MLA_VT_ROW + 8 * tq), lo2, hi2);
         }
       }
 
-      // ---- scores S^T: 2 tiles of 16 permuted keys x 16 heads ----
-      f32x4 st[2];
+      // ---- scores S^T: per head group, 2 tiles of 16 permuted keys x 16 heads ----
+      f32x4 st[HG][2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < HG; ++g) st[g][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const uint32_t rb = slot + (uint32_t)qk_row[kt];
 #pragma unroll
         for (int j = 0; j < S::KS; ++j) {
           const u32x4 kf = lds_read16(rb + (uint32_t)(16 * ((4 * j + q4) ^ qk_swz[kt])));
-          st[kt] = mfma_bf16(kf, qf[j], st[kt]);
+#pragma unroll
+          for (int g = 0; g < HG; ++g) st[g][kt] = mfma_bf16(kf, qf[g][j], st[g][kt]);
         }
       }
-      // this lane's keys: 8 q4 + 4 kt + r of the tile
-      float xv[2][4];
-      float tmax = -INFINITY;
+      u32x4 pf[HG];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int g = 0; g < HG; ++g) {
+        // this lane's keys: 8 q4 + 4 kt + r of the tile
+        float xv[2][4];
+        float tmax = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = st[kt][r] * a.scale_log2;
-          v = (8 * q4 + 4 * kt + r < kend) ? v : -INFINITY;
-          xv[kt][r] = v;
-          tmax = fmaxf(tmax, v);
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float v = st[g][kt][r] * a.scale_log2;
+            v = (8 * q4 + 4 * kt + r < kend) ? v : -INFINITY;
+            xv[kt][r] = v;
+            tmax = fmaxf(tmax, v);
+          }
+        tmax = strided_max<16>(tmax);  // key 0 of the tile is always valid
+        const bool up = tmax > m[g] + 8.f;
+        if (__any(up)) {
+          const float alpha = up ? __builtin_amdgcn_exp2f(m[g] - tmax) : 1.f;
+          m[g] = up ? tmax : m[g];
+          lsum[g] *= alpha;
+#pragma unroll
+          for (int t = 0; t < DTW; ++t) {
+            o[g][t][0] *= alpha; o[g][t][1] *= alpha; o[g][t][2] *= alpha; o[g][t][3] *= alpha;
+          }
         }
-      tmax = strided_max<16>(tmax);  // over the 32 keys of the head (key 0 of the tile is always valid)
-      const bool up = tmax > m + 8.f;
-      if (__any(up)) {
-        const float alpha = up ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;
-        m = up ? tmax : m;
-        lsum *= alpha;
+        // p scaled by 2^7 (at most 2^15): fp16 keeps small weights normal
+        const float mb = m[g] - 7.f;
+        float pv[8];
 #pragma unroll
-        for (int t = 0; t < DTW; ++t) {
-          o[t][0] *= alpha; o[t][1] *= alpha; o[t][2] *= alpha; o[t][3] *= alpha;
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(xv[e >> 2][e & 3] - mb);
+          lsum[g] += pv[e];
         }
+        pf[g][0] = f16x2_bits(pv[0], pv[1]);
+        pf[g][1] = f16x2_bits(pv[2], pv[3]);
+        pf[g][2] = f16x2_bits(pv[4], pv[5]);
+        pf[g][3] = f16x2_bits(pv[6], pv[7]);
       }
-      // p scaled by 2^7 (at most 2^15): fp16 keeps small weights normal
-      const float mb = m - 7.f;
-      float pv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pv[e] = __builtin_amdgcn_exp2f(xv[e >> 2][e & 3] - mb);
-        lsum += pv[e];
-      }
-      u32x4 pf;
-      pf[0] = f16x2_bits(pv[0], pv[1]);
-      pf[1] = f16x2_bits(pv[2], pv[3]);
-      pf[2] = f16x2_bits(pv[4], pv[5]);
-      pf[3] = f16x2_bits(pv[6], pv[7]);
 
       barrier_keep_loads();  // the transposed value tile is complete
       // ---- O^T += V^T P^T ----
 #pragma unroll
       for (int t = 0; t < DTW; ++t) {
         const u32x4 vf = lds_read16(pv_base + (uint32_t)(16 * t * MLA_VT_ROW));
-        o[t] = mfma_f16(vf, pf, o[t]);
+#pragma unroll
+        for (int g = 0; g < HG; ++g) o[g][t] = mfma_f16(vf, pf[g], o[g][t]);
       }
     }
     // ---- result of the segment ----
-    const float L = strided_sum<16>(lsum);
     const bool single = (sp0 / C) == ((sp0 + np - 1) / C);
-    const int head = 16 * hg + c16;
-    if (single) {
-      const float inv = 1.f / L;
-      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)s * H + head) * MLA_DV + dp * DVW + 4 * q4;
 #pragma unroll
-      for (int t = 0; t < DTW; ++t) {
-        uint2 w;
-        w.x = pack_bf16x2(o[t][0] * inv, o[t][1] * inv);
-        w.y = pack_bf16x2(o[t][2] * inv, o[t][3] * inv);
-        *reinterpret_cast<uint2*>(op + 16 * t) = w;
-      }
-    } else {
-      const size_t rec = (size_t)(blockIdx.x + s) * H + head;
-      float* op = a.part_o + rec * MLA_DV + dp * DVW + 4 * q4;
+    for (int g = 0; g < HG; ++g) {
+      const float L = strided_sum<16>(lsum[g]);
+      const int head = 16 * (HG * hg + g) + c16;
+      if (single) {
+        const float inv = 1.f / L;
+        uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)s * H + head) * MLA_DV + dp * DVW + 4 * q4;
 #pragma unroll
-      for (int t = 0; t < DTW; ++t) *reinterpret_cast<f32x4*>(op + 16 * t) = o[t];
-      if (dp == 0 && q4 == 0) {
-        a.part_ml[rec * 2] = m - 7.f;
-        a.part_ml[rec * 2 + 1] = L;
+        for (int t = 0; t < DTW; ++t) {
+          uint2 w;
+          w.x = pack_bf16x2(o[g][t][0] * inv, o[g][t][1] * inv);
+          w.y = pack_bf16x2(o[g][t][2] * inv, o[g][t][3] * inv);
+          *reinterpret_cast<uint2*>(op + 16 * t) = w;
+        }
+      } else {
+        const size_t rec = (size_t)(blockIdx.x + s) * H + head;
+        float* op = a.part_o + rec * MLA_DV + dp * DVW + 4 * q4;
+#pragma unroll
+        for (int t = 0; t < DTW; ++t) *reinterpret_cast<f32x4*>(op + 16 * t) = o[g][t];
+        if (dp == 0 && q4 == 0) {
+          a.part_ml[rec * 2] = m[g] - 7.f;
+          a.part_ml[rec * 2 + 1] = L;
+        }
       }
     }
     barrier_keep_loads();  // the ring is reused by the next segment
@@ -438,7 +459,11 @@ int mla_max_seqs() { return kMlaMaxSeqs; }
 
 template <int DK, int H>
 static hipError_t run_mla(const MlaArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((mla_decode_split<DK, H>), dim3((unsigned)grid), dim3(MLA_NT), 0, st, a);
+  // 8 waves of one 16-head group each. (Four waves of two groups, which
+  // halves the LDS operand reads, measured slower: one wave per SIMD hides
+  // the LDS latency worse, and at 128 heads the registers spill.)
+  constexpr int NW = 8, HG = 1;
+  hipLaunchKernelGGL((mla_decode_split<DK, H, NW, HG>), dim3((unsigned)grid), dim3(64 * NW), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((mla_merge<H>), dim3((unsigned)((a.num_seqs * H + 3) / 4)), dim3(256), 0, st, a);
