@@ -411,7 +411,7 @@ def main():
     ap.add_argument("--profile-pass", action="store_true",
                     help="only the kernels a counter run needs: a plain 1 GiB device copy (the "
                          "calibration kernel for FETCH_SIZE/WRITE_SIZE), a few decode and mixed steps, "
-                         "the mixed step's chunk alone and a few sparse decode calls")
+                         "the mixed step's chunk alone, a few sparse decode calls and latent-cache decode calls")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
@@ -454,6 +454,7 @@ def main():
             sp_attend()
         torch.cuda.synchronize()
         del sb
+        run_mla(pa, torch, W, 3, 0)
         log("profile pass done")
         return
 
