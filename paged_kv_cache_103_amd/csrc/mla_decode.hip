@@ -94,6 +94,16 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t lane_offset, ui
       : "memory");
 }
 
+// The lane id, recomputed where it is used: the compiler cannot hoist a
+// volatile asm out of the loop, so values derived from it are rematerialised
+// instead of being kept live (or spilled, and a spill reload waits for every
+// copy in flight).
+__device__ __forceinline__ int lane_id_here() {
+  int l;
+  __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 template <typename T>
 __device__ __forceinline__ uint32_t lds_addr(const T* p) {
   typedef __attribute__((address_space(3))) const T lds_t;
@@ -179,23 +189,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // ---- per-lane constant offsets ----
   // copies: piece k of a tile = bytes [1024 k, 1024 k + 1024), wholly inside
   // block k / (PIECES / 2); this lane's source offset inside that block
-  auto src_off = [&](int k) {
-    const int P = 1024 * k + 16 * lane;
+  auto src_off = [&](int k, int ln) {
+    const int P = 1024 * k + 16 * ln;
     const int row = P / S::ROWB, pch = (P % S::ROWB) / 16;
     return (uint32_t)((row & 15) * S::ROWB + 16 * (pch ^ row_swizzle<DK>(row)));
   };
   const int npieces = (S::PIECES - wave + NW - 1) / NW;  // uniform per wave
   const uint32_t ring_lds = lds_addr(ring), vt_lds = lds_addr(vt);
   // score operand rows: tile kt, MFMA row c16 holds key 8 (c16 / 4) + 4 kt + c16 % 4
-  int qk_row[2], qk_swz[2];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const int key = 8 * (c16 >> 2) + 4 * kt + (c16 & 3);
-    qk_row[kt] = key * S::ROWB;
-    qk_swz[kt] = row_swizzle<DK>(key);
-  }
-  // value operand rows: dim dp * DVW + 16 dt + c16, keys 8 q4 .. 8 q4 + 7
-  const uint32_t pv_base = vt_lds + (uint32_t)((dp * DVW + c16) * MLA_VT_ROW + 16 * q4);
+  // (addresses computed in the loop); value operand rows: dim dp * DVW +
+  // 16 dt + c16, keys 8 q4 .. 8 q4 + 7
 
   const uint8_t* cache = reinterpret_cast<const uint8_t*>(a.cache);
   const long long x_end = min<long long>((long long)(blockIdx.x + 1) * C, T);
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
       lsum[g] = 0.f;
     }
 
-    auto issue = [&](int i) {  // copies of the segment's pair i into slot i % 3
+    auto issue = [&](int i, int ln) {  // copies of the segment's pair i into slot i % 3
       const int pb = 2 * (p0 + i);
       const int b0 = bt[pb];
       const int b1 = pb + 1 < nblk ? bt[pb + 1] : b0;
@@ -252,12 +255,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
         if (c < npieces) {
           const int k = wave + NW * c;
           const int blk = k < S::PIECES / 2 ? b0 : b1;
-          dma16(cache + (size_t)(uint32_t)blk * S::BLKB, src_off(k), slot + 1024u * (uint32_t)k);
+          dma16(cache + (size_t)(uint32_t)blk * S::BLKB, src_off(k, ln), slot + 1024u * (uint32_t)k);
         }
       }
     };
-    issue(0);
-    if (n > 1) issue(1);
+    // the queries have landed before any copy is issued: the compiler cannot
+    // count the copies, and a wait it placed for the queries inside the loop
+    // would drain every copy in flight each step
+    wait_vm<0>();
+    issue(0, lane);
+    if (n > 1) issue(1, lane);
 
     for (int i = 0; i < n; ++i) {
       // the copies of pair i have landed (those of pair i + 1 may be in flight)
@@ -268,14 +275,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
         wait_vm<0>();
       }
       barrier_keep_loads();  // every wave is done with pair i - 1
-      if (i + 2 < n) issue(i + 2);
+      // with 128 heads the registers are full: lane-derived addresses are
+      // recomputed once per step (see lane_id_here) instead of kept live
+      const int ln = H >= 128 ? lane_id_here() : lane;
+      if (i + 2 < n) issue(i + 2, ln);
       const int key0 = 32 * (p0 + i);
       const int kend = ctx - key0;  // keys of this tile at or past kend are masked
       const uint32_t slot = ring_lds + (uint32_t)((i % S::SLOTS) * S::TILEB);
 
       // ---- transposed fp16 value tile: item = (key quad tq, 8-dim chunk tc) ----
 #pragma unroll
-      for (int it = tid; it < S::TITEMS; it += NT) {
+      for (int it0 = 0; it0 < S::TITEMS; it0 += NT) {
+        const int it = it0 + 64 * wave + ln;
         const int tq = it & 7, tc = it >> 3;
         u32x4 h[4];  // h[t][w]: bf16, then fp16, pair (dims 2w, 2w+1) of key 4 tq + t
 #pragma unroll
@@ -309,10 +320,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int g = 0; g < HG; ++g) st[g][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint32_t rb = slot + (uint32_t)qk_row[kt];
+        const int r16 = ln & 15, rq = ln >> 4;
+        const int key = 8 * (r16 >> 2) + 4 * kt + (r16 & 3);
+        const uint32_t rb = slot + (uint32_t)(key * S::ROWB);
+        const int swz = row_swizzle<DK>(key);
 #pragma unroll
         for (int j = 0; j < S::KS; ++j) {
-          const u32x4 kf = lds_read16(rb + (uint32_t)(16 * ((4 * j + q4) ^ qk_swz[kt])));
+          const u32x4 kf = lds_read16(rb + (uint32_t)(16 * ((4 * j + rq) ^ swz)));
 #pragma unroll
           for (int g = 0; g < HG; ++g) st[g][kt] = mfma_bf16(kf, qf[g][j], st[g][kt]);
         }
@@ -359,6 +373,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
       barrier_keep_loads();  // the transposed value tile is complete
       // ---- O^T += V^T P^T ----
+      const uint32_t pv_base = vt_lds + (uint32_t)((dp * DVW + (ln & 15)) * MLA_VT_ROW + 16 * (ln >> 4));
 #pragma unroll
       for (int t = 0; t < DTW; ++t) {
         const u32x4 vf = lds_read16(pv_base + (uint32_t)(16 * t * MLA_VT_ROW));
