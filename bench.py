@@ -479,6 +479,16 @@ def main():
         f"({100 * pre_tflops / BF16_MFMA_PEAK_TFLOPS:.1f}% of bf16 MFMA peak)")
     del mb, chunk
     torch.cuda.empty_cache()
+    # the same chunk over an fp8 e4m3 cache (per-block scales)
+    fb = W.make_batch("mixed_step_chunk_fp8", 4, [65536 + 2048], [2048], 32, 8, 128, "bf16", "fp8_e4m3",
+                      device="cuda")
+    _, f8_attend = prefill_step_fns(pa, torch, fb)
+    _, f8_ms, _ = time_steps(torch, lambda: None, f8_attend, max(10, args.steps // 2), 5)
+    f8_tflops = causal_flops(fb) / (f8_ms * 1e-3) / 1e12
+    log(f"prefill chunk alone, fp8 cache: {f8_ms:.3f} ms, {f8_tflops:.0f} TFLOP/s "
+        f"({100 * f8_tflops / BF16_MFMA_PEAK_TFLOPS:.1f}% of bf16 MFMA peak)")
+    del fb
+    torch.cuda.empty_cache()
 
     # ---- sparse decode over chosen blocks, long contexts ----
     sb, sp = run_sparse(pa, torch, W, max(10, args.steps // 2), args.warmup)
@@ -562,6 +572,8 @@ def main():
                        "workload": "192 decode rows (context U{4096..32768}) + one 2048-token chunk on a "
                                    "65536-token prefix; 2240 new tokens written; 32/8 heads, d128, bf16",
                        "prefill_chunk_only_ms": round(pre_ms, 5), "prefill_tflops": round(pre_tflops, 2),
+                       "prefill_fp8_cache_chunk": {"ms": round(f8_ms, 5), "tflops": round(f8_tflops, 2),
+                                                   "frac_bf16_peak": round(f8_tflops / BF16_MFMA_PEAK_TFLOPS, 4)},
                        "prefill_frac_bf16_peak": round(pre_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                        "prefill_roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel (the chunk alone)",
                                             "achieved": round(pre_tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,

@@ -159,9 +159,9 @@ struct PrefillArgs {
 int prefill_tokens_per_tile(int cache_kind, int group);
 int prefill_bf16_tokens_per_tile(int group);
 hipError_t launch_prefill(const PrefillArgs& args, int cache_kind, int head_size, hipStream_t stream);
-// bf16 caches: the 32x32 MFMA kernel (bf16 scores, fp16 PV) with direct
-// global->LDS copies, 8 waves per workgroup.
-hipError_t launch_prefill_bf16(const PrefillArgs& args, int head_size, hipStream_t stream);
+// The 32x32 MFMA kernel (bf16 scores, fp16 PV) with direct global->LDS
+// copies, 8 waves per workgroup, for bf16 and fp8 caches.
+hipError_t launch_prefill_bf16(const PrefillArgs& args, int cache_kind, int head_size, hipStream_t stream);
 bool prefill_supported(int q_kind, int cache_kind, int head_size, int group);
 
 }  // namespace pa

@@ -1,6 +1,6 @@
-// Chunked-prefill paged attention for bf16 KV caches on gfx950 matrix cores:
-// scores on 32x32x16 bf16 MFMA, the weighted sum of values on 32x32x16 fp16
-// MFMA, both with fp32 accumulation.
+// Chunked-prefill paged attention for bf16 and fp8 (e4m3fn) KV caches on
+// gfx950 matrix cores: scores on 32x32x16 bf16 MFMA, the weighted sum of
+// values on 32x32x16 fp16 MFMA, both with fp32 accumulation.
 //
 // What it computes: every query row of a chunk longer than one token attends
 // causally to its sequence's cached keys, read through the block table; query
@@ -43,7 +43,13 @@
 //  * masks (causal edge, sliding window, context end) are evaluated only in
 //    the steps that cross an edge; values of keys past the context are
 //    zeroed in the last step, because the block of a partial last block may
-//    hold anything past the context.
+//    hold anything past the context;
+//  * fp8 caches (one fp32 scale per block for K and one for V): the K tiles
+//    stay e4m3 in LDS (half the bytes) and are widened to bf16 in registers
+//    just before their MFMA (exact); the score takes the block's K scale.
+//    The V tiles are copied to a ring of their own and the conversion pass
+//    writes them as fp16 values times the block's V scale into the V slots
+//    the bf16 path uses (the scaled values are the kernel's fp16 domain).
 #include <math.h>
 
 #include <type_traits>
@@ -100,6 +106,14 @@ __device__ __forceinline__ int k_swizzle(int key) {
   else return (key >> 1) & 7;
 }
 __device__ __forceinline__ int v_swizzle(int d) { return (d >> 3) & 1; }
+// fp8 K rows (D bytes = D/16 chunks): the 32 lanes of a half-wave read one
+// 8-byte half-chunk of 32 permuted keys; spreading the chunk by key bits
+// 1..3 (or 1..2) makes them cover every bank pair of two LDS cycles.
+template <int D>
+__device__ __forceinline__ int k8_swizzle(int key) {
+  if constexpr (D == 128) return (key >> 1) & 7;
+  else return (key >> 1) & 3;
+}
 
 // Score row m of a step holds this key of the step.
 __device__ __forceinline__ int step_key_of_row(int m) {
@@ -168,13 +182,18 @@ __device__ __forceinline__ void step_barrier() {
 constexpr int PF_NW = 8;             // waves per workgroup
 constexpr int PF_NT = 64 * PF_NW;    // threads per workgroup
 
-template <int D, int G>
+template <int D, int G, int CK>
 __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(PrefillArgs a) {
   using S = PfShape<D>;
   constexpr int NW = PF_NW, NT = PF_NT;
   constexpr int TQ = 32 * NW / G;
-  __shared__ __attribute__((aligned(16))) uint16_t kring[S::KSLOTS * S::KSLOT];
+  constexpr bool FP8 = CK == KFP8;
+  constexpr int E = FP8 ? 1 : 2;          // bytes per cached element
+  constexpr int KSLOTB = 32 * D * E;      // bytes of one K slot
+  constexpr int RVSLOTB = 32 * D;         // bytes of one raw fp8 V slot
+  __shared__ __attribute__((aligned(16))) uint16_t kring[S::KSLOTS * KSLOTB / 2];
   __shared__ __attribute__((aligned(16))) uint16_t vring[S::VSLOTS * S::VSLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t rvring[FP8 ? S::KSLOTS * RVSLOTB : 16];
   __shared__ int sh_scan[NT];
   __shared__ int sh_found[3];
 
@@ -233,12 +252,15 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   // D/16 of them K, the rest V. Each lane fetches the global chunk that
   // lands, swizzled, where the MFMA operand reads expect it. Blocks past the
   // context re-read the last block (masked, zeroed).
-  constexpr int KCOPIES = D / 16;
-  constexpr int CPW = 2 * KCOPIES / NW;  // copies per wave per step
-  static_assert(CPW >= 1 && 2 * KCOPIES % NW == 0, "copy split");
-  const uint32_t head_stride = (uint32_t)a.num_kv_heads * S::BLK_BYTES;
-  const uint8_t* kcache = reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)g * S::BLK_BYTES;
-  const uint8_t* vcache = reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * S::BLK_BYTES;
+  constexpr int KCOPIES = D * E / 32;       // 1 KiB copies per K slot (and per V slot)
+  constexpr int NCOPY = 2 * KCOPIES;
+  constexpr int CPW = NCOPY >= NW ? NCOPY / NW : 1;  // copies per copying wave per step
+  static_assert(NCOPY % NW == 0 || NCOPY < NW, "copy split");
+  const bool copier = NCOPY >= NW || wave < NCOPY;  // (fp8, head size 64: half the waves copy)
+  constexpr uint32_t TILE_BYTES = 16 * D * E;      // one (block, head) tile
+  const uint32_t head_stride = (uint32_t)a.num_kv_heads * TILE_BYTES;
+  const uint8_t* kcache = reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)g * TILE_BYTES;
+  const uint8_t* vcache = reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * TILE_BYTES;
   const int b0 = jstart >> 4;
   constexpr int CPR = D / 8;  // chunks per K row
   uint32_t cp_off[CPW];
@@ -246,32 +268,44 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   for (int n = 0; n < CPW; ++n) {
     const int j = wave + NW * n;
     const int p = 64 * (j < KCOPIES ? j : j - KCOPIES) + lane;  // 16-byte position in the slot
-    if (j < KCOPIES) {
-      const int key = p / CPR;
-      cp_off[n] = (key % 16) * (2 * D) + 16 * ((p % CPR) ^ k_swizzle<D>(key));
+    if constexpr (FP8) {
+      if (j < KCOPIES) {  // K rows of D bytes, chunk-swizzled
+        const int key = p / (D / 16);
+        cp_off[n] = (key % 16) * D + 16 * ((p % (D / 16)) ^ k8_swizzle<D>(key));
+      } else {            // raw V: the two blocks' [D][16] tiles as they are
+        cp_off[n] = (p % D) * 16;
+      }
     } else {
-      const int d = (p / 2) % D;
-      cp_off[n] = d * 32 + 16 * ((p % 2) ^ v_swizzle(d));
+      if (j < KCOPIES) {
+        const int key = p / CPR;
+        cp_off[n] = (key % 16) * (2 * D) + 16 * ((p % CPR) ^ k_swizzle<D>(key));
+      } else {
+        const int d = (p / 2) % D;
+        cp_off[n] = d * 32 + 16 * ((p % 2) ^ v_swizzle(d));
+      }
     }
   }
   const uint32_t kring_lds = lds_offset(kring), vring_lds = lds_offset(vring);
+  const uint32_t rvring_lds = FP8 ? lds_offset(reinterpret_cast<const uint16_t*>(rvring)) : 0u;
   // block ids are non-negative and a head's block stride is below 4 GiB
   auto copy_step = [&](int step, int kslot, int vslot) {
     if constexpr (CPW == 2) {
       // one K and one V copy per wave, both of block wave / (2 D / 64) of
       // the step
-      const int b = min(b0 + 2 * step + (64 * wave) / (2 * D), b_last);
+      const int b = min(b0 + 2 * step + (64 * wave) / (D * E), b_last);
       const uint64_t off = (uint64_t)(uint32_t)bt[b] * head_stride;
-      copy_kv_to_lds(kcache + off, cp_off[0], kring_lds + kslot * (2 * S::KSLOT) + 1024 * wave,
+      copy_kv_to_lds(kcache + off, cp_off[0], kring_lds + kslot * KSLOTB + 1024 * wave,
                      vcache + off, cp_off[1], vring_lds + vslot * (2 * S::VSLOT) + 1024 * wave);
     } else {
       static_assert(CPW == 1, "one or two copies per wave");
+      if (!copier) return;
       const bool isv = wave >= KCOPIES;
       const int jj = isv ? wave - KCOPIES : wave;
-      const int b = min(b0 + 2 * step + (64 * jj) / (2 * D), b_last);
+      const int b = min(b0 + 2 * step + (64 * jj) / (D * E), b_last);
       const uint64_t off = (uint64_t)(uint32_t)bt[b] * head_stride;
-      const uint32_t lds = isv ? vring_lds + vslot * (2 * S::VSLOT) + 1024 * jj
-                               : kring_lds + kslot * (2 * S::KSLOT) + 1024 * jj;
+      // (fp8: the raw V ring turns with the K ring)
+      const uint32_t vdst = FP8 ? rvring_lds + kslot * RVSLOTB : vring_lds + vslot * (2 * S::VSLOT);
+      const uint32_t lds = isv ? vdst + 1024 * jj : kring_lds + kslot * KSLOTB + 1024 * jj;
       copy_to_lds((isv ? vcache : kcache) + off, cp_off[0], lds);
     }
   };
@@ -285,21 +319,34 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   // offset)
   uint32_t kaddr[S::DK];
 #pragma unroll
-  for (int ks = 0; ks < S::DK; ++ks)
-    kaddr[ks] = lds_offset(kring) + 2 * (key_l * D + 8 * ((2 * ks + h) ^ kswz_l));
-  u32x4 kf[S::DK];
+  for (int ks = 0; ks < S::DK; ++ks) {
+    if constexpr (FP8)
+      kaddr[ks] = lds_offset(kring) + key_l * D + 16 * (ks ^ k8_swizzle<D>(key_l)) + 8 * h;
+    else
+      kaddr[ks] = lds_offset(kring) + 2 * (key_l * D + 8 * ((2 * ks + h) ^ kswz_l));
+  }
+  u32x4 kf[FP8 ? 1 : S::DK];
+  u32x2 k8[FP8 ? S::DK : 1];  // fp8: the raw 8 bytes, widened just before their MFMA
   auto scores_load = [&](int slot) {
-    const uint32_t sb = __builtin_amdgcn_readfirstlane(slot * S::KSLOT * 2);
+    const uint32_t sb = __builtin_amdgcn_readfirstlane(slot * KSLOTB);
 #pragma unroll
     for (int ks = 0; ks < S::DK; ++ks) {
-      typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-      kf[ks] = *(const lds_u32x4*)(uintptr_t)(kaddr[ks] + sb);
+      if constexpr (FP8) {
+        typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
+        k8[ks] = *(const lds_u32x2*)(uintptr_t)(kaddr[ks] + sb);
+      } else {
+        typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+        kf[ks] = *(const lds_u32x4*)(uintptr_t)(kaddr[ks] + sb);
+      }
     }
   };
   auto scores_mfma = [&]() {
     f32x16 acc = {};
 #pragma unroll
-    for (int ks = 0; ks < S::DK; ++ks) acc = mfma32x32x16(kf[ks], qf[ks], acc);
+    for (int ks = 0; ks < S::DK; ++ks) {
+      if constexpr (FP8) acc = mfma32x32x16(fp8x8_to_bf16x8(k8[ks][0], k8[ks][1]), qf[ks], acc);
+      else acc = mfma32x32x16(kf[ks], qf[ks], acc);
+    }
     return acc;
   };
   auto scores = [&](int slot) { scores_load(slot); return scores_mfma(); };
@@ -327,19 +374,51 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   // bf16 -> fp16 in place: thread tid owns the 16-byte chunk tid of the
   // slot (4 D chunks; threads past them idle). The chunk is read early in an
   // iteration and written back at its end.
-  constexpr int VCH = 4 * D;
+  // (fp8: thread tid < 2 D owns raw chunk tid = 16 keys of dim tid % D of
+  // block tid / D, and writes them as two fp16 chunks times the V scale)
+  constexpr int VCH = FP8 ? 2 * D : 4 * D;
   static_assert(VCH <= NT, "one chunk per thread");
   const bool converts = VCH == NT || tid < VCH;
   u32x4 cvt = {0, 0, 0, 0};
-  auto convert_load = [&](int slot) {
-    if (converts) cvt = reinterpret_cast<const u32x4*>(vring + slot * S::VSLOT)[tid];
+  float cvt_scale = 1.f;
+  typedef __attribute__((address_space(4))) const float cfloat;
+  auto convert_load = [&](int slot, int raw_slot, int step) {
+    if constexpr (FP8) {
+      if (converts) {
+        cvt = reinterpret_cast<const u32x4*>(rvring + raw_slot * RVSLOTB)[tid];
+        // both blocks' scales by uniform (scalar) loads, then picked per thread
+        const float s0 = ((const cfloat*)a.v_scale)[bt[min(b0 + 2 * step, b_last)]];
+        const float s1 = ((const cfloat*)a.v_scale)[bt[min(b0 + 2 * step + 1, b_last)]];
+        cvt_scale = tid >= D ? s1 : s0;
+      }
+    } else {
+      if (converts) cvt = reinterpret_cast<const u32x4*>(vring + slot * S::VSLOT)[tid];
+    }
   };
   auto convert_store = [&](int slot) {
-    if (converts) {
-      u32x4 w = cvt;
-      w[0] = bf16x2_to_f16x2(w[0]); w[1] = bf16x2_to_f16x2(w[1]);
-      w[2] = bf16x2_to_f16x2(w[2]); w[3] = bf16x2_to_f16x2(w[3]);
-      reinterpret_cast<u32x4*>(vring + slot * S::VSLOT)[tid] = w;
+    if constexpr (FP8) {
+      if (converts) {
+        const int t = tid / D, d = tid % D;
+        uint16_t* row = vring + slot * S::VSLOT + t * D * 16 + d * 16;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {  // keys 8c .. 8c + 7
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t src = cvt[2 * c + (e >> 1)];
+            const f32x2 f = (e & 1) ? fp8x2_hi(src) : fp8x2_lo(src);
+            w[e] = pack_f16x2(f.x * cvt_scale, f.y * cvt_scale);
+          }
+          *reinterpret_cast<u32x4*>(row + 8 * (c ^ v_swizzle(d))) = w;
+        }
+      }
+    } else {
+      if (converts) {
+        u32x4 w = cvt;
+        w[0] = bf16x2_to_f16x2(w[0]); w[1] = bf16x2_to_f16x2(w[1]);
+        w[2] = bf16x2_to_f16x2(w[2]); w[3] = bf16x2_to_f16x2(w[3]);
+        reinterpret_cast<u32x4*>(vring + slot * S::VSLOT)[tid] = w;
+      }
     }
   };
 
@@ -353,7 +432,7 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   }
   wait_vmcnt<0>();
   __syncthreads();
-  convert_load(0);
+  convert_load(0, 0, 0);
   convert_store(0);
   f32x16 sc = scores(0), sc2;
   int krot = 0;  // step % KSLOTS of the next iteration
@@ -378,7 +457,7 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const int slot_va = vrot >= 2 ? vrot - 2 : vrot + VS - 2;  // V of step st+AHEAD replaces V of step st-2
     vrot = slot_v1;
     copy_step(st + S::AHEAD, slot_ka, slot_va);
-    convert_load(slot_v1);                  // converted below; read by the PV product two iterations on
+    convert_load(slot_v1, slot_k1, st + 1);  // converted below; read by the PV product two iterations on
     scores_load(slot_k1);
     __builtin_amdgcn_sched_barrier(0);
     sn = scores_mfma();                     // S of step st+1 (unused past the end)
@@ -388,9 +467,14 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     float x[16];
     float tmax = -INFINITY;
     const int kbase = jstart + 32 * st + 8 * h;
+    float ksc[2] = {1.f, 1.f};  // fp8: K scales of the step's two blocks (scalar loads)
+    if constexpr (FP8) {
+      ksc[0] = ((const cfloat*)a.k_scale)[bt[min(b0 + 2 * st, b_last)]];
+      ksc[1] = ((const cfloat*)a.k_scale)[bt[min(b0 + 2 * st + 1, b_last)]];
+    }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      float sv = sc[v];
+      float sv = FP8 ? sc[v] * ksc[v >> 3] : sc[v];
       if constexpr (MASKED) {
         const int kp = kbase + 16 * (v >> 3) + 4 * ((v >> 2) & 1) + (v & 3);
         const bool ok = kp <= qpos && kp < ctx && (W <= 0 || kp > qpos - W);
@@ -485,32 +569,34 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   }
 }
 
-template <int D, int G>
+template <int D, int G, int CK>
 static hipError_t run_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
   const unsigned blocks = (unsigned)a.num_tiles * (unsigned)a.num_kv_heads;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, G>), dim3(blocks), dim3(PF_NT), 0, st, a);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, G, CK>), dim3(blocks), dim3(PF_NT), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int CK>
 static hipError_t run_prefill_bf16_g(const PrefillArgs& a, int G, hipStream_t st) {
   switch (G) {
-    case 1: return run_prefill_bf16<D, 1>(a, st);
-    case 2: return run_prefill_bf16<D, 2>(a, st);
-    case 4: return run_prefill_bf16<D, 4>(a, st);
-    case 8: return run_prefill_bf16<D, 8>(a, st);
-    case 16: return run_prefill_bf16<D, 16>(a, st);
+    case 1: return run_prefill_bf16<D, 1, CK>(a, st);
+    case 2: return run_prefill_bf16<D, 2, CK>(a, st);
+    case 4: return run_prefill_bf16<D, 4, CK>(a, st);
+    case 8: return run_prefill_bf16<D, 8, CK>(a, st);
+    case 16: return run_prefill_bf16<D, 16, CK>(a, st);
   }
   return hipErrorInvalidValue;
 }
 
 int prefill_bf16_tokens_per_tile(int group) { return 32 * PF_NW / group; }
 
-hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_size, hipStream_t stream) {
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int cache_kind, int head_size, hipStream_t stream) {
   const int G = a.num_heads / a.num_kv_heads;
-  if (head_size == 64) return run_prefill_bf16_g<64>(a, G, stream);
-  if (head_size == 128) return run_prefill_bf16_g<128>(a, G, stream);
+  if (cache_kind == KBF16 && head_size == 64) return run_prefill_bf16_g<64, KBF16>(a, G, stream);
+  if (cache_kind == KBF16 && head_size == 128) return run_prefill_bf16_g<128, KBF16>(a, G, stream);
+  if (cache_kind == KFP8 && head_size == 64) return run_prefill_bf16_g<64, KFP8>(a, G, stream);
+  if (cache_kind == KFP8 && head_size == 128) return run_prefill_bf16_g<128, KFP8>(a, G, stream);
   return hipErrorInvalidValue;
 }
 

@@ -307,6 +307,8 @@ PREFILL_CASES = [
     ([1000, 260], [300, 260], 8, 2, 128, "bf16", 100),
     ([2000, 33], [64, 1], 16, 8, 128, "bf16", 1),
     ([5000], [1], 8, 2, 128, "bf16", 0),
+    ([1500, 300], [700, 300], 64, 4, 128, "fp8_e4m3", 0),    # fp8, G = 16
+    ([900, 2000], [128, 513], 16, 4, 64, "fp8_e4m3", 200),  # fp8, head 64 (half the waves copy), window
 ]
 
 
