@@ -53,12 +53,12 @@ __device__ __forceinline__ f32x2 fp8x2_lo(uint32_t w) {
 __device__ __forceinline__ f32x2 fp8x2_hi(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
 }
-// Four e4m3fn bytes -> two packed bf16 pairs (exact: every e4m3 value is a bf16 value).
+// Four e4m3fn bytes -> two packed bf16 pairs (exact: every e4m3 value is a bf16
+// value). gfx950 converts a byte pair straight to packed bf16 (scale 1.0:
+// checked equal to the fp32 route for all 65536 code pairs, NaNs included).
 __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& p01, uint32_t& p23) {
-  f32x2 a = fp8x2_lo(w);
-  f32x2 b = fp8x2_hi(w);
-  p01 = pack_bf16x2(a.x, a.y);
-  p23 = pack_bf16x2(b.x, b.y);
+  p01 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  p23 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
 
 // Eight e4m3fn bytes (two words) -> eight bf16 (four packed pairs).
