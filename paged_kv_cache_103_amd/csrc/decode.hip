@@ -465,16 +465,21 @@ DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num
   const int G = std::max(1, num_heads / std::max(1, num_kv_heads));
   // (the matrix-core kernel keeps per-sequence prefix sums in LDS: up to
   // 16000 sequences per call; larger batches take the VALU kernel)
+  int max_blocks = (max_context_len + 15) / 16;
+  if (sliding_window > 0) max_blocks = std::min(max_blocks, (sliding_window + 15) / 16 + 1);
+  if (max_blocks < 1) max_blocks = 1;
   if (decode_uses_mfma(q_kind, cache_kind, G) && num_seqs <= 16000) {
     // two resident workgroups of four waves per CU
     plan.split_waves = 8 * device_cu_count();
     plan.pb = 0;
     plan.max_parts = 0;
+    // every (sequence, KV head) stream at most 16 blocks (a short context or
+    // a sliding window): one wave per stream finishes it in place, with no
+    // summaries and no merge launch; a split would leave each wave a pair or
+    // two and cost more in summaries, merge and launch than it saves
+    plan.one_per_stream = max_blocks <= kOnePerStreamMaxBlocks ? 1 : 0;
     return plan;
   }
-  int max_blocks = (max_context_len + 15) / 16;
-  if (sliding_window > 0) max_blocks = std::min(max_blocks, (sliding_window + 15) / 16 + 1);
-  if (max_blocks < 1) max_blocks = 1;
   // VALU kernel: a workgroup per (sequence, KV head, partition of pb blocks);
   // the largest partition (16..256 blocks) that still leaves about 16 work
   // items per CU, assuming contexts average half the maximum.
@@ -500,6 +505,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int num_heads, int num_kv_heads,
                               int head_size) {
+  if (plan.split_waves > 0 && plan.one_per_stream) return 0;
   if (plan.split_waves > 0) {
     const int G = num_heads / num_kv_heads;
     const size_t slots = (size_t)plan.split_waves + (size_t)num_seqs * num_kv_heads;

@@ -244,7 +244,7 @@ __device__ __forceinline__ void wave_write(WaveAcc<D>& acc, const DecodeArgs& a,
   const float L = strided_sum<16>(acc.lsum);
   if (c16 >= ncols) return;
   if (single) {
-    const float inv = 1.f / L;
+    const float inv = L > 0.f ? 1.f / L : 0.f;  // no keys (an empty range): zeros
     if (a.lse != nullptr && q4 == 0) a.lse[(size_t)qrow * a.num_heads + g * G + c16] = (acc.m + log2f(L)) * kLn2;
     uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * a.num_heads + g * G + c16) * D + 4 * q4;
 #pragma unroll
@@ -482,6 +482,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int* psum = SHARED ? effp + NG : lds;
   int* scan = psum + (SHARED ? 2 * NSEQ + 1 : NSEQ + 1);
 
+  if constexpr (!SHARED) {
+    if (a.one_per_stream) {  // uniform: no barrier is reached on this path
+      const int w = blockIdx.x * 4 + wave;
+      if (w >= NSEQ * H) return;
+      const int s = w / H, g = w % H;
+      if (a.cu_seqlens != nullptr && a.cu_seqlens[s + 1] - a.cu_seqlens[s] != 1) return;  // a chunk row
+      int qrow, ctx, lo;
+      const int nb = seq_blocks(a, s, qrow, ctx, lo);
+      WaveAcc<D> acc;
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt) acc.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc.m = -INFINITY;
+      acc.lsum = 0.f;
+      if (nb > 0) {
+        u32x4 qf[S::DS];
+        load_query<CK, D>(qf, a, qrow, g, G, c16, q4, G);
+        wave_blocks<CK, D>(acc, qf, reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)g * S::TILE,
+                           reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * S::TILE,
+                           a.block_table + (size_t)s * a.bt_stride, lo >> 4, (lo >> 4) + nb, lo, ctx,
+                           (size_t)H * S::TILE, a, c16, q4);
+      }
+      wave_write<D>(acc, a, 0, qrow, g, G, true, c16, q4, G);  // an empty range: zeros, lse -inf
+      return;
+    }
+  }
   int nstreams = NSEQ;
   if constexpr (SHARED) nstreams += shared_prefix_setup(a, G, sg, cbase, effp, scan);
   const int per_head = lds_exclusive_scan(
@@ -647,6 +672,11 @@ __global__ __launch_bounds__(256) void decode_split_merge(DecodeArgs a) {
 
 template <int CK, int D, bool SHARED>
 static hipError_t run_decode_mfma(const DecodeArgs& a, hipStream_t st) {
+  if (!SHARED && a.one_per_stream) {  // a wave per (sequence, KV head), finished in place
+    const long long streams = (long long)a.num_seqs * a.num_kv_heads;
+    hipLaunchKernelGGL((decode_mfma_split<CK, D, SHARED>), dim3((unsigned)((streams + 3) / 4)), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)(a.split_waves / 4));
   const size_t lds = SHARED ? (size_t)(3 * a.num_seqs + 2 * a.num_groups + 2 + 256) * sizeof(int)
                             : (size_t)(a.num_seqs + 1 + 256) * sizeof(int);

@@ -152,6 +152,7 @@ static void bind_workspace(pa::DecodeArgs& a, const pa::DecodePlan& plan, void* 
   a.pb = plan.pb;
   a.max_parts = plan.max_parts;
   a.split_waves = plan.split_waves;
+  a.one_per_stream = plan.one_per_stream;
   a.meta = nullptr;
   a.part_o = nullptr;
   a.part_ml = nullptr;

@@ -37,10 +37,14 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
 // wave writes one summary per stream segment it covers, in slot
 // wave + stream (unique, since consecutive segments advance exactly one of
 // the two).
+// Longest (sequence, KV head) stream, in blocks, that the matrix-core decode
+// serves with one wave per stream.
+constexpr int kOnePerStreamMaxBlocks = 16;
 struct DecodePlan {
   int pb;
   int max_parts;
   int split_waves;  // > 0: even split over this many waves (matrix-core kernel)
+  int one_per_stream;  // matrix-core kernel, every stream short: a wave per (sequence, KV head), no merge
 };
 DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num_kv_heads, int head_size,
                        int q_kind, int cache_kind, int sliding_window);
@@ -82,6 +86,7 @@ struct DecodeArgs {
   int pb;
   int max_parts;
   int split_waves;
+  int one_per_stream;  // see DecodePlan
   float scale_log2;  // softmax scale * log2(e)
   float* lse;        // optional [rows][num_heads]: ln of the softmax denominator (matrix-core kernel)
 };

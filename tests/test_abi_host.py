@@ -145,6 +145,12 @@ def test_workspace_queries(lib):
         lib.decode_workspace_bytes(128, 131072, 64, 8, 128, "fp8_e4m3", 0)
     assert lib.decode_workspace_bytes(8, 131072, 8, 2, 64, "f32", 128) < \
         lib.decode_workspace_bytes(8, 131072, 8, 2, 64, "f32", 0)
+    # matrix-core decode with every stream at most 16 blocks (contexts up to
+    # 256 tokens, or a window up to 240): a wave per stream, no summaries
+    assert lib.decode_workspace_bytes(64, 256, 32, 8, 128, "bf16") == 0
+    assert lib.decode_workspace_bytes(64, 257, 32, 8, 128, "bf16") > 0
+    assert lib.decode_workspace_bytes(128, 131072, 64, 8, 128, "fp8_e4m3", 240) == 0
+    assert lib.decode_workspace_bytes(128, 131072, 64, 8, 128, "fp8_e4m3", 241) > 0
     # the one-token rows of a mixed batch use the decode plan
     assert lib.prefill_workspace_bytes(193, 2240, 2048, 67584, 32, 8, 128, "bf16") == \
         lib.decode_workspace_bytes(193, 67584, 32, 8, 128, "bf16")
@@ -278,7 +284,7 @@ def test_partial_decode_and_merge_reject_bad_arguments(lib):
     assert partial(lse=None) == 1
     assert partial(qd=0, cd=0) == 2  # fp32 caches take the VALU kernel: no partial results
     assert partial(B=8) == 2
-    assert partial(ws_bytes=8) == 3
+    assert partial(ws_bytes=8, max_ctx=1000, bt_stride=64) == 3  # split plan: summaries need workspace
     assert partial(S=0, lse=None) == 0
 
     def merge(**over):

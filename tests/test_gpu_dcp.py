@@ -86,6 +86,7 @@ DCP_CASES = [
     ([5000, 700, 16, 1], 2, 16, 2, 64, "fp8_e4m3", True),
     ([3000, 999, 130], 8, 64, 4, 128, "bf16", True),
     ([1500, 257, 40], 3, 32, 8, 128, "bf16", False),
+    ([200, 33, 256, 1], 2, 32, 8, 128, "bf16", True),  # every range short: a wave per stream, empty ranges
 ]
 
 

@@ -283,6 +283,10 @@ DECODE_CASES = [
     ([1, 50, 129, 700], 8, 8, 64, "bf16", "fp8_e4m3", 0),
     ([1, 100, 128, 129, 5000], 8, 1, 128, "bf16", "bf16", 128),
     ([20, 300, 3000], 16, 2, 64, "f32", "f32", 37),
+    # every stream at most 16 blocks: one wave per (sequence, KV head), no merge
+    ([1, 2, 15, 16, 17, 100, 255, 256], 8, 2, 128, "bf16", "bf16", 0),
+    ([1, 30, 200, 256], 16, 4, 64, "bf16", "fp8_e4m3", 0),
+    ([3000, 40000, 5, 241], 32, 8, 128, "bf16", "fp8_e4m3", 240),
     ([1, 33, 800], 4, 1, 128, "f32", "f32", 0),
 ]
 
