@@ -301,9 +301,12 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
                            int32_t sliding_window, void* workspace, size_t workspace_bytes,
                            pa_stream_t stream);
 
-/* Workspace bytes pa_decode needs for these sizes and cache type (0 if
- * none): the split-K partition summaries, num_seqs x num_heads x partitions
- * x (head_size + 2) floats. */
+/* Workspace bytes pa_decode needs for these sizes and cache type: the
+ * split-K summaries (per partition and query head, head_size + 2 floats) and
+ * per-sequence block counts. 0 when no summaries are needed: one partition
+ * (fp32 caches with short contexts), or bf16/fp8 caches whose (sequence, KV
+ * head) streams are at most 16 blocks (max_context_len <= 256, or
+ * sliding_window <= 240), which one wave each finishes in place. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
                                  int32_t num_kv_heads, int32_t head_size, pa_dtype cache_dtype,
                                  int32_t sliding_window);
