@@ -300,6 +300,8 @@ def cpu_baseline(b, budget_s=12.0):
 
 DECODE_SOURCES = ("decode_mfma.hip", "decode.hip", "pa_device.h", "pa_internal.h")
 PREFILL_SOURCES = ("prefill_bf16.hip", "prefill_tiles.h", "pa_device.h", "pa_internal.h")
+MLA_SOURCES = ("mla_decode.hip", "pa_device.h", "pa_internal.h")
+SPARSE_SOURCES = ("sparse_select.hip", "decode_mfma.hip", "decode.hip", "pa_device.h", "pa_internal.h")
 
 
 def kernel_source_digest(files=DECODE_SOURCES):
@@ -593,6 +595,7 @@ def main():
                        "bytes_per_call": ml["bytes_per_call"], "flops_per_call": ml["flops_per_call"],
                        "roofline": {"bound": "hbm", "achieved": ml["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                     "frac": round(ml["gbs"] / HBM_PEAK_GBS, 4),
+                                    "traffic": stored_traffic("mla_decode_128h_576.md", MLA_SOURCES),
                                     "mfma_tflops": ml["tflops"],
                                     "mfma_frac": round(ml["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)}},
         "sparse_decode": {"value": round(sp["kv_gbs_attend"], 2), "unit": "GB/s", "attend_ms": round(sp["attend_ms"], 5),
@@ -602,7 +605,8 @@ def main():
                           "kv_bytes_per_call": sp["kv_bytes"], "dense_kv_bytes": sp["dense_kv_bytes"],
                           "roofline": {"bound": "hbm", "achieved": round(sp["kv_gbs_attend"], 2),
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                       "frac": round(sp["kv_gbs_attend"] / HBM_PEAK_GBS, 4)}},
+                                       "frac": round(sp["kv_gbs_attend"] / HBM_PEAK_GBS, 4),
+                                       "traffic": stored_traffic("decode_sparse_long_context.md", SPARSE_SOURCES)}},
     }
     if extra:
         line["extra"] = extra
