@@ -457,6 +457,7 @@ def main():
         torch.cuda.synchronize()
         del sb
         run_mla(pa, torch, W, 3, 0)
+        run_mla(pa, torch, W, 3, 0, 16, 576)
         log("profile pass done")
         return
 
@@ -503,10 +504,14 @@ def main():
     ml = run_mla(pa, torch, W, max(10, args.steps // 2), args.warmup)
     log(f"mla_decode (128 heads, rows of 576): {ml['attend_ms']*1e3:.1f} us, {ml['gbs']:.0f} GB/s of latent rows, "
         f"{ml['tflops']:.0f} TFLOP/s")
+    # 16 heads: one GPU's share of 128 heads under 8-way tensor parallelism,
+    # which still reads every latent row
+    ml16 = run_mla(pa, torch, W, max(10, args.steps // 2), args.warmup, 16, 576)
+    log(f"mla_decode (16 heads, rows of 576): {ml16['attend_ms']*1e3:.1f} us, {ml16['gbs']:.0f} GB/s of latent rows")
 
     extra = {}
     if args.extra:
-        for h, dk in ((64, 576), (128, 512), (16, 576)):
+        for h, dk in ((64, 576), (128, 512), (16, 512)):
             r = run_mla(pa, torch, W, max(10, args.steps // 2), args.warmup, h, dk)
             extra[f"mla_decode_{h}h_{dk}"] = r
             log(f"mla_decode ({h} heads, rows of {dk}): {r['attend_ms']*1e3:.1f} us, {r['gbs']:.0f} GB/s, "
@@ -598,6 +603,13 @@ def main():
                                     "traffic": stored_traffic("mla_decode_128h_576.md", MLA_SOURCES),
                                     "mfma_tflops": ml["tflops"],
                                     "mfma_frac": round(ml["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)}},
+        "mla_decode_16_heads": {"value": ml16["gbs"], "unit": "GB/s", "attend_ms": ml16["attend_ms"],
+                                "workload": "the same batch with 16 heads (one GPU's share of 128 under "
+                                            "8-way tensor parallelism); pa_mla_decode",
+                                "bytes_per_call": ml16["bytes_per_call"],
+                                "roofline": {"bound": "hbm", "achieved": ml16["gbs"], "peak": HBM_PEAK_GBS,
+                                             "unit": "GB/s", "frac": round(ml16["gbs"] / HBM_PEAK_GBS, 4),
+                                             "traffic": stored_traffic("mla_decode_16h_576.md", MLA_SOURCES)}},
         "sparse_decode": {"value": round(sp["kv_gbs_attend"], 2), "unit": "GB/s", "attend_ms": round(sp["attend_ms"], 5),
                           "step_ms": round(sp["step_ms"], 5),
                           "workload": "64 sequences, context U{32768..524288}, 128 chosen blocks (2048 keys) + "

@@ -120,6 +120,43 @@ __device__ __forceinline__ void lds_write8(uint32_t addr, uint32_t lo, uint32_t 
 
 }  // namespace
 
+// Units of work of every sequence (pairs of blocks, UNIT = 2, or blocks,
+// UNIT = 1) and their exclusive prefix sums, by all NT threads of the
+// workgroup, into psum[0..num_seqs]; returns the total.
+template <int NT, int UNIT>
+__device__ __forceinline__ int unit_prefix_sums(const MlaArgs& a, int* psum, int* scan) {
+  const int tid = threadIdx.x, NS = a.num_seqs;
+  int running = 0;
+  for (int base = 0; base < NS; base += NT) {
+    const int i = base + tid;
+    const int ctx = i < NS ? a.context_lens[i] : 0;
+    const int nb = ctx > 0 ? (ctx + 15) >> 4 : 0;
+    const int n = UNIT == 2 ? (nb + 1) >> 1 : nb;
+    scan[tid] = n;
+    __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {
+      const int v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    if (i < NS) psum[i] = running + scan[tid] - n;
+    running += scan[NT - 1];
+    __syncthreads();
+  }
+  if (tid == 0) psum[NS] = running;
+  __syncthreads();
+  return psum[NS];
+}
+
+// For the merge: units per worker and the prefix sums (workgroup 0).
+template <int NT>
+__device__ __forceinline__ void write_meta(const MlaArgs& a, const int* psum, int C) {
+  if (blockIdx.x != 0) return;
+  if (threadIdx.x == 0) a.meta[0] = C;
+  for (int i = threadIdx.x; i <= a.num_seqs; i += NT) a.meta[1 + i] = psum[i];
+}
+
 template <int DK, int NW>
 struct MlaShape {
   static constexpr int NT = 64 * NW;
@@ -157,34 +194,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int hg = wave / NDP, dp = wave % NDP;
   const int NS = a.num_seqs;
 
-  // ---- pairs of blocks per sequence, prefix sums (all threads) ----
-  {
-    int running = 0;
-    for (int base = 0; base < NS; base += NT) {
-      const int i = base + tid;
-      const int ctx = i < NS ? a.context_lens[i] : 0;
-      const int n = ctx > 0 ? (((ctx + 15) >> 4) + 1) >> 1 : 0;
-      scan[tid] = n;
-      __syncthreads();
-      for (int off = 1; off < NT; off <<= 1) {
-        const int v = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
-      }
-      if (i < NS) psum[i] = running + scan[tid] - n;
-      running += scan[NT - 1];
-      __syncthreads();
-    }
-    if (tid == 0) psum[NS] = running;
-    __syncthreads();
-  }
-  const int T = psum[NS];
+  const int T = unit_prefix_sums<NT, 2>(a, psum, scan);
   const int C = max(1, (T + (int)gridDim.x - 1) / (int)gridDim.x);
-  if (blockIdx.x == 0) {
-    if (tid == 0) a.meta[0] = C;
-    for (int i = tid; i <= NS; i += NT) a.meta[1 + i] = psum[i];
-  }
+  write_meta<NT>(a, psum, C);
 
   // ---- per-lane constant offsets ----
   // copies: piece k of a tile = bytes [1024 k, 1024 k + 1024), wholly inside
@@ -413,6 +425,252 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   }
 }
 
+// ---- 16 heads: the waves split the keys ----------------------------------
+//
+// With 16 heads a 32-key step holds too little work for 8 waves to share:
+// the kernel above would repeat the 16-head score product in every wave.
+// Here each of a workgroup's 4 waves (one per SIMD) walks its own even share
+// of the concatenated blocks, as the grouped-query decode does, and stages
+// its blocks by global->LDS copies in a ring of its own (no workgroup
+// barrier in the loop), with the copies of the next NSL - 1 blocks in flight. Per 16-key block: scores S^T = C Q^T on
+// 16x16x32 bf16 MFMAs (the 16 heads are the MFMA columns; a lane's four
+// score values are keys 4 (lane / 16) + r of head lane % 16, exactly its
+// P^T operand for a 16x16x16 MFMA over the 16 keys), online softmax with
+// lazy rescaling, O^T += V^T P^T on 16x16x16 bf16 MFMAs with P split into
+// bf16 hi + lo (2^-16 relative), the value operand read transposed straight
+// from the row-major block with gfx950's transposing LDS read.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma_bf16_k16(const u32x2& a, const u32x2& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, a), __builtin_bit_cast(v4i16, b), c, 0,
+                                                   0, 0);
+}
+// ds_read_b64_tr_b16: in each 16-lane group, lane j receives element j % 4 of
+// the four-element pieces that lanes j / 4, j / 4 + 4, j / 4 + 8 and
+// j / 4 + 12 of the group point at.
+__device__ __forceinline__ u32x2 lds_read_tr8(uint32_t addr) {
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)addr));
+}
+// Chunk swizzle of a block row (key 0..15), chosen so that the score reads
+// (16 lanes: 16 rows, one chunk column) and the transposed value reads (32
+// lanes: 8 rows x 2 chunks) hit distinct banks.
+template <int DK>
+__device__ __forceinline__ int narrow_swizzle(int row) {
+  const int r = row & 15;
+  if constexpr (DK == 576) return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);  // rows of 72 chunks
+  else return ((r & 7) << 1) | (r >> 3);                                   // rows of 64 chunks
+}
+
+#ifndef MLA_NARROW_WAVES
+#define MLA_NARROW_WAVES 4
+#endif
+constexpr int kNarrowWaves = MLA_NARROW_WAVES;          // waves per workgroup
+constexpr int kNarrowSlots = 8 / MLA_NARROW_WAVES;      // ring slots per wave (the LDS holds 8 blocks)
+
+// At most `ahead` blocks of this wave's copies (COPIES each) still in flight.
+template <int COPIES, int NSL>
+__device__ __forceinline__ void wait_blocks(int ahead) {
+  if constexpr (NSL >= 4) {
+    if (ahead >= 3) { wait_vm<3 * COPIES>(); return; }
+  }
+  if constexpr (NSL >= 3) {
+    if (ahead >= 2) { wait_vm<2 * COPIES>(); return; }
+  }
+  if (ahead >= 1) { wait_vm<COPIES>(); return; }
+  wait_vm<0>();
+}
+
+template <int DK>
+struct MlaNarrowShape {
+  static constexpr int ROWB = DK * 2;
+  static constexpr int BLKB = 16 * ROWB;       // one block = one slot
+  static constexpr int COPIES = BLKB / 1024;   // 1 KiB copies per block (18 or 16)
+  static constexpr int KS = DK / 32;           // score MFMAs per block
+  static constexpr int DTV = MLA_DV / 16;      // 16-dim output tiles
+};
+
+template <int DK>
+__global__ __launch_bounds__(64 * kNarrowWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_decode_narrow(
+    MlaArgs a) {
+  using S = MlaNarrowShape<DK>;
+  constexpr int H = 16, NW = kNarrowWaves, NT = 64 * NW, NSL = kNarrowSlots;
+  static_assert((NSL & (NSL - 1)) == 0 && NSL >= 2 && NSL <= 4, "2 or 4 slots");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NW * NSL * S::BLKB];
+  __shared__ int psum[kMlaMaxSeqs + 1];
+  __shared__ int scan[NT];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, q4 = lane >> 4;
+  const int NS = a.num_seqs;
+  const int T = unit_prefix_sums<NT, 1>(a, psum, scan);
+  const int workers = NW * (int)gridDim.x;
+  const int C = max(1, (T + workers - 1) / workers);  // blocks per wave
+  write_meta<NT>(a, psum, C);
+
+  // copies: piece k of a block = bytes [1024 k, 1024 k + 1024) of its slot;
+  // this lane's source offset in the block for each piece
+  uint32_t src[S::COPIES];
+#pragma unroll
+  for (int k = 0; k < S::COPIES; ++k) {
+    const int P = 1024 * k + 16 * lane;
+    const int row = P / S::ROWB, pch = (P % S::ROWB) / 16;
+    src[k] = (uint32_t)(row * S::ROWB + 16 * (pch ^ narrow_swizzle<DK>(row)));
+  }
+  const uint32_t ring_lds = lds_addr(ring) + (uint32_t)(wave * NSL * S::BLKB);
+  // score operand: key c16, dims 32 j + 8 q4 .. + 7 (chunk 4 j + q4)
+  const int kswz = narrow_swizzle<DK>(c16);
+  // value operand: lane (group q4, j = c16) points at key 4 q4 + j / 4, dims
+  // 16 t + 4 (j % 4) .. + 3, i.e. chunk 2 t + (j % 4) / 2, half j % 2
+  const int vrow = 4 * q4 + (c16 >> 2);
+  const int vswz = narrow_swizzle<DK>(vrow);
+  const uint32_t vbase = (uint32_t)(vrow * S::ROWB + 8 * (c16 & 1));
+  const int vch = (c16 & 3) >> 1;
+
+  const uint8_t* cache = reinterpret_cast<const uint8_t*>(a.cache);
+  const int w = (int)blockIdx.x * NW + wave;
+  const long long x_end = min<long long>((long long)(w + 1) * C, T);
+  long long x = (long long)w * C;
+  while (x < x_end) {
+    int lo = 0, hi = NS - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (psum[mid] <= x) lo = mid;
+      else hi = mid - 1;
+    }
+    const int s = __builtin_amdgcn_readfirstlane(lo);
+    const int sp0 = __builtin_amdgcn_readfirstlane(psum[s]);
+    const int nbs = psum[s + 1] - sp0;
+    const int b0 = (int)(x - sp0);
+    const int b1 = (int)(min<long long>(x_end, (long long)sp0 + nbs) - sp0);
+    const int n = b1 - b0;
+    typedef __attribute__((address_space(4))) const int cint;
+    const int ctx = ((const cint*)a.context_lens)[s];
+    const cint* bt = (const cint*)(a.block_table + (size_t)s * a.bt_stride);
+
+    u32x4 qf[S::KS];
+    {
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.query) + ((size_t)s * H + c16) * S::ROWB + 16 * q4;
+#pragma unroll
+      for (int j = 0; j < S::KS; ++j) qf[j] = load16(qp + 64 * j);
+    }
+    f32x4 o[S::DTV];
+#pragma unroll
+    for (int t = 0; t < S::DTV; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.f;
+
+    auto issue = [&](int i) {  // copies of the segment's block i into slot i % NSL
+      const uint8_t* base = cache + (size_t)(uint32_t)bt[b0 + i] * S::BLKB;
+      const uint32_t slot = ring_lds + (uint32_t)((i & (NSL - 1)) * S::BLKB);
+#pragma unroll
+      for (int k = 0; k < S::COPIES; ++k) dma16(base, src[k], slot + 1024u * (uint32_t)k);
+    };
+    // the queries have landed before any copy is issued (a wait the compiler
+    // placed for them later would drain the copies in flight)
+    wait_vm<0>();
+#pragma unroll
+    for (int j = 0; j < NSL - 1; ++j)
+      if (j < n) issue(j);
+    for (int i = 0; i < n; ++i) {
+      // block i + NSL - 1 into the slot block i - 1 left; block i has landed
+      // once at most the blocks after it are in flight
+      if (i + NSL - 1 < n) issue(i + NSL - 1);
+      wait_blocks<S::COPIES, NSL>(min(n - 1 - i, NSL - 1));
+      const uint32_t slot = ring_lds + (uint32_t)((i & (NSL - 1)) * S::BLKB);
+      const int kend = ctx - 16 * (b0 + i);  // keys at or past kend are masked (last block only)
+
+      // ---- scores: lane holds keys 4 q4 + r of head c16. All operand reads
+      // are issued before the MFMAs, and the value operands right after
+      // them, so that one wave per SIMD does not wait out each read ----
+      f32x4 st = {0.f, 0.f, 0.f, 0.f};
+      const uint32_t kb = slot + (uint32_t)(c16 * S::ROWB);
+      u32x4 kf[S::KS];
+#pragma unroll
+      for (int j = 0; j < S::KS; ++j) kf[j] = lds_read16(kb + (uint32_t)(16 * ((4 * j + q4) ^ kswz)));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < S::KS; ++j) st = mfma_bf16(kf[j], qf[j], st);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint32_t vb = slot + vbase;
+      u32x2 vf[S::DTV];
+#pragma unroll
+      for (int t = 0; t < S::DTV; ++t) vf[t] = lds_read_tr8(vb + (uint32_t)(16 * ((2 * t + vch) ^ vswz)));
+      __builtin_amdgcn_sched_barrier(0);
+      float xv[4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = st[r] * a.scale_log2;
+        v = 4 * q4 + r < kend ? v : -INFINITY;
+        xv[r] = v;
+        tmax = fmaxf(tmax, v);
+      }
+      tmax = strided_max<16>(tmax);  // key 0 of a block is always valid
+      const bool up = tmax > m + 8.f;
+      if (__any(up)) {
+        const float alpha = up ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;
+        m = up ? tmax : m;
+        lsum *= alpha;
+#pragma unroll
+        for (int t = 0; t < S::DTV; ++t) {
+          o[t][0] *= alpha; o[t][1] *= alpha; o[t][2] *= alpha; o[t][3] *= alpha;
+        }
+      }
+      // p = 2^(x - m) <= 2^8 as bf16 hi + lo
+      uint32_t ph[2], pl[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(xv[2 * e] - m);
+        const float p1 = __builtin_amdgcn_exp2f(xv[2 * e + 1] - m);
+        lsum += p0 + p1;
+        ph[e] = pack_bf16x2(p0, p1);
+        pl[e] = pack_bf16x2(p0 - bf16_lo(ph[e]), p1 - bf16_hi(ph[e]));
+      }
+      const u32x2 phv = {ph[0], ph[1]}, plv = {pl[0], pl[1]};
+      // values of keys past the context may be anything (NaN): zero them
+      const bool edge = kend < 16;
+      uint32_t vmask[2] = {0xffffffffu, 0xffffffffu};
+      if (edge) {
+        vmask[0] = (4 * q4 < kend ? 0x0000ffffu : 0u) | (4 * q4 + 1 < kend ? 0xffff0000u : 0u);
+        vmask[1] = (4 * q4 + 2 < kend ? 0x0000ffffu : 0u) | (4 * q4 + 3 < kend ? 0xffff0000u : 0u);
+      }
+      // ---- O^T += V^T P^T over the 16 keys ----
+#pragma unroll
+      for (int t = 0; t < S::DTV; ++t) {
+        vf[t][0] &= vmask[0];
+        vf[t][1] &= vmask[1];
+        o[t] = mfma_bf16_k16(vf[t], phv, o[t]);
+        o[t] = mfma_bf16_k16(vf[t], plv, o[t]);
+      }
+    }
+    // ---- result of the segment: lane holds dims 16 t + 4 q4 + r of head c16 ----
+    const float L = strided_sum<16>(lsum);
+    const bool single = (sp0 / C) == ((sp0 + nbs - 1) / C);
+    if (single) {
+      const float inv = 1.f / L;
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)s * H + c16) * MLA_DV + 4 * q4;
+#pragma unroll
+      for (int t = 0; t < S::DTV; ++t) {
+        uint2 wv;
+        wv.x = pack_bf16x2(o[t][0] * inv, o[t][1] * inv);
+        wv.y = pack_bf16x2(o[t][2] * inv, o[t][3] * inv);
+        *reinterpret_cast<uint2*>(op + 16 * t) = wv;
+      }
+    } else {
+      const size_t rec = (size_t)(w + s) * H + c16;
+      float* op = a.part_o + rec * MLA_DV + 4 * q4;
+#pragma unroll
+      for (int t = 0; t < S::DTV; ++t) *reinterpret_cast<f32x4*>(op + 16 * t) = o[t];
+      if (q4 == 0) {
+        a.part_ml[rec * 2] = m;
+        a.part_ml[rec * 2 + 1] = L;
+      }
+    }
+    x = (long long)sp0 + b1;
+  }
+}
+
 // Exact merge of a (sequence, head)'s summaries, one wave each: the
 // workgroups w0..w1 covering the sequence left theirs in slot w + s.
 template <int H>
@@ -452,16 +710,23 @@ __global__ __launch_bounds__(256) void mla_merge(MlaArgs a) {
     reinterpret_cast<uint16_t*>(a.out)[((size_t)s * H + h) * MLA_DV + 64 * k + lane] = f32_to_bf16(acc[k] * inv);
 }
 
+// Summary slots: one per worker (a workgroup; a wave for 16 heads) plus one
+// per sequence (a worker's segments each advance the sequence or the worker).
+static size_t mla_slots(int num_seqs, int num_heads, int grid) {
+  const size_t workers = (size_t)grid * (num_heads == 16 ? kNarrowWaves : 1);
+  return workers + (size_t)num_seqs;
+}
+
 size_t mla_workspace_bytes(int num_seqs, int num_heads, int grid) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t slots = (size_t)grid + (size_t)num_seqs;
+  const size_t slots = mla_slots(num_seqs, num_heads, grid);
   return al((size_t)(num_seqs + 2) * sizeof(int)) + al(slots * num_heads * MLA_DV * sizeof(float)) +
          al(slots * num_heads * 2 * sizeof(float));
 }
 
 void mla_bind_workspace(MlaArgs& a, void* workspace, int num_seqs, int num_heads, int grid) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t slots = (size_t)grid + (size_t)num_seqs;
+  const size_t slots = mla_slots(num_seqs, num_heads, grid);
   char* ws = static_cast<char*>(workspace);
   a.meta = reinterpret_cast<int*>(ws);
   ws += al((size_t)(num_seqs + 2) * sizeof(int));
@@ -478,7 +743,10 @@ static hipError_t run_mla(const MlaArgs& a, int grid, hipStream_t st) {
   // halves the LDS operand reads, measured slower: one wave per SIMD hides
   // the LDS latency worse, and at 128 heads the registers spill.)
   constexpr int NW = 8, HG = 1;
-  hipLaunchKernelGGL((mla_decode_split<DK, H, NW, HG>), dim3((unsigned)grid), dim3(64 * NW), 0, st, a);
+  if constexpr (H == 16)  // the waves split the keys
+    hipLaunchKernelGGL((mla_decode_narrow<DK>), dim3((unsigned)grid), dim3(64 * kNarrowWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((mla_decode_split<DK, H, NW, HG>), dim3((unsigned)grid), dim3(64 * NW), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((mla_merge<H>), dim3((unsigned)((a.num_seqs * H + 3) / 4)), dim3(256), 0, st, a);

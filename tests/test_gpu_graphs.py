@@ -118,17 +118,18 @@ def test_sparse_decode_graph():
     check_graph(step, [out], perturb, "sparse decode")
 
 
-def test_mla_decode_graph():
-    b = W.make_mla_batch("graph_mla", 953, [1, 700, 20000], 128, 576, device=DEV)
-    out = torch.empty((3, 128, 512), dtype=torch.bfloat16, device=DEV)
-    ws = torch.empty(pa.mla_decode_workspace_bytes(3, 128), dtype=torch.uint8, device=DEV)
+@pytest.mark.parametrize("H", [128, 16])
+def test_mla_decode_graph(H):
+    b = W.make_mla_batch(f"graph_mla{H}", 953, [1, 700, 20000], H, 576, device=DEV)
+    out = torch.empty((3, H, 512), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(pa.mla_decode_workspace_bytes(3, H), dtype=torch.uint8, device=DEV)
     bt = torch.from_numpy(b.block_table).to(DEV)
     cl = torch.from_numpy(b.context_lens).to(DEV)
 
     def step():
         pa.mla_decode(out, b.query, b.cache, bt, cl, b.max_context_len, b.scale, ws)
 
-    check_graph(step, [out], _perturb_query(b.query), "latent-cache decode")
+    check_graph(step, [out], _perturb_query(b.query), f"latent-cache decode, {H} heads")
 
 
 def test_partial_and_merge_graph():

@@ -79,6 +79,16 @@ def test_mla_few_long_sequences():
     check(b, out, [0, 1, 2], "mla few long")
 
 
+@pytest.mark.parametrize("DK", [576, 512])
+def test_mla_16_heads_long_and_short(DK):
+    """16 heads take the kernel whose waves split the keys: long sequences
+    spread over many waves and merged, short ones finished in place."""
+    b = W.make_mla_batch(f"mla16_{DK}", 1102 + DK, [70000, 3, 40000, 1, 17, 2500], 16, DK, device=DEV)
+    out = run_mla(b)
+    torch.cuda.synchronize()
+    check(b, out, range(b.num_seqs), f"mla 16 heads dk={DK}")
+
+
 def test_mla_benchmark_batch_sampled():
     b = W.make_mla_config(device=DEV)
     out = run_mla(b)
