@@ -2,9 +2,10 @@
 
 Unowned slots of the pool are NaN, so a read outside a context shows.
 Cases: ragged contexts from 1 token to several thousand for every head count
-(16, 32, 64, 128) and both row widths (512, 576); a batch of many short
-sequences (each finished inside one workgroup) and few long ones (split over
-many workgroups and merged); the benchmark's batch on sampled sequences.
+(16, 32, 64, 128) and both row widths (512, 576); batches of many short
+sequences (each finished inside one worker; up to the 2048-sequence limit)
+and few long ones (split over many workers and merged), for the 16-head
+kernel too; the benchmark's batch on sampled sequences.
 """
 
 import numpy as np
@@ -63,13 +64,14 @@ def test_mla_small(H, DK):
     check(b, out, range(b.num_seqs), f"mla H={H} dk={DK}")
 
 
-def test_mla_many_short_sequences():
+@pytest.mark.parametrize("H,S", [(64, 1500), (16, 2048)])
+def test_mla_many_short_sequences(H, S):
     rng = np.random.default_rng(5)
-    ctx = rng.integers(1, 200, 1500).tolist()
-    b = W.make_mla_batch("mla_short", 1100, ctx, 64, 576, device=DEV)
+    ctx = rng.integers(1, 200, S).tolist()
+    b = W.make_mla_batch(f"mla_short{H}", 1100, ctx, H, 576, device=DEV)
     out = run_mla(b)
     torch.cuda.synchronize()
-    check(b, out, list(range(0, 1500, 97)) + [1499], "mla many short")
+    check(b, out, list(range(0, S, 97)) + [S - 1], f"mla many short, {H} heads")
 
 
 def test_mla_few_long_sequences():
