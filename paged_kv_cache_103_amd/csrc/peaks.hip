@@ -27,7 +27,10 @@ __global__ __launch_bounds__(256) void read_tiles(const u32x4* __restrict__ p, c
       const int off = MODE == 0 ? 64 * j + lane : (lane & 15) * 16 + 4 * j + (lane >> 4);
       a[j] = __builtin_nontemporal_load(base + off);
     }
-    acc ^= a[0].x ^ a[1].y ^ a[2].z ^ a[3].w;
+    // every component is used, so that each load stays a 16-byte load (a
+    // partly used vector is narrowed to 4-byte loads by the compiler)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc ^= a[j].x ^ a[j].y ^ a[j].z ^ a[j].w;
   }
   if (threadIdx.x == 0) sink[blockIdx.x] = acc;
 }
