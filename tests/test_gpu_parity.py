@@ -271,6 +271,21 @@ def test_mixed_step_sampled():
     _log(f"mixed_step chunk: rows {rows}, max abs {ma:.2e}, max rel {mr:.2e}")
 
 
+def test_prefill_fp8_chunk_sampled():
+    """The 2048-token chunk on a 65,536-token prefix over an fp8 e4m3 cache
+    with per-block scales: the batch and launch the fp8 chunk timing uses,
+    sampled rows across the tiles (first and last tile, a tile edge)."""
+    b = W.make_batch("mixed_step_chunk_fp8", 4, [65536 + 2048], [2048], 32, 8, 128, "bf16", "fp8_e4m3",
+                     device=DEV)
+    out = run_prefill(b)
+    torch.cuda.synchronize()
+    ref = oracle_rows(b, [0])[0]
+    got = out_f64(out)
+    rows = [0, 1, 63, 64, 1000, 1983, 2046, 2047]
+    ma, mr = assert_close(got[rows], ref[rows], "fp8 chunk rows")
+    _log(f"fp8 chunk: rows {rows}, max abs {ma:.2e}, max rel {mr:.2e}")
+
+
 # ----------------------------------------------------------------------------
 # small ragged batches: decode and chunked prefill
 # ----------------------------------------------------------------------------
