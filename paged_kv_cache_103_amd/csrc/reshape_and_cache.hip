@@ -22,15 +22,27 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const float* __restrict__ k_scale, const float* __restrict__ v_scale,
     const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads, int head_size) {
   typedef typename CacheElem<CK>::T CT;
-  const int chunks = head_size >> 3;
+  const int cshift = head_size == 128 ? 4 : 3;  // 8-element chunks per row: 16 or 8
+  const int chunks = 1 << cshift;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
   if (idx >= total) return;
-  const int c = (int)(idx % chunks);
-  const int h = (int)((idx / chunks) % num_kv_heads);
-  const int64_t t = idx / ((int64_t)chunks * num_kv_heads);
+  const int c = (int)(idx & (chunks - 1));
+  int h;
+  int64_t t;
+  if (total <= 0x7fffffff) {  // uniform; 32-bit division (64-bit is a long emulated sequence)
+    const uint32_t r = (uint32_t)idx >> cshift;
+    h = (int)(r % (uint32_t)num_kv_heads);
+    t = r / (uint32_t)num_kv_heads;
+  } else {
+    h = (int)((idx >> cshift) % num_kv_heads);
+    t = (idx >> cshift) / num_kv_heads;
+  }
+  // the row loads below do not depend on the slot: each branch issues them
+  // before it tests the slot, so the two memory latencies overlap (rows of
+  // skipped tokens are read too: they are inside key and value)
   const int64_t slot = slot_mapping[t];
-  if (slot < 0) return;
+  const bool skip = slot < 0;
   const int64_t blk = slot >> 4;
   const int off = (int)(slot & 15);
   const int d0 = c << 3;
@@ -45,9 +57,11 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     // bit copy
     if constexpr (sizeof(IT) == 4) {
       u32x4 a = load16(ksrc), b = load16(ksrc + 4);
+      u32x4 va = load16(vsrc), vb = load16(vsrc + 4);
+      __asm__ volatile("" ::"v"(a), "v"(b), "v"(va), "v"(vb));  // keeps the loads above the test
+      if (skip) return;
       *reinterpret_cast<u32x4*>(kdst) = a;
       *reinterpret_cast<u32x4*>(kdst + 4) = b;
-      u32x4 va = load16(vsrc), vb = load16(vsrc + 4);
       const uint32_t* w = reinterpret_cast<const uint32_t*>(&va);
       const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vb);
 #pragma unroll
@@ -56,8 +70,10 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
       for (int e = 0; e < 4; ++e) reinterpret_cast<uint32_t*>(vdst)[(e + 4) * 16] = w2[e];
     } else if constexpr (sizeof(IT) == 2) {
       u32x4 a = load16(ksrc);
-      *reinterpret_cast<u32x4*>(kdst) = a;
       u32x4 v = load16(vsrc);
+      __asm__ volatile("" ::"v"(a), "v"(v));  // keeps the loads above the test
+      if (skip) return;
+      *reinterpret_cast<u32x4*>(kdst) = a;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         vdst[(2 * e) * 16] = (CT)(v[e] & 0xffffu);
@@ -65,8 +81,10 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
       }
     } else {
       uint2 a = *reinterpret_cast<const uint2*>(ksrc);
-      *reinterpret_cast<uint2*>(kdst) = a;
       uint2 v = *reinterpret_cast<const uint2*>(vsrc);
+      __asm__ volatile("" ::"v"(a.x), "v"(a.y), "v"(v.x), "v"(v.y));  // keeps the loads above the test
+      if (skip) return;
+      *reinterpret_cast<uint2*>(kdst) = a;
 #pragma unroll
       for (int e = 0; e < 4; ++e) vdst[e * 16] = (CT)((v.x >> (8 * e)) & 0xff);
 #pragma unroll
@@ -88,6 +106,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
         vx[2 * e] = bf16_lo(b[e]); vx[2 * e + 1] = bf16_hi(b[e]);
       }
     }
+    if (skip) return;
     const float ks = k_scale[blk], vs = v_scale[blk];
     uint8_t kb[8], vb[8];
 #pragma unroll
