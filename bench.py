@@ -385,7 +385,36 @@ def chunk_of(mb):
     return chunk
 
 
-def run_config(pa, torch, W, name, steps, warmup, shared_prefix=False):
+def graph_call_us(torch, attend, calls=16, replays=20):
+    """Mean device time of one attend call when `calls` of them are captured
+    back to back in one HIP graph and the graph is replayed: the figure a
+    serving loop that replays its small launches sees, without this
+    script's per-call host overhead (ctypes marshalling and the launch)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        attend()  # outside the capture: first-call work stays out of the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            attend()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / (replays * calls)
+    del g
+    return us
+
+
+def run_config(pa, torch, W, name, steps, warmup, shared_prefix=False, graph=False):
     b = W.make_config(name, device="cuda")
     torch.cuda.synchronize()
     prefill = b.max_q_len > 1
@@ -399,6 +428,8 @@ def run_config(pa, torch, W, name, steps, warmup, shared_prefix=False):
     res["kv_gbs_attend"] = res["kv_bytes"] / (attend_ms * 1e-3) / 1e9
     res["unique_gbs_attend"] = res["unique_kv_bytes"] / (attend_ms * 1e-3) / 1e9
     res["tokens_per_s"] = b.num_q_tokens / (step_ms * 1e-3)
+    if graph:
+        res["attend_us_graph_replay"] = graph_call_us(torch, attend)
     return b, res
 
 
@@ -528,10 +559,13 @@ def main():
         extra["context_parallel_llama8b"] = run_context_parallel(pa, torch, W, 8, max(10, args.steps // 2),
                                                                  args.warmup)
         for name in ("tiny_decode", "agentic_decode", "fp8_decode", "fp8_swa128"):
-            eb, r = run_config(pa, torch, W, name, max(5, args.steps // 2), args.warmup)
+            # the launch-bound ones also replayed from a graph
+            small = name in ("tiny_decode", "fp8_swa128")
+            eb, r = run_config(pa, torch, W, name, max(5, args.steps // 2), args.warmup, graph=small)
             extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
             log(f"{name}: pa_decode {r['attend_ms']*1e3:.1f} us, {r['kv_gbs_attend']:.0f} GB/s logical, "
-                f"{r['unique_gbs_attend']:.0f} GB/s unique")
+                f"{r['unique_gbs_attend']:.0f} GB/s unique"
+                + (f"; {r['attend_us_graph_replay']:.1f} us per call replayed from a graph" if small else ""))
             del eb
             torch.cuda.empty_cache()
         # the agentic batch again, its groups' shared prefix blocks read once
