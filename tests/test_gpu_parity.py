@@ -369,7 +369,7 @@ def test_random_shapes():
     """Seeded random small shapes over head size, group size, dtypes, context,
     chunk length and window (decode and prefill)."""
     rng = np.random.default_rng(777)
-    for it in range(24):
+    for it in range(64):
         D = int(rng.choice([64, 128]))
         G = int(rng.choice([1, 2, 4, 8, 16]))
         Hkv = int(rng.choice([1, 2, 4]))
@@ -385,6 +385,28 @@ def test_random_shapes():
         out = run_prefill(b)
         torch.cuda.synchronize()
         check_rows(b, out, range(S), f"random case {it}")
+
+
+def test_random_decode_shapes():
+    """Seeded random decode batches through pa_decode: head size, group size,
+    KV heads, bf16/fp8/fp32 caches, contexts long (split work, merged) and
+    short (a wave per stream), sliding windows."""
+    rng = np.random.default_rng(778)
+    for it in range(64):
+        D = int(rng.choice([64, 128]))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        cd = str(rng.choice(["bf16", "bf16", "fp8_e4m3", "f32"]))
+        qd = "f32" if cd == "f32" else "bf16"
+        S = int(rng.integers(1, 9))
+        ctx = rng.integers(1, 300 if rng.random() < 0.3 else 6000, S)
+        w = int(rng.choice([0, 0, int(rng.integers(1, 300))]))
+        b = W.make_batch(f"rdec{it}", 500 + it, ctx.tolist(), [1] * S, G * Hkv, Hkv, D, qd, cd,
+                         sliding_window=w, device=DEV, extra_blocks=int(rng.integers(0, 5)))
+        _log(f"random decode {it}: D {D} G {G} Hkv {Hkv} {qd}/{cd} ctx {ctx.tolist()} W {w}")
+        out = run_decode(b)
+        torch.cuda.synchronize()
+        check_rows(b, out, range(S), f"random decode {it}")
 
 
 # ----------------------------------------------------------------------------
