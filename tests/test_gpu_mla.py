@@ -97,3 +97,20 @@ def test_mla_benchmark_batch_sampled():
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
     check(b, out, [0, 21, 42, 63], "mla benchmark batch")
+
+
+def test_mla_random_shapes():
+    """Seeded random latent-cache batches: head counts, row widths, batch
+    sizes, contexts short and long."""
+    rng = np.random.default_rng(1200)
+    for it in range(24):
+        H = int(rng.choice([16, 32, 64, 128]))
+        DK = int(rng.choice([512, 576]))
+        S = int(rng.integers(1, 9))
+        ctx = rng.integers(1, 300 if rng.random() < 0.3 else 6000, S).tolist()
+        _log(f"mla random {it}: H {H} dk {DK} ctx {ctx}")
+        b = W.make_mla_batch(f"mla_rand{it}", 1300 + it, ctx, H, DK, device=DEV,
+                             extra_blocks=int(rng.integers(0, 5)))
+        out = run_mla(b)
+        torch.cuda.synchronize()
+        check(b, out, range(S), f"mla random {it}")

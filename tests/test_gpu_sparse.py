@@ -135,3 +135,24 @@ def test_sparse_long_context_sampled():
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
     check(b, choice, out, [0, 17, 40, 63], "sparse long context")
+
+
+def test_sparse_random_shapes():
+    """Seeded random sparse batches: head size, group size, KV heads, cache
+    dtype, contexts and the number of chosen blocks (also beyond a short
+    context's earlier blocks)."""
+    rng = np.random.default_rng(1400)
+    for it in range(24):
+        D = int(rng.choice([64, 128]))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        cd = str(rng.choice(["bf16", "bf16", "fp8_e4m3"]))
+        S = int(rng.integers(1, 7))
+        ctx = rng.integers(1, 8000, S).tolist()
+        k = int(rng.integers(0, 300))
+        _log(f"sparse random {it}: ctx {ctx}, k {k}, {G * Hkv}/{Hkv} d{D} {cd}")
+        b, choice = W.make_sparse_batch(f"sparse_rand{it}", 1500 + it, ctx, k, G * Hkv, Hkv, D, "bf16", cd,
+                                        device=DEV, noise=True)
+        out = run_sparse(b, choice)
+        torch.cuda.synchronize()
+        check(b, choice, out, range(S), f"sparse random {it}")
