@@ -237,6 +237,35 @@ def test_decode_shared_prefix_small(case):
     check_rows(b, out, range(b.num_seqs), f"shared-prefix case {case}")
 
 
+def test_decode_shared_prefix_random():
+    """Seeded random shared-prefix batches: groups of consecutive sequences
+    (singletons too), prefix lengths up to and beyond what every member
+    holds, head and group sizes, bf16/fp8 caches."""
+    rng = np.random.default_rng(779)
+    for it in range(32):
+        D = int(rng.choice([64, 128]))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        cd = str(rng.choice(["bf16", "bf16", "fp8_e4m3"]))
+        S = int(rng.integers(1, 13))
+        base = int(rng.integers(1, 4000))
+        ctx = [max(1, base + int(rng.integers(-40, 200))) for _ in range(S)]
+        sg, s0 = [], 0
+        while s0 < S:
+            n = int(rng.integers(1, S - s0 + 1))
+            sg.append(list(range(s0, s0 + n)))
+            s0 += n
+        sp = {gi: int(rng.integers(0, base + 100)) for gi in range(len(sg))}
+        sp_blocks = {gi: max(0, min(p, min(ctx[s] for s in sg[gi]) - 1)) // 16 * 16 for gi, p in sp.items()}
+        _log(f"shared random {it}: D {D} G {G} Hkv {Hkv} {cd} ctx {ctx} groups {sg} prefix {sp}")
+        b = W.make_batch(f"shr{it}", 800 + it, ctx, [1] * S, G * Hkv, Hkv, D, "bf16", cd,
+                         shared_groups=sg, shared_prefix=sp_blocks, device=DEV, extra_blocks=2)
+        b.shared_prefix = sp  # the call gets the unclamped lengths
+        out = run_decode_shared(b)
+        torch.cuda.synchronize()
+        check_rows(b, out, range(S), f"shared random {it}")
+
+
 def test_decode_fp8_sampled():
     b = W.make_config("fp8_decode", device=DEV)
     out = run_decode(b)
