@@ -88,6 +88,14 @@ DCP_CASES = [
     ([1500, 257, 40], 3, 32, 8, 128, "bf16", False),
     ([200, 33, 256, 1], 2, 32, 8, 128, "bf16", True),  # every range short: a wave per stream, empty ranges
 ]
+# and seeded random ones (cuts off block boundaries with bf16 caches only, as above)
+_rng = np.random.default_rng(901)
+for _ in range(12):
+    _hkv, _g = int(_rng.choice([1, 2, 4, 8])), int(_rng.choice([1, 2, 4, 8, 16]))
+    _cd = str(_rng.choice(["bf16", "bf16", "fp8_e4m3"]))
+    DCP_CASES.append((_rng.integers(1, 6000, int(_rng.integers(1, 7))).tolist(), int(_rng.integers(2, 9)),
+                      _g * _hkv, _hkv, int(_rng.choice([64, 128])), _cd,
+                      _cd != "bf16" or bool(_rng.random() < 0.6)))
 
 
 @pytest.mark.parametrize("case", range(len(DCP_CASES)))
