@@ -59,6 +59,7 @@
  *  cu_seqlens[0] = 0, cu_seqlens[num_seqs] = num_q_tokens, q_len(s) <= max_q_len;
  *  slots of one write call are unique and name blocks the writer owns
  *  exclusively (a shared non-full block is copied before it is written).
+ *  pa_check_batch checks all of these on host copies of the metadata.
  *
  * Determinism: identical inputs and sizes give bitwise identical outputs.
  */
@@ -132,6 +133,29 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
                     int32_t head_size, int32_t block_size, int32_t num_blocks, pa_dtype q_dtype,
                     pa_dtype cache_dtype, float scale, int32_t sliding_window, void* workspace,
                     size_t workspace_bytes, pa_stream_t stream);
+
+/*
+ * pa_decode on the vector-ALU kernel, whatever the cache type: scores as
+ * packed-bf16 dot products reduced across the wave with DPP row shuffles,
+ * the online-softmax max and sum by the same shuffles, weights passed to the
+ * value lanes through LDS, split-K partitions merged by log-sum-exp. This is
+ * the design the grouped-query decode was first planned on; pa_decode serves
+ * bf16 and fp8 caches on matrix cores instead (a grouped-query step is a
+ * (group x head_size)(head_size x keys) product, so the dot products cost
+ * no vector-ALU time there). Kept as an entry point of its own so that the
+ * two can be measured side by side on the same batch; it computes the same
+ * attention ("大模型推理优化学习笔记", "Decode": decode is memory-bound, each
+ * step reading the whole KV cache). Arguments, layouts, support and errors
+ * are pa_decode's; the workspace must hold
+ * pa_decode_valu_workspace_bytes(...) bytes.
+ */
+pa_status pa_decode_valu(void* out, const void* query, const void* k_cache, const void* v_cache,
+                         const float* k_scale, const float* v_scale, const int32_t* block_table,
+                         int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                         int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                         int32_t block_size, int32_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype,
+                         float scale, int32_t sliding_window, void* workspace, size_t workspace_bytes,
+                         pa_stream_t stream);
 
 /*
  * Decode attention where runs of consecutive sequences share the physical
@@ -270,6 +294,14 @@ pa_status pa_merge_partials(void* out, float* lse_out, const void* parts, const 
  *   [num_seqs][num_heads][512]; head_dim_v must be 512.
  * num_heads: 16, 32, 64 or 128; num_seqs at most 2048; context_lens[s] >= 1.
  * workspace: pa_mla_decode_workspace_bytes(num_seqs, num_heads) bytes.
+ * Numerics: scores on bf16 matrix cores with fp32 accumulation. With 16
+ *   heads the weighted sum multiplies the bf16 rows by the weights split
+ *   into bf16 hi + lo (16 significant bits). With more heads the rows'
+ *   value part is converted to fp16 and the weights scaled by 2^7 into fp16
+ *   (11 significant bits): exact for |c| in [2^-14, 65504]; a row whose
+ *   values overflow fp16 comes out non-finite there and is then computed
+ *   again in fp32 by the merge step. Any finite cached value gives a finite
+ *   result as long as the fp32 sums stay in range.
  */
 pa_status pa_mla_decode(void* out, const void* query, const void* latent_cache, const int32_t* block_table,
                         int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
@@ -290,6 +322,15 @@ size_t pa_mla_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads);
  * scalars bounding the device arrays.
  * Supported as pa_decode, except that chunks longer than one token need
  *   q_dtype BF16 (cache BF16 or FP8_E4M3).
+ * Numerics of the chunks: scores on bf16 matrix cores (fp8 keys widened to
+ *   bf16 exactly, the block scale applied to the fp32 score), fp32
+ *   accumulation. The weighted sum of values runs on fp16 matrix cores: the
+ *   values (bf16, or e4m3 times the block scale) rounded to fp16, the
+ *   weights scaled by 2^7 into fp16 (11 significant bits). A tile of query
+ *   rows whose values reach beyond fp16's range (|v| > 65504) is computed
+ *   again with the values in bf16 (exact) against the weights split into
+ *   bf16 hi + lo, so every finite cached value is in the domain; the fp32
+ *   accumulator needs 2^15 * sum_j |v_j| below 3.4e38.
  */
 pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, const void* v_cache,
                            const float* k_scale, const float* v_scale, const int32_t* block_table,
@@ -311,6 +352,11 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len, int3
                                  int32_t num_kv_heads, int32_t head_size, pa_dtype cache_dtype,
                                  int32_t sliding_window);
 
+/* Workspace bytes pa_decode_valu needs for these sizes (0 if none). */
+size_t pa_decode_valu_workspace_bytes(int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_size, pa_dtype cache_dtype,
+                                      int32_t sliding_window);
+
 /* Workspace bytes pa_decode_shared_prefix needs for these sizes (0 if none). */
 size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_groups, int32_t max_context_len,
                                                int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
@@ -326,6 +372,30 @@ size_t pa_decode_sparse_workspace_bytes(int32_t num_seqs, int32_t max_selected, 
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len,
                                   int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
                                   int32_t head_size, pa_dtype cache_dtype, int32_t sliding_window);
+
+/*
+ * Checks a batch's metadata, on HOST copies, against the device-side
+ * preconditions listed at the top of this header (which the kernels never
+ * check): for each sequence 1 <= context_lens[s] <= max_context_len and
+ * ceil(context_lens[s]/16) <= block_table_stride; every block id the
+ * attention reads (from the first query's window start to the newest block)
+ * in [0, num_blocks); with cu_seqlens (else a decode batch, num_q_tokens ==
+ * num_seqs): cu_seqlens[0] = 0, cu_seqlens[num_seqs] = num_q_tokens and
+ * 1 <= q_len(s) <= min(context_lens[s], max_q_len). With slot_mapping
+ * ([num_q_tokens] int64; NULL skips the write checks): every non-negative
+ * slot is its token's position in its own sequence's table (query row r
+ * of sequence s at position context_lens[s] - q_len(s) + r), no slot twice,
+ * and no written block mapped by any other (sequence, logical block) entry
+ * of the batch: a block shared through a prefix is copied before it is
+ * written ("从静态批处理到状态化推理集群", "Prefix reuse：分页让细粒度共享更便宜").
+ * Returns PA_OK, or PA_ERR_INVALID_ARGUMENT with the first violation in
+ * pa_last_error(). Touches no device memory; cost O(num_blocks + read
+ * blocks + num_q_tokens).
+ */
+pa_status pa_check_batch(const int32_t* block_table, int32_t block_table_stride, const int32_t* context_lens,
+                         const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len,
+                         int32_t max_context_len, int32_t num_blocks, int32_t sliding_window,
+                         const int64_t* slot_mapping);
 
 /* Static name of a status code. */
 const char* pa_status_string(pa_status s);

@@ -33,6 +33,7 @@ BLOCK_SIZE = 16
 EXPORTED = (
     "pa_reshape_and_cache",
     "pa_decode",
+    "pa_decode_valu",
     "pa_decode_shared_prefix",
     "pa_decode_sparse",
     "pa_decode_partial",
@@ -41,9 +42,11 @@ EXPORTED = (
     "pa_mla_decode_workspace_bytes",
     "pa_prefill_chunk",
     "pa_decode_workspace_bytes",
+    "pa_decode_valu_workspace_bytes",
     "pa_decode_shared_prefix_workspace_bytes",
     "pa_decode_sparse_workspace_bytes",
     "pa_prefill_workspace_bytes",
+    "pa_check_batch",
     "pa_status_string",
     "pa_last_error",
     "pa_abi_version",
@@ -74,6 +77,12 @@ def load() -> ctypes.CDLL:
     L.pa_decode.restype = ctypes.c_int
     L.pa_decode.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32,
                             ctypes.c_int, ctypes.c_int, ctypes.c_float, i32, vp, sz, vp]
+    L.pa_decode_valu.restype = ctypes.c_int
+    L.pa_decode_valu.argtypes = L.pa_decode.argtypes
+    L.pa_decode_valu_workspace_bytes.restype = sz
+    L.pa_decode_valu_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, i32]
+    L.pa_check_batch.restype = ctypes.c_int
+    L.pa_check_batch.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     L.pa_decode_shared_prefix.restype = ctypes.c_int
     L.pa_decode_shared_prefix.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i32, vp, i32, i32, vp, vp, i32, i32,
                                           i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_float, i32,
@@ -173,6 +182,33 @@ def decode_workspace_bytes(num_seqs: int, max_context_len: int, num_heads: int, 
                                                 head_size, _cache_code(cache_dtype), sliding_window))
 
 
+def decode_valu_workspace_bytes(num_seqs: int, max_context_len: int, num_heads: int, num_kv_heads: int,
+                                head_size: int, cache_dtype="bf16", sliding_window: int = 0) -> int:
+    """Bytes of device workspace pa_decode_valu needs."""
+    return int(load().pa_decode_valu_workspace_bytes(num_seqs, max_context_len, num_heads, num_kv_heads,
+                                                     head_size, _cache_code(cache_dtype), sliding_window))
+
+
+def check_batch(block_table, context_lens, num_blocks: int, max_context_len: int, cu_seqlens=None,
+                max_q_len: int = 1, sliding_window: int = 0, slot_mapping=None) -> None:
+    """pa_check_batch on host (numpy) copies of a batch's metadata: raises
+    PAError naming the first violated precondition."""
+    import numpy as np
+
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    S = int(cl.shape[0])
+    cu = None if cu_seqlens is None else np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    sm = None if slot_mapping is None else np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    nq = S if cu is None else int(cu[-1])
+    if sm is not None and sm.shape[0] != nq:
+        raise ValueError(f"slot_mapping has {sm.shape[0]} entries for {nq} query tokens")
+    stride = int(bt.shape[1]) if bt.ndim == 2 else 0
+    p = lambda a: None if a is None else a.ctypes.data
+    _check(load().pa_check_batch(p(bt), stride, p(cl), p(cu), S, nq, int(max_q_len), int(max_context_len),
+                                 int(num_blocks), int(sliding_window), p(sm)))
+
+
 def decode_shared_prefix_workspace_bytes(num_seqs: int, num_groups: int, max_context_len: int, num_heads: int,
                                          num_kv_heads: int, head_size: int, cache_dtype="bf16",
                                          sliding_window: int = 0) -> int:
@@ -217,6 +253,21 @@ def decode(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cach
                             S, int(max_context_len), Hq, Hkv, D, k_cache.shape[2], NB,
                             dtype_code(query.dtype), dtype_code(k_cache.dtype), float(scale),
                             int(sliding_window), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def decode_valu(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                block_table: torch.Tensor, context_lens: torch.Tensor, max_context_len: int, scale: float,
+                k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                sliding_window: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """pa_decode_valu: pa_decode on the vector-ALU kernel (same arguments)."""
+    S, Hq, D = query.shape
+    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().pa_decode_valu(_ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                 _ptr(v_scale), _ptr(block_table), block_table.shape[1], _ptr(context_lens),
+                                 S, int(max_context_len), Hq, Hkv, D, k_cache.shape[2], NB,
+                                 dtype_code(query.dtype), dtype_code(k_cache.dtype), float(scale),
+                                 int(sliding_window), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def decode_shared_prefix(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -38,6 +38,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -436,31 +438,32 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // host side: plan and dispatch
 // ---------------------------------------------------------------------------
+// Compute units of the calling thread's current device, asked once per
+// device (the grids of the split plans are sized by it).
 int device_cu_count() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
   }
-  return cus;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 // Which decode kernel serves a request: the matrix-core kernel for bf16/fp8
 // caches (any group up to 16 query heads per KV head), the VALU kernel for
-// fp32 caches. PA_DECODE_KERNEL=valu forces the VALU kernel (diagnostics and
-// side-by-side measurement).
+// fp32 caches (and for every cache type when the caller asks for it:
+// pa_decode_valu, kept for side-by-side measurement).
 bool decode_uses_mfma(int q_kind, int cache_kind, int group) {
-  const char* v = getenv("PA_DECODE_KERNEL");
-  if (v && strcmp(v, "valu") == 0) return false;
   return q_kind == KBF16 && (cache_kind == KBF16 || cache_kind == KFP8) && group <= 16;
 }
 
 DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num_kv_heads, int head_size,
-                       int q_kind, int cache_kind, int sliding_window) {
+                       int q_kind, int cache_kind, int sliding_window, bool force_valu) {
   DecodePlan plan{};
   const int G = std::max(1, num_heads / std::max(1, num_kv_heads));
   // (the matrix-core kernel keeps per-sequence prefix sums in LDS: up to
@@ -468,7 +471,7 @@ DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num
   int max_blocks = (max_context_len + 15) / 16;
   if (sliding_window > 0) max_blocks = std::min(max_blocks, (sliding_window + 15) / 16 + 1);
   if (max_blocks < 1) max_blocks = 1;
-  if (decode_uses_mfma(q_kind, cache_kind, G) && num_seqs <= 16000) {
+  if (!force_valu && decode_uses_mfma(q_kind, cache_kind, G) && num_seqs <= 16000) {
     // two resident workgroups of four waves per CU
     plan.split_waves = 8 * device_cu_count();
     plan.pb = 0;
@@ -489,11 +492,6 @@ DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num
     const long long half = (max_blocks + 1) / 2;
     const long long items = (long long)num_seqs * num_kv_heads * ((half + cand - 1) / cand);
     if (items >= target) { pb = cand; break; }
-  }
-  // PA_DECODE_PB (a power of two >= 2) overrides the choice for measurements.
-  if (const char* v = getenv("PA_DECODE_PB")) {
-    const int f = atoi(v);
-    if (f >= 2 && (f & (f - 1)) == 0) pb = f;
   }
   plan.pb = pb;
   plan.max_parts = (max_blocks + pb - 1) / pb;

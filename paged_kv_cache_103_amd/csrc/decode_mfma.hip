@@ -595,6 +595,9 @@ __global__ __launch_bounds__(256) void decode_split_merge(DecodeArgs a) {
   if (idx >= a.num_seqs * a.num_heads) return;
   const int H = a.num_kv_heads, G = a.num_heads / H, NSEQ = a.num_seqs;
   const int s = idx / a.num_heads, hq = idx % a.num_heads, g = hq / G, h = hq % G;
+  // rows of longer chunks in a mixed batch belong to the prefill kernel,
+  // which may run concurrently: never write them
+  if (a.cu_seqlens != nullptr && a.cu_seqlens[s + 1] - a.cu_seqlens[s] != 1) return;
   const int* psum = a.meta + 1;
   const int C = a.meta[0];
   // the sequence's own stream: segments w0..w1, summary slot w + stream

@@ -27,6 +27,10 @@
 //    the B operand, keys in the permuted row order that makes each lane's
 //    score accumulator its own P^T operand), online softmax with lazy
 //    rescaling, O^T += V^T P^T on 16x16x32 fp16 MFMAs with P scaled by 2^7.
+//    A value beyond fp16's range (65504) becomes infinity in the tile and
+//    leaves inf or NaN in the outputs of every head; the merge kernel finds
+//    such rows and computes them again exactly (fp32, from the bf16 rows), so
+//    every finite cached value is in the call's domain.
 // The concatenated (sequence, pair of blocks) streams are split evenly over
 // the workgroups; a sequence covered by one workgroup is finished in place,
 // others leave (max, sum, unnormalised output) summaries that a second kernel
@@ -671,10 +675,50 @@ __global__ __launch_bounds__(64 * kNarrowWaves) __attribute__((amdgpu_waves_per_
   }
 }
 
+// One (sequence, head) row computed directly, by one wave, in fp32 from the
+// bf16 rows: online softmax over every key of the sequence (lane l holds
+// dims l + 64 k). Slow; it serves the rows whose fp16 value tiles overflowed.
+template <int DK, int H>
+__device__ void mla_row_exact(const MlaArgs& a, int s, int h, int lane) {
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.query) + ((size_t)s * H + h) * DK;
+  float qv[DK / 64];
+#pragma unroll
+  for (int k = 0; k < DK / 64; ++k) qv[k] = bf16_to_f32(q[64 * k + lane]);
+  const int ctx = a.context_lens[s];
+  const int* bt = a.block_table + (size_t)s * a.bt_stride;
+  float m = -INFINITY, l = 0.f, acc[MLA_DV / 64];
+#pragma unroll
+  for (int k = 0; k < MLA_DV / 64; ++k) acc[k] = 0.f;
+  for (int j = 0; j < ctx; ++j) {
+    const uint16_t* row =
+        reinterpret_cast<const uint16_t*>(a.cache) + ((size_t)(uint32_t)bt[j >> 4] * 16 + (j & 15)) * DK;
+    float c[DK / 64];
+    float d = 0.f;
+#pragma unroll
+    for (int k = 0; k < DK / 64; ++k) {
+      c[k] = bf16_to_f32(row[64 * k + lane]);
+      d = fmaf(qv[k], c[k], d);
+    }
+    const float x = group_sum<64>(d) * a.scale_log2;
+    const float mn = fmaxf(m, x);
+    const float corr = exp2f(m - mn), p = exp2f(x - mn);
+    l = l * corr + p;
+#pragma unroll
+    for (int k = 0; k < MLA_DV / 64; ++k) acc[k] = fmaf(p, c[k], acc[k] * corr);
+    m = mn;
+  }
+  uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((size_t)s * H + h) * MLA_DV;
+#pragma unroll
+  for (int k = 0; k < MLA_DV / 64; ++k) o[64 * k + lane] = f32_to_bf16(acc[k] / l);
+}
+
 // Exact merge of a (sequence, head)'s summaries, one wave each: the
-// workgroups w0..w1 covering the sequence left theirs in slot w + s.
-template <int H>
+// workgroups w0..w1 covering the sequence left theirs in slot w + s. With
+// fp16 value tiles (more than 16 heads) a row that comes out non-finite is
+// computed again exactly (mla_row_exact).
+template <int DK, int H>
 __global__ __launch_bounds__(256) void mla_merge(MlaArgs a) {
+  constexpr bool FP16_TILES = H > 16;
   const int lane = threadIdx.x & 63;
   const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (idx >= a.num_seqs * H) return;
@@ -687,7 +731,16 @@ __global__ __launch_bounds__(256) void mla_merge(MlaArgs a) {
     return;
   }
   const int w0 = psum[s] / C, w1 = (psum[s] + np - 1) / C;
-  if (w0 == w1) return;  // finished in place
+  if (w0 == w1) {  // finished in place
+    if constexpr (FP16_TILES) {
+      const uint16_t* o = reinterpret_cast<const uint16_t*>(a.out) + ((size_t)s * H + h) * MLA_DV;
+      bool bad = false;
+#pragma unroll
+      for (int k = 0; k < MLA_DV / 64; ++k) bad |= (o[64 * k + lane] & 0x7f80u) == 0x7f80u;
+      if (__any(bad)) mla_row_exact<DK, H>(a, s, h, lane);
+    }
+    return;
+  }
   const int n = w1 - w0 + 1;
   auto rec = [&](int i) { return (size_t)(w0 + i + s) * H + h; };
   float M = -INFINITY;
@@ -705,6 +758,15 @@ __global__ __launch_bounds__(256) void mla_merge(MlaArgs a) {
     for (int k = 0; k < MLA_DV / 64; ++k) acc[k] = fmaf(w, row[64 * k + lane], acc[k]);
   }
   const float inv = 1.f / L;
+  if constexpr (FP16_TILES) {
+    bool bad = false;
+#pragma unroll
+    for (int k = 0; k < MLA_DV / 64; ++k) bad |= !(fabsf(acc[k] * inv) <= 3.4028235e38f);
+    if (__any(bad)) {
+      mla_row_exact<DK, H>(a, s, h, lane);
+      return;
+    }
+  }
 #pragma unroll
   for (int k = 0; k < MLA_DV / 64; ++k)
     reinterpret_cast<uint16_t*>(a.out)[((size_t)s * H + h) * MLA_DV + 64 * k + lane] = f32_to_bf16(acc[k] * inv);
@@ -749,7 +811,7 @@ static hipError_t run_mla(const MlaArgs& a, int grid, hipStream_t st) {
     hipLaunchKernelGGL((mla_decode_split<DK, H, NW, HG>), dim3((unsigned)grid), dim3(64 * NW), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((mla_merge<H>), dim3((unsigned)((a.num_seqs * H + 3) / 4)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((mla_merge<DK, H>), dim3((unsigned)((a.num_seqs * H + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

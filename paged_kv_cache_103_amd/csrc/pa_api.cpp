@@ -138,10 +138,10 @@ static int elem_bytes(pa_dtype d) { return d == PA_F32 ? 4 : (d == PA_BF16 ? 2 :
 // (bf16, fp8): the cache type decides the query type.
 static pa::DecodePlan make_plan(int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
                                 int32_t num_kv_heads, int32_t head_size, pa_dtype cache_dtype,
-                                int32_t sliding_window) {
+                                int32_t sliding_window, bool force_valu = false) {
   const int q_kind = cache_dtype == PA_F32 ? PA_F32 : PA_BF16;
   return pa::plan_decode(num_seqs, max_context_len, num_heads, num_kv_heads, head_size, q_kind,
-                         (int)cache_dtype, sliding_window);
+                         (int)cache_dtype, sliding_window, force_valu);
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -177,14 +177,27 @@ static void bind_workspace(pa::DecodeArgs& a, const pa::DecodePlan& plan, void* 
   }
 }
 
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
-                                 int32_t num_kv_heads, int32_t head_size, pa_dtype cache_dtype,
-                                 int32_t sliding_window) {
+static size_t decode_ws_bytes(int32_t num_seqs, int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                              int32_t head_size, pa_dtype cache_dtype, int32_t sliding_window, bool force_valu) {
   if (num_seqs <= 0 || max_context_len <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0)
     return 0;
   const pa::DecodePlan plan = make_plan(num_seqs, max_context_len, num_heads, num_kv_heads, head_size,
-                                        cache_dtype, sliding_window);
+                                        cache_dtype, sliding_window, force_valu);
   return pa::decode_workspace_bytes(plan, num_seqs, num_heads, num_kv_heads, head_size);
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_size, pa_dtype cache_dtype,
+                                 int32_t sliding_window) {
+  return decode_ws_bytes(num_seqs, max_context_len, num_heads, num_kv_heads, head_size, cache_dtype,
+                         sliding_window, false);
+}
+
+size_t pa_decode_valu_workspace_bytes(int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_size, pa_dtype cache_dtype,
+                                      int32_t sliding_window) {
+  return decode_ws_bytes(num_seqs, max_context_len, num_heads, num_kv_heads, head_size, cache_dtype,
+                         sliding_window, true);
 }
 
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len,
@@ -197,14 +210,15 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_
                                    cache_dtype, sliding_window);
 }
 
-// pa_decode, and pa_decode_partial when lse is given.
+// pa_decode, pa_decode_partial when lse is given, pa_decode_valu with
+// force_valu.
 static pa_status decode_impl(void* out, float* lse, const void* query, const void* k_cache, const void* v_cache,
                              const float* k_scale, const float* v_scale, const int32_t* block_table,
                              int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
                              int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
                              int32_t head_size, int32_t block_size, int32_t num_blocks, pa_dtype q_dtype,
                              pa_dtype cache_dtype, float scale, int32_t sliding_window, void* workspace,
-                             size_t workspace_bytes, pa_stream_t stream) {
+                             size_t workspace_bytes, pa_stream_t stream, bool force_valu = false) {
   pa_status st = check_attention_common(out, query, k_cache, v_cache, k_scale, v_scale, block_table,
                                         block_table_stride, context_lens, num_seqs, max_context_len,
                                         num_heads, num_kv_heads, head_size, block_size, num_blocks,
@@ -215,7 +229,7 @@ static pa_status decode_impl(void* out, float* lse, const void* query, const voi
     return PA_OK;
   }
   const pa::DecodePlan plan = make_plan(num_seqs, max_context_len, num_heads, num_kv_heads, head_size,
-                                        cache_dtype, sliding_window);
+                                        cache_dtype, sliding_window, force_valu);
   if (lse != nullptr && plan.split_waves <= 0)
     return fail(PA_ERR_UNSUPPORTED, "partial decode needs the matrix-core kernel (bf16 queries, bf16 or fp8 "
                 "cache, at most 16000 sequences)");
@@ -255,6 +269,19 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
   return decode_impl(out, nullptr, query, k_cache, v_cache, k_scale, v_scale, block_table, block_table_stride,
                      context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_size, block_size,
                      num_blocks, q_dtype, cache_dtype, scale, sliding_window, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_valu(void* out, const void* query, const void* k_cache, const void* v_cache,
+                         const float* k_scale, const float* v_scale, const int32_t* block_table,
+                         int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                         int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                         int32_t block_size, int32_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype,
+                         float scale, int32_t sliding_window, void* workspace, size_t workspace_bytes,
+                         pa_stream_t stream) {
+  return decode_impl(out, nullptr, query, k_cache, v_cache, k_scale, v_scale, block_table, block_table_stride,
+                     context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_size, block_size,
+                     num_blocks, q_dtype, cache_dtype, scale, sliding_window, workspace, workspace_bytes, stream,
+                     true);
 }
 
 pa_status pa_decode_partial(void* out, float* lse, const void* query, const void* k_cache, const void* v_cache,
@@ -600,7 +627,7 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
     p.window = sliding_window;
     p.scale_log2 = scale_log2;
     // bound on sum over sequences with q_len > 1 of ceil(q_len / TQ)
-    const long long tq = pa::prefill_tokens_per_tile((int)cache_dtype, group);
+    const long long tq = pa::prefill_tokens_per_tile(group);
     const long long long_seqs = std::min<long long>(num_seqs, num_q_tokens / 2);
     const long long bound_a = long_seqs + (num_q_tokens + tq - 1) / tq;
     const long long bound_b = long_seqs * ((max_q_len + tq - 1) / tq);

@@ -46,8 +46,9 @@ struct DecodePlan {
   int split_waves;  // > 0: even split over this many waves (matrix-core kernel)
   int one_per_stream;  // matrix-core kernel, every stream short: a wave per (sequence, KV head), no merge
 };
+// force_valu: the VALU kernel whatever the cache type (pa_decode_valu).
 DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num_kv_heads, int head_size,
-                       int q_kind, int cache_kind, int sliding_window);
+                       int q_kind, int cache_kind, int sliding_window, bool force_valu = false);
 size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int num_heads, int num_kv_heads,
                               int head_size);
 // Decode with groups of sequences sharing prefix blocks (matrix-core kernel
@@ -160,13 +161,11 @@ struct PrefillArgs {
   int num_tiles;  // grid bound on (sequence, query tile) pairs
   float scale_log2;
 };
-// Query tokens per workgroup tile of the chunked-prefill kernel for a cache type.
-int prefill_tokens_per_tile(int cache_kind, int group);
-int prefill_bf16_tokens_per_tile(int group);
-hipError_t launch_prefill(const PrefillArgs& args, int cache_kind, int head_size, hipStream_t stream);
-// The 32x32 MFMA kernel (bf16 scores, fp16 PV) with direct global->LDS
-// copies, 8 waves per workgroup, for bf16 and fp8 caches.
-hipError_t launch_prefill_bf16(const PrefillArgs& args, int cache_kind, int head_size, hipStream_t stream);
+// The chunked-prefill kernel (prefill_bf16.hip: 32x32 MFMA, bf16 scores and
+// fp16 values, direct global->LDS copies, 8 waves per workgroup) for bf16
+// and fp8 caches: query tokens per workgroup tile, what it supports, launch.
+int prefill_tokens_per_tile(int group);
 bool prefill_supported(int q_kind, int cache_kind, int head_size, int group);
+hipError_t launch_prefill(const PrefillArgs& args, int cache_kind, int head_size, hipStream_t stream);
 
 }  // namespace pa

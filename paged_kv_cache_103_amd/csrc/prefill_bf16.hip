@@ -22,9 +22,15 @@
 //    by 2^7 so that they stay in fp16's range (p <= 2^15) and keep 2^-31 of
 //    resolution below the running maximum. The values are therefore
 //    converted to fp16 once per workgroup, in LDS: exact for |v| in
-//    [2^-14, 65504]; smaller magnitudes keep 2^-24 of absolute resolution and
-//    larger ones overflow, so bf16 values beyond fp16's range are outside
-//    this kernel's domain;
+//    [2^-14, 65504], and smaller magnitudes keep 2^-24 of absolute
+//    resolution. A value beyond fp16's range becomes infinity there and
+//    leaves inf or NaN in the accumulators of every column; a tile whose
+//    accumulators end non-finite is computed again with the value product
+//    taken from the cache itself: the values as bf16 (exact; fp8 widened
+//    exactly, its block scale moved onto the weights) against the weights
+//    split into bf16 hi + lo, two MFMAs per term. Every finite cached value
+//    is in the kernel's domain; the fp32 accumulator bounds it only through
+//    2^15 * sum |v| < 3.4e38;
 //  * score rows are fed in a permuted key order, so that the accumulator of
 //    lane l holds, for its column, exactly the 8-key runs the PV B operand
 //    wants from it: probabilities never leave the lane. A column's 32 keys
@@ -49,7 +55,8 @@
 //    just before their MFMA (exact); the score takes the block's K scale.
 //    The V tiles are copied to a ring of their own and the conversion pass
 //    writes them as fp16 values times the block's V scale into the V slots
-//    the bf16 path uses (the scaled values are the kernel's fp16 domain).
+//    the bf16 path uses (a tile whose scaled values overflow fp16 is computed
+//    again with the exact product above).
 #include <math.h>
 
 #include <type_traits>
@@ -77,10 +84,6 @@ __device__ __forceinline__ f32x16 mfma32x32x16_f16(const u32x4& a, const u32x4& 
 // Two floats as packed fp16, rounded to nearest even.
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
-}
-// A pair of bf16 values as a pair of fp16 values (exact inside fp16's range).
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
-  return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 
 template <int D>
@@ -196,6 +199,7 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   __shared__ __attribute__((aligned(16))) uint8_t rvring[FP8 ? S::KSLOTS * RVSLOTB : 16];
   __shared__ int sh_scan[NT];
   __shared__ int sh_found[3];
+  __shared__ int sh_redo;  // some column's accumulators ended non-finite
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -352,13 +356,9 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   auto scores = [&](int slot) { scores_load(slot); return scores_mfma(); };
 
   f32x16 o[S::DT];
-#pragma unroll
-  for (int dt = 0; dt < S::DT; ++dt) o[dt] = f32x16{};
-  float m = -INFINITY, lsum = 0.f, alpha = 1.f;
-  bool pending = false;            // o waits for a rescale by alpha
+  float m, lsum, alpha;
+  bool pending;                    // o waits for a rescale by alpha
   u32x4 pf[2];                     // P of the previous step (fp16, x 2^7), per key half
-#pragma unroll
-  for (int t = 0; t < 2; ++t) pf[t] = u32x4{0, 0, 0, 0};
 
   auto pv = [&](int slot, const u32x4* pk, const uint32_t (*vmask)[4]) {
     const uint16_t* vp = vrow + slot * S::VSLOT;
@@ -371,6 +371,47 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         o[dt] = mfma32x32x16_f16(vf, pk[t], o[dt]);
       }
   };
+  // The same product without the fp16 values, for a tile whose values do
+  // not all fit fp16: the lane's 8 keys of each value row come straight from
+  // the cache tile (bf16 exact; fp8 widened exactly and its block scale
+  // moved onto the weights), the weights (fp16, x 2^7) split exactly into
+  // bf16 hi + lo, two MFMAs per term.
+  typedef __attribute__((address_space(4))) const float cfloat;
+  auto pv_exact = [&](int step, const u32x4* pk, const uint32_t (*vmask)[4]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t bid = (uint32_t)bt[min(b0 + 2 * step + t, b_last)];
+      const uint8_t* tile = vcache + (size_t)bid * head_stride;
+      const float vs = FP8 ? ((const cfloat*)a.v_scale)[bid] : 1.f;
+      u32x4 phi, plo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // (through a named scalar: hipcc's bit_cast of a vector element
+        // subscript reads element 0 whatever the index)
+        const uint32_t pe = pk[t][e];
+        const f16x2_t w = __builtin_bit_cast(f16x2_t, pe);
+        const float f0 = (float)w.x * vs, f1 = (float)w.y * vs;
+        const uint32_t h0 = __float_as_uint(f0) & 0xffff0000u, h1 = __float_as_uint(f1) & 0xffff0000u;
+        phi[e] = (h0 >> 16) | h1;
+        plo[e] = pack_bf16x2(f0 - __uint_as_float(h0), f1 - __uint_as_float(h1));
+      }
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt) {
+        const int row = dt * 32 + c32;
+        u32x4 vf;
+        if constexpr (FP8) {
+          const u32x2 raw = *reinterpret_cast<const u32x2*>(tile + row * 16 + 8 * h);
+          vf = fp8x8_to_bf16x8(raw[0], raw[1]);
+        } else {
+          vf = load16(tile + (row * 16 + 8 * h) * 2);
+        }
+        if (vmask) { vf[0] &= vmask[t][0]; vf[1] &= vmask[t][1]; vf[2] &= vmask[t][2]; vf[3] &= vmask[t][3]; }
+        o[dt] = mfma32x32x16(vf, phi, o[dt]);
+        o[dt] = mfma32x32x16(vf, plo, o[dt]);
+        __builtin_amdgcn_sched_barrier(0);  // one value fragment live at a time (rare path)
+      }
+    }
+  };
   // bf16 -> fp16 in place: thread tid owns the 16-byte chunk tid of the
   // slot (4 D chunks; threads past them idle). The chunk is read early in an
   // iteration and written back at its end.
@@ -381,7 +422,6 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const bool converts = VCH == NT || tid < VCH;
   u32x4 cvt = {0, 0, 0, 0};
   float cvt_scale = 1.f;
-  typedef __attribute__((address_space(4))) const float cfloat;
   auto convert_load = [&](int slot, int raw_slot, int step) {
     if constexpr (FP8) {
       if (converts) {
@@ -415,13 +455,25 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     } else {
       if (converts) {
         u32x4 w = cvt;
-        w[0] = bf16x2_to_f16x2(w[0]); w[1] = bf16x2_to_f16x2(w[1]);
-        w[2] = bf16x2_to_f16x2(w[2]); w[3] = bf16x2_to_f16x2(w[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_f16x2(bf16_lo(w[e]), bf16_hi(w[e]));
         reinterpret_cast<u32x4*>(vring + slot * S::VSLOT)[tid] = w;
       }
     }
   };
 
+  // One pass over the tile's keys; EXACT takes the value product from the
+  // cache (pv_exact) instead of the fp16 slots.
+  auto pass = [&](auto exact_tag) {
+  constexpr bool EXACT = decltype(exact_tag)::value;
+#pragma unroll
+  for (int dt = 0; dt < S::DT; ++dt) o[dt] = f32x16{};
+  m = -INFINITY;
+  lsum = 0.f;
+  alpha = 1.f;
+  pending = false;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) pf[t] = u32x4{0, 0, 0, 0};
   // ---- prologue: K and V of steps 0..2; V of step 0 converted; the V slot
   // of step -1 (read with P = 0 by the first iteration) cleared ----
 #pragma unroll
@@ -461,7 +513,11 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     scores_load(slot_k1);
     __builtin_amdgcn_sched_barrier(0);
     sn = scores_mfma();                     // S of step st+1 (unused past the end)
-    pv(slot_vp, pf, nullptr);               // O^T += V^T P^T of step st-1
+    if constexpr (EXACT) {                  // (step -1 has P = 0: nothing to add)
+      if (st > 0) pv_exact(st - 1, pf, nullptr);
+    } else {
+      pv(slot_vp, pf, nullptr);             // O^T += V^T P^T of step st-1
+    }
 
     // ---- softmax of step st ----
     float x[16];
@@ -544,7 +600,24 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         const int kp = kb + 16 * t + 2 * e;
         vmask[t][e] = (kp < ctx ? 0x0000ffffu : 0u) | (kp + 1 < ctx ? 0xffff0000u : 0u);
       }
-    pv((nsteps - 1) % S::VSLOTS, pf, vmask);  // V of step nsteps-1
+    if constexpr (EXACT) pv_exact(nsteps - 1, pf, vmask);
+    else pv((nsteps - 1) % S::VSLOTS, pf, vmask);  // V of step nsteps-1
+  }
+  };  // pass
+
+  if (tid == 0) sh_redo = 0;  // (read after the barriers of the first pass)
+  pass(std::false_type{});
+  {
+    // a value beyond fp16's range leaves inf or NaN in the accumulators of
+    // every column it reaches: then the tile is computed again, exactly
+    bool bad = false;
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bad |= !(fabsf(o[dt][i]) <= 3.4028235e38f);
+    if (__any(bad) && lane == 0) sh_redo = 1;
+    __syncthreads();  // (also: no wave still reads the rings)
+    if (sh_redo) pass(std::true_type{});
   }
 
   // ---- normalise and write: lane holds rows d = 32 dt + 8 i + 4 h + r of
@@ -589,9 +662,15 @@ static hipError_t run_prefill_bf16_g(const PrefillArgs& a, int G, hipStream_t st
   return hipErrorInvalidValue;
 }
 
-int prefill_bf16_tokens_per_tile(int group) { return 32 * PF_NW / group; }
+int prefill_tokens_per_tile(int group) { return 32 * PF_NW / group; }
 
-hipError_t launch_prefill_bf16(const PrefillArgs& a, int cache_kind, int head_size, hipStream_t stream) {
+bool prefill_supported(int q_kind, int cache_kind, int head_size, int group) {
+  if (head_size != 64 && head_size != 128) return false;
+  if (!(group == 1 || group == 2 || group == 4 || group == 8 || group == 16)) return false;
+  return q_kind == KBF16 && (cache_kind == KBF16 || cache_kind == KFP8);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int cache_kind, int head_size, hipStream_t stream) {
   const int G = a.num_heads / a.num_kv_heads;
   if (cache_kind == KBF16 && head_size == 64) return run_prefill_bf16_g<64, KBF16>(a, G, stream);
   if (cache_kind == KBF16 && head_size == 128) return run_prefill_bf16_g<128, KBF16>(a, G, stream);

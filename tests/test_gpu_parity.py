@@ -345,6 +345,24 @@ def test_decode_small(case):
     check_rows(b, out, range(b.num_seqs), f"decode case {case}")
 
 
+@pytest.mark.parametrize("case", [0, 1, 3, 4, 5, 9])
+def test_decode_valu_small(case):
+    """pa_decode_valu (the vector-ALU kernel, kept for side-by-side
+    measurement) on the bf16 and fp8 decode cases."""
+    ctx, Hq, Hkv, D, qd, cd, w = DECODE_CASES[case]
+    b = W.make_batch(f"valu{case}", 150 + case, ctx, [1] * len(ctx), Hq, Hkv, D, qd, cd,
+                     sliding_window=w, device=DEV, extra_blocks=5)
+    m = b.meta(DEV)
+    out = torch.empty_like(b.query)
+    n = pa.decode_valu_workspace_bytes(b.num_seqs, b.max_context_len, b.num_heads, b.num_kv_heads, b.head_size,
+                                       b.cache_dtype, b.sliding_window)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+    pa.decode_valu(out, b.query, b.k_cache, b.v_cache, m["block_table"], m["context_lens"], b.max_context_len,
+                   b.scale, b.k_scale, b.v_scale, b.sliding_window, ws)
+    torch.cuda.synchronize()
+    check_rows(b, out, range(b.num_seqs), f"valu decode case {case}")
+
+
 PREFILL_CASES = [
     # (ctx lens, q lens, Hq, Hkv, D, cache dtype, window)
     ([37, 50, 1000, 17, 2100], [37, 1, 130, 1, 300], 32, 8, 128, "bf16", 0),
