@@ -135,6 +135,29 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
                     size_t workspace_bytes, pa_stream_t stream);
 
 /*
+ * pa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. The
+ * arguments are pa_decode's without the workspace; the split-K summaries go
+ * to a scratch array inside the library instead: PA_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) per GPU, part of the code object, held by each GPU the library
+ * runs on until the process ends. The call allocates and frees nothing.
+ * A request whose pa_decode_workspace_bytes(...) exceeds the array returns
+ * PA_ERR_WORKSPACE_TOO_SMALL and enqueues nothing (about 14,000 (sequence,
+ * KV head) streams at 4 query heads per KV head, head size 128). Every call
+ * on one GPU shares that GPU's array and leaves its last contents there
+ * (nothing in it needs clearing between calls): calls that can overlap on
+ * one GPU (unordered streams) race, and must be ordered by the caller.
+ * Results equal pa_decode's bit for bit.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pa_status pa_decode_noalloc(void* out, const void* query, const void* k_cache, const void* v_cache,
+                            const float* k_scale, const float* v_scale, const int32_t* block_table,
+                            int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                            int32_t block_size, int32_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype,
+                            float scale, int32_t sliding_window, pa_stream_t stream);
+
+/*
  * pa_decode on the vector-ALU kernel, whatever the cache type: scores as
  * packed-bf16 dot products reduced across the wave with DPP row shuffles,
  * the online-softmax max and sum by the same shuffles, weights passed to the

@@ -33,6 +33,7 @@ BLOCK_SIZE = 16
 EXPORTED = (
     "pa_reshape_and_cache",
     "pa_decode",
+    "pa_decode_noalloc",
     "pa_decode_valu",
     "pa_decode_shared_prefix",
     "pa_decode_sparse",
@@ -77,6 +78,9 @@ def load() -> ctypes.CDLL:
     L.pa_decode.restype = ctypes.c_int
     L.pa_decode.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32,
                             ctypes.c_int, ctypes.c_int, ctypes.c_float, i32, vp, sz, vp]
+    L.pa_decode_noalloc.restype = ctypes.c_int
+    L.pa_decode_noalloc.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_float, i32, vp]
     L.pa_decode_valu.restype = ctypes.c_int
     L.pa_decode_valu.argtypes = L.pa_decode.argtypes
     L.pa_decode_valu_workspace_bytes.restype = sz
@@ -253,6 +257,24 @@ def decode(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cach
                             S, int(max_context_len), Hq, Hkv, D, k_cache.shape[2], NB,
                             dtype_code(query.dtype), dtype_code(k_cache.dtype), float(scale),
                             int(sliding_window), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # PA_NOALLOC_SCRATCH_BYTES
+
+
+def decode_noalloc(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   block_table: torch.Tensor, context_lens: torch.Tensor, max_context_len: int, scale: float,
+                   k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                   sliding_window: int = 0, stream=None) -> None:
+    """pa_decode_noalloc: pa_decode with the library's own per-GPU scratch
+    instead of a workspace (nothing allocated)."""
+    S, Hq, D = query.shape
+    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
+    _check(load().pa_decode_noalloc(_ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                    _ptr(v_scale), _ptr(block_table), block_table.shape[1], _ptr(context_lens),
+                                    S, int(max_context_len), Hq, Hkv, D, k_cache.shape[2], NB,
+                                    dtype_code(query.dtype), dtype_code(k_cache.dtype), float(scale),
+                                    int(sliding_window), _stream(stream)))
 
 
 def decode_valu(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

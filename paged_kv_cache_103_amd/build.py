@@ -25,7 +25,7 @@ PEAKS_LIB = os.path.join(LIBDIR, "libpa_peaks.so")
 
 ARCH = "gfx950"
 SOURCES = ["pa_api.cpp", "pa_check.cpp", "pa_blocks.cpp", "reshape_and_cache.hip", "copy_blocks.hip", "decode.hip", "decode_mfma.hip",
-           "sparse_select.hip", "merge_lse.hip", "mla_decode.hip", "prefill_bf16.hip"]
+           "sparse_select.hip", "merge_lse.hip", "mla_decode.hip", "prefill_bf16.hip", "noalloc.hip"]
 # the achievable-peak probes bench.py runs beside the path (a library of their own)
 PEAKS_SOURCES = ["peaks.hip"]
 

@@ -284,6 +284,40 @@ pa_status pa_decode_valu(void* out, const void* query, const void* k_cache, cons
                      true);
 }
 
+pa_status pa_decode_noalloc(void* out, const void* query, const void* k_cache, const void* v_cache,
+                            const float* k_scale, const float* v_scale, const int32_t* block_table,
+                            int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                            int32_t block_size, int32_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype,
+                            float scale, int32_t sliding_window, pa_stream_t stream) {
+  // every argument check before the scratch array is looked up
+  pa_status st = check_attention_common(out, query, k_cache, v_cache, k_scale, v_scale, block_table,
+                                        block_table_stride, context_lens, num_seqs, max_context_len,
+                                        num_heads, num_kv_heads, head_size, block_size, num_blocks,
+                                        q_dtype, cache_dtype, scale, sliding_window);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) {
+    g_last_error.clear();
+    return PA_OK;
+  }
+  const size_t need = decode_ws_bytes(num_seqs, max_context_len, num_heads, num_kv_heads, head_size, cache_dtype,
+                                      sliding_window, false);
+  if (need > pa::kNoallocScratchBytes)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                "this decode needs %zu bytes of scratch; the no-allocation entry point holds %zu "
+                "(use pa_decode with a workspace)",
+                need, pa::kNoallocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    hipError_t e = hipSuccess;
+    ws = pa::noalloc_scratch(&e);
+    if (ws == nullptr) return hip_status(e == hipSuccess ? hipErrorInvalidSymbol : e, "scratch lookup");
+  }
+  return decode_impl(out, nullptr, query, k_cache, v_cache, k_scale, v_scale, block_table, block_table_stride,
+                     context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_size, block_size,
+                     num_blocks, q_dtype, cache_dtype, scale, sliding_window, ws, need, stream);
+}
+
 pa_status pa_decode_partial(void* out, float* lse, const void* query, const void* k_cache, const void* v_cache,
                             const float* k_scale, const float* v_scale, const int32_t* block_table,
                             int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,

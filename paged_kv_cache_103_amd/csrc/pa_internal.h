@@ -92,6 +92,11 @@ struct DecodeArgs {
   float* lse;        // optional [rows][num_heads]: ln of the softmax denominator (matrix-core kernel)
 };
 
+// pa_decode_noalloc's per-GPU scratch array (noalloc.hip): its size and this
+// device's address of it (null, with *err set, if the runtime lookup fails).
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+void* noalloc_scratch(hipError_t* err);
+
 // q_kind / cache_kind: 0 = f32, 1 = bf16, 2 = fp8 e4m3fn.
 hipError_t launch_decode(const DecodeArgs& args, int q_kind, int cache_kind, int head_size,
                          hipStream_t stream);
