@@ -66,31 +66,36 @@ def _visible(q_pos: np.ndarray, k_pos: np.ndarray, window: int) -> np.ndarray:
 
 def attend_sequence(q_f64, k_pool, v_pool, cache_dtype: str, k_scale, v_scale,
                     block_table_row, ctx: int, num_kv_heads: int, scale: float,
-                    sliding_window: int = 0, block_size: int = 16, heads=None):
+                    sliding_window: int = 0, block_size: int = 16, heads=None, rows=None):
     """Attention output of one sequence, float64.
 
     q_f64: [q_len][Hq][D] queries of this sequence (already float64), the
     last q_len positions of a context of ``ctx`` tokens. Returns
-    [q_len][Hq][D]; heads not listed in ``heads`` are left NaN.
+    [q_len][Hq][D]; heads not listed in ``heads`` and query rows not listed
+    in ``rows`` are left NaN (each row's result depends on that row alone,
+    so leaving rows out changes nothing for the others).
     """
     q_len, Hq, D = q_f64.shape
     assert 1 <= q_len <= ctx, "a sequence attends to at least itself"
     G = Hq // num_kv_heads
-    q_pos = np.arange(ctx - q_len, ctx, dtype=np.int64)
-    lo = 0 if sliding_window <= 0 else max(0, int(q_pos[0]) - sliding_window + 1)
+    rows = np.arange(q_len, dtype=np.int64) if rows is None else np.asarray(sorted(set(rows)), dtype=np.int64)
+    q_pos_all = np.arange(ctx - q_len, ctx, dtype=np.int64)
+    lo = 0 if sliding_window <= 0 else max(0, int(q_pos_all[rows[0]]) - sliding_window + 1)
     k_pos = np.arange(lo, ctx, dtype=np.int64)
-    vis = _visible(q_pos, k_pos, sliding_window)
     out = np.full((q_len, Hq, D), np.nan)
     heads = range(Hq) if heads is None else heads
     for g in sorted({h // G for h in heads}):
         K, V = gather_kv(k_pool, v_pool, cache_dtype, k_scale, v_scale, block_table_row,
                          g, k_pos, block_size)
-        for h in [h for h in heads if h // G == g]:
-            s = scale * (q_f64[:, h, :] @ K.T)                # [q_len][n]
-            s = np.where(vis, s, -np.inf)
-            m = s.max(axis=1, keepdims=True)
-            p = np.exp(s - m)
-            out[:, h, :] = (p @ V) / p.sum(axis=1, keepdims=True)
+        for r0 in range(0, len(rows), 256):  # bounded memory for long chunks
+            rr = rows[r0:r0 + 256]
+            vis = _visible(q_pos_all[rr], k_pos, sliding_window)
+            for h in [h for h in heads if h // G == g]:
+                s = scale * (q_f64[rr, h, :] @ K.T)               # [rows][n]
+                s = np.where(vis, s, -np.inf)
+                m = s.max(axis=1, keepdims=True)
+                p = np.exp(s - m)
+                out[rr, h, :] = (p @ V) / p.sum(axis=1, keepdims=True)
     return out
 
 

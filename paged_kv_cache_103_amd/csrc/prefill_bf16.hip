@@ -109,13 +109,14 @@ __device__ __forceinline__ int k_swizzle(int key) {
   else return (key >> 1) & 7;
 }
 __device__ __forceinline__ int v_swizzle(int d) { return (d >> 3) & 1; }
-// fp8 K rows (D bytes = D/16 chunks): the 32 lanes of a half-wave read one
-// 8-byte half-chunk of 32 permuted keys; spreading the chunk by key bits
-// 1..3 (or 1..2) makes them cover every bank pair of two LDS cycles.
+// fp8 K rows (D bytes = D/16 chunks), read 16 bytes per lane: each group
+// of 16 lanes reads one chunk column of 16 keys (key bits 0..3), and the
+// swizzle by the key bits the row stride leaves alone puts them on 16
+// distinct bank groups.
 template <int D>
 __device__ __forceinline__ int k8_swizzle(int key) {
   if constexpr (D == 128) return (key >> 1) & 7;
-  else return (key >> 1) & 3;
+  else return (key >> 2) & 3;
 }
 
 // Score row m of a step holds this key of the step.
@@ -238,14 +239,19 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const bool neg = a.scale_log2 < 0.f;
   float c = fabsf(a.scale_log2);
   c = c > 0.f ? c : 1.17549435e-38f;  // scale 0 (uniform weights) as the smallest normal
+  // bf16 caches: k-step ks of the score product covers dims 16 ks + 8 h ..
+  // + 7 for lane half h; fp8 caches read 16 key bytes per lane, so there
+  // k-steps 2 m and 2 m + 1 cover the lane half's 16 dims 32 m + 16 h .. + 15
+  // (the order of a dot product's terms is free; K and Q use the same one)
   u32x4 qf[S::DK];
   {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) +
-                         ((size_t)(q0 + tok0 + tok) * a.num_heads + g * G + head) * D + 8 * h;
+                         ((size_t)(q0 + tok0 + tok) * a.num_heads + g * G + head) * D;
     const uint32_t flip = neg ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < S::DK; ++ks) {
-      qf[ks] = tok < ntok ? load16(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+      const int d0 = FP8 ? 32 * (ks >> 1) + 16 * h + 8 * (ks & 1) : 16 * ks + 8 * h;
+      qf[ks] = tok < ntok ? load16(qp + d0) : u32x4{0, 0, 0, 0};
       qf[ks][0] ^= flip; qf[ks][1] ^= flip; qf[ks][2] ^= flip; qf[ks][3] ^= flip;
     }
   }
@@ -321,35 +327,32 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const uint16_t* vrow = vring + c32 * 16 + 8 * (h ^ vswz_l);
   // per-lane byte offsets of the K operand chunks (the slot adds a uniform
   // offset)
-  uint32_t kaddr[S::DK];
+  constexpr int KREADS = FP8 ? S::DK / 2 : S::DK;  // 16-byte K operand reads per step
+  uint32_t kaddr[KREADS];
 #pragma unroll
-  for (int ks = 0; ks < S::DK; ++ks) {
+  for (int j = 0; j < KREADS; ++j) {
     if constexpr (FP8)
-      kaddr[ks] = lds_offset(kring) + key_l * D + 16 * (ks ^ k8_swizzle<D>(key_l)) + 8 * h;
+      kaddr[j] = lds_offset(kring) + key_l * D + 16 * ((2 * j + h) ^ k8_swizzle<D>(key_l));
     else
-      kaddr[ks] = lds_offset(kring) + 2 * (key_l * D + 8 * ((2 * ks + h) ^ kswz_l));
+      kaddr[j] = lds_offset(kring) + 2 * (key_l * D + 8 * ((2 * j + h) ^ kswz_l));
   }
-  u32x4 kf[FP8 ? 1 : S::DK];
-  u32x2 k8[FP8 ? S::DK : 1];  // fp8: the raw 8 bytes, widened just before their MFMA
+  u32x4 kf[KREADS];  // fp8: raw bytes of two k-steps, widened just before their MFMAs
   auto scores_load = [&](int slot) {
     const uint32_t sb = __builtin_amdgcn_readfirstlane(slot * KSLOTB);
+    typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 #pragma unroll
-    for (int ks = 0; ks < S::DK; ++ks) {
-      if constexpr (FP8) {
-        typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
-        k8[ks] = *(const lds_u32x2*)(uintptr_t)(kaddr[ks] + sb);
-      } else {
-        typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-        kf[ks] = *(const lds_u32x4*)(uintptr_t)(kaddr[ks] + sb);
-      }
-    }
+    for (int j = 0; j < KREADS; ++j) kf[j] = *(const lds_u32x4*)(uintptr_t)(kaddr[j] + sb);
   };
   auto scores_mfma = [&]() {
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < S::DK; ++ks) {
-      if constexpr (FP8) acc = mfma32x32x16(fp8x8_to_bf16x8(k8[ks][0], k8[ks][1]), qf[ks], acc);
-      else acc = mfma32x32x16(kf[ks], qf[ks], acc);
+      if constexpr (FP8) {
+        const int j = ks >> 1, w = 2 * (ks & 1);
+        acc = mfma32x32x16(fp8x8_to_bf16x8(kf[j][w], kf[j][w + 1]), qf[ks], acc);
+      } else {
+        acc = mfma32x32x16(kf[ks], qf[ks], acc);
+      }
     }
     return acc;
   };

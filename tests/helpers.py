@@ -42,10 +42,10 @@ def seq_blocks(batch, s: int) -> np.ndarray:
     return batch.block_table[s, lo // 16:(ctx - 1) // 16 + 1], lo // 16
 
 
-def oracle_rows(batch, seqs, q=None):
+def oracle_rows(batch, seqs, q=None, rows=None, heads=None):
     """Oracle output (float64) for the query rows of ``seqs``; returns a dict
     s -> [q_len][Hq][D]. Only the blocks those sequences read are copied to
-    the host."""
+    the host. ``rows`` / ``heads`` restrict the evaluation (the rest is NaN)."""
     q = raw(batch.query) if q is None else q
     cu = batch.cu_seqlens
     dt = ORACLE_DTYPE[batch.cache_dtype]
@@ -67,7 +67,8 @@ def oracle_rows(batch, seqs, q=None):
         r0, r1 = int(cu[s]), int(cu[s + 1])
         qf = F.to_f64(q[r0:r1], qd)
         res[s] = oracle.attend_sequence(qf, kp, vp, dt, ks, vs, row, int(batch.context_lens[s]),
-                                        batch.num_kv_heads, batch.scale, batch.sliding_window)
+                                        batch.num_kv_heads, batch.scale, batch.sliding_window, heads=heads,
+                                        rows=rows)
     return res
 
 

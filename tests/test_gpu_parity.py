@@ -172,9 +172,8 @@ def test_decode_agentic_sampled():
     b = W.make_config("agentic_decode", device=DEV)
     out = run_decode(b)
     torch.cuda.synchronize()
-    # one member of two groups (the longest and the shortest context)
-    order = np.argsort(b.context_lens)
-    check_rows(b, out, [int(order[0]), int(order[-1])], "agentic_decode")
+    # one member of every group (a different position in each group)
+    check_rows(b, out, [grp[i % len(grp)] for i, grp in enumerate(b.shared_groups)], "agentic_decode")
     # members of a group share their prefix blocks but not their tails;
     # equal context lengths within a group
     for grp in b.shared_groups:
@@ -270,8 +269,10 @@ def test_decode_fp8_sampled():
     b = W.make_config("fp8_decode", device=DEV)
     out = run_decode(b)
     torch.cuda.synchronize()
+    # 16 sequences spread over the context range, shortest and longest included
     order = np.argsort(b.context_lens)
-    check_rows(b, out, [int(order[0]), int(order[len(order) // 2]), int(order[-1])], "fp8_decode")
+    check_rows(b, out, sorted({int(order[i]) for i in np.linspace(0, len(order) - 1, 16).astype(int)}),
+               "fp8_decode")
 
 
 def test_decode_fp8_swa128_full():
@@ -283,21 +284,43 @@ def test_decode_fp8_swa128_full():
 
 def test_mixed_step_sampled():
     """Write all 2240 new tokens, then the flattened varlen batch (192 decode
-    rows + one 2048-row chunk on a 65536-token prefix)."""
+    rows + one 2048-row chunk on a 65536-token prefix), as the benchmark's
+    step runs it. The write is compared byte for byte with the oracle's over
+    every block it touches (the destination slots scribbled over first);
+    the chunk on the first and last row of each of its 32 query tiles (every
+    head) plus every row for the query heads of one KV head; decode rows on
+    a spread of sequences."""
     b = W.make_config("mixed_step", device=DEV)
     m = b.meta(DEV)
-    pa.reshape_and_cache(b.new_key, b.new_value, b.k_cache, b.v_cache, m["slot_mapping"])
+    st = m["slot_mapping"]
+    blk, off = st // 16, st % 16
+    touched = torch.unique(blk)
+    b.k_cache[blk, :, off, :] = -3.0
+    b.v_cache[blk, :, :, off] = -3.0
+    k_before, v_before = raw(b.k_cache[touched]), raw(b.v_cache[touched])
+    pa.reshape_and_cache(b.new_key, b.new_value, b.k_cache, b.v_cache, st)
     out = run_prefill(b)
     torch.cuda.synchronize()
-    # decode rows: three sequences; chunk: sampled query rows
-    check_rows(b, out, [0, 95, 191], "mixed_step decode rows")
+    remap = {int(x): i for i, x in enumerate(touched.tolist())}
+    local = np.array([remap[int(s) // 16] * 16 + int(s) % 16 for s in b.slot_mapping], dtype=np.int64)
+    oracle.reshape_and_cache(k_before, v_before, raw(b.new_key), raw(b.new_value), local)
+    assert np.array_equal(raw(b.k_cache[touched]).view(np.uint8), k_before.view(np.uint8))
+    assert np.array_equal(raw(b.v_cache[touched]).view(np.uint8), v_before.view(np.uint8))
+    _log(f"mixed_step write: {b.num_q_tokens} tokens into {len(touched)} blocks, byte-exact")
+    # decode rows: a spread of sequences
+    check_rows(b, out, list(range(0, 192, 12)) + [191], "mixed_step decode rows")
     s = 192
     cu = b.cu_seqlens
-    ref = oracle_rows(b, [s])[s]
     got = out_f64(out)[cu[s]:cu[s + 1]]
-    rows = [0, 1, 31, 32, 1000, 2046, 2047]
+    tq = 256 // (b.num_heads // b.num_kv_heads)  # query tokens per tile
+    rows = sorted({r for t in range(2048 // tq) for r in (t * tq, t * tq + tq - 1)} | {1, 31, 32, 1000})
+    ref = oracle_rows(b, [s], rows=rows)[s]
     ma, mr = assert_close(got[rows], ref[rows], "mixed_step chunk rows")
-    _log(f"mixed_step chunk: rows {rows}, max abs {ma:.2e}, max rel {mr:.2e}")
+    _log(f"mixed_step chunk: {len(rows)} rows over all {2048 // tq} tiles, max abs {ma:.2e}, max rel {mr:.2e}")
+    heads = list(range(b.num_heads // b.num_kv_heads))  # the query heads of KV head 0
+    ref = oracle_rows(b, [s], heads=heads)[s]
+    ma, mr = assert_close(got[:, heads], ref[:, heads], "mixed_step chunk, KV head 0")
+    _log(f"mixed_step chunk: all 2048 rows of heads {heads}, max abs {ma:.2e}, max rel {mr:.2e}")
 
 
 def test_prefill_fp8_chunk_sampled():

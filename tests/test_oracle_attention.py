@@ -90,6 +90,33 @@ def test_oracle_matches_brute_force(Hq, Hkv, D, window, q_lens, ctxs):
             np.testing.assert_allclose(got[cu[s]:cu[s + 1], h, :], np.array(ref), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("window", [0, 40])
+def test_sampled_rows_and_heads_match_brute_force(window):
+    """attend_sequence(rows=, heads=) evaluates only the listed query rows and
+    heads (more than 256 rows: evaluated in bounded batches) and each equals
+    the pure-Python brute force; the rest stays NaN."""
+    rng = np.random.default_rng(7 + window)
+    B, Hq, Hkv, D, ctx, ql = 4, 4, 2, 3, 320, 300
+    K = [rng.normal(size=(Hkv, ctx, D)).astype(np.float32)]
+    V = [rng.normal(size=(Hkv, ctx, D)).astype(np.float32)]
+    NB = -(-ctx // B) + 2
+    k_pool, v_pool, table = place_in_pool(K, V, B, NB, rng.permutation(NB), Hkv, D)
+    q = rng.normal(size=(ql, Hq, D)).astype(np.float64)
+    rows, heads = [299, 0, 7, 255, 256, 257], [1, 2]
+    scale = 0.5
+    got = oracle.attend_sequence(q, k_pool, v_pool, F.F32, None, None, table[0], ctx, Hkv, scale, window, B,
+                                 heads=heads, rows=rows)
+    for h in range(Hq):
+        for r in range(ql):
+            if h not in heads or r not in rows:
+                assert np.isnan(got[r, h]).all()
+                continue
+            g = h // (Hq // Hkv)
+            ref = brute_attention([[float(x) for x in q[r, h]]], [[float(x) for x in K[0][g, j]] for j in range(ctx)],
+                                  [[float(x) for x in V[0][g, j]] for j in range(ctx)], scale, [ctx - ql + r], window)
+            np.testing.assert_allclose(got[r, h], np.array(ref[0]), rtol=0, atol=1e-12)
+
+
 def test_weighted_average_example(golden):
     g = golden("weighted_average_merge.json")
     wa, wb = g["worker_a"], g["worker_b"]
