@@ -488,6 +488,7 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_ca
   return hip_status(e, "shared-prefix decode launch");
 }
 
+// The selection's compacted tables and their key counts.
 static size_t sparse_table_bytes(int32_t num_seqs, int32_t max_selected) {
   return align256((size_t)num_seqs * (size_t)(max_selected + 1) * sizeof(int)) +
          align256((size_t)num_seqs * sizeof(int));
@@ -528,7 +529,7 @@ pa_status pa_decode_sparse(void* out, const void* query, const void* k_cache, co
     g_last_error.clear();
     return PA_OK;
   }
-  if (pa::sparse_select_lds_bytes(max_context_len) > pa::kSparseMaxLds)
+  if (pa::sparse_select_lds_bytes(max_context_len, pa::kSparseRankMax) > pa::kSparseMaxLds)
     return fail(PA_ERR_UNSUPPORTED, "max_context_len %d is beyond the sparse decode's block bitmap",
                 max_context_len);
   const size_t need = pa_decode_sparse_workspace_bytes(num_seqs, max_selected, num_heads, num_kv_heads, head_size,
@@ -550,6 +551,8 @@ pa_status pa_decode_sparse(void* out, const void* query, const void* k_cache, co
   sa.cbt = reinterpret_cast<int*>(ws);
   sa.cbt_stride = max_selected + 1;
   sa.eff_ctx = reinterpret_cast<int*>(ws + align256((size_t)num_seqs * (size_t)(max_selected + 1) * sizeof(int)));
+  sa.rank_list = pa::sparse_select_lds_bytes(max_context_len, max_selected) >
+                 pa::sparse_select_lds_bytes(max_context_len, pa::kSparseRankMax);
   hipError_t e = pa::launch_sparse_select(sa, num_seqs, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, "sparse block selection launch");
 
@@ -566,8 +569,8 @@ pa_status pa_decode_sparse(void* out, const void* query, const void* k_cache, co
   a.block_table = sa.cbt;
   a.context_lens = sa.eff_ctx;
   a.cu_seqlens = nullptr;
-  bind_workspace(a, plan, dec_need ? ws + sparse_table_bytes(num_seqs, max_selected) : nullptr, num_seqs,
-                 num_heads, num_kv_heads, head_size);
+  bind_workspace(a, plan, dec_need ? ws + sparse_table_bytes(num_seqs, max_selected) : nullptr,
+                 num_seqs, num_heads, num_kv_heads, head_size);
   a.bt_stride = sa.cbt_stride;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;

@@ -117,10 +117,14 @@ struct SparseSelectArgs {
   int* cbt;
   int cbt_stride;           // max_selected + 1
   int* eff_ctx;
+  int rank_list;            // compact by rank through an LDS list (short lists; see the kernel)
 };
 constexpr int kSparseMaxSelected = 1 << 22;
-constexpr size_t kSparseMaxLds = 64 * 1024;  // bitmap + scan: contexts up to 8,257,536 tokens
-size_t sparse_select_lds_bytes(int max_context_len);
+constexpr int kSparseRankMax = 1024;         // lists shorter than this are compacted by rank
+constexpr size_t kSparseMaxLds = 64 * 1024;  // bitmap + scan (+ list): contexts up to ~8M tokens
+// LDS of the selection kernel: the bitmap and scan, plus the rank list when
+// max_selected < kSparseRankMax and it fits kSparseMaxLds (then it is used).
+size_t sparse_select_lds_bytes(int max_context_len, int max_selected);
 hipError_t launch_sparse_select(const SparseSelectArgs& a, int num_seqs, hipStream_t stream);
 
 // Decode over a paged latent (MLA) cache: [num_blocks][16][head_dim_k] bf16

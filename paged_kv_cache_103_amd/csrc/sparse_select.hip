@@ -11,8 +11,12 @@
 //
 // One workgroup per sequence. The chosen entries set bits of a per-sequence
 // bitmap of its logical blocks in LDS (so order and repeats do not matter,
-// and entries outside [0, newest block) are dropped); the set bits are then
-// compacted in ascending order by a workgroup scan of per-word popcounts.
+// and entries outside [0, newest block) are dropped). With short lists (at
+// most kSparseRankMax entries, the usual top-k sizes) the entry that sets a
+// bit first also appends its block to a list in LDS, and each listed block
+// goes to its rank among them: no scan over the bitmap's words. Longer lists
+// compact the set bits in ascending order by a workgroup scan of per-word
+// popcounts.
 #include <hip/hip_runtime.h>
 
 #include "pa_internal.h"
@@ -22,11 +26,15 @@ namespace pa {
 __global__ __launch_bounds__(256) void sparse_select_kernel(SparseSelectArgs a) {
   extern __shared__ unsigned int lds_bits[];
   int* scan = reinterpret_cast<int*>(lds_bits + a.words_max);
+  int* listed = scan + 256;  // short lists: the distinct chosen blocks, unordered
+  __shared__ int nlisted;
   const int s = blockIdx.x, tid = threadIdx.x;
   const int ctx = a.context_lens[s];
   const int nbk = min(ctx > 0 ? (ctx + 15) >> 4 : 0, a.blocks_max);
   const int W = (nbk + 31) >> 5;
+  const bool short_list = a.rank_list != 0;
   for (int w = tid; w < W; w += 256) lds_bits[w] = 0u;
+  if (tid == 0) nlisted = 0;
   __syncthreads();
   if (nbk == 0) {  // uniform over the workgroup
     if (tid == 0) a.eff_ctx[s] = 0;
@@ -34,14 +42,29 @@ __global__ __launch_bounds__(256) void sparse_select_kernel(SparseSelectArgs a) 
   }
   const int n = min(max(a.num_selected != nullptr ? a.num_selected[s] : 0, 0), a.max_selected);
   const int* sel = a.selected + (size_t)s * a.sel_stride;
-  for (int i = tid; i < n; i += 256) {
-    const int e = sel[i];
-    if (e >= 0 && e < nbk - 1) atomicOr(&lds_bits[e >> 5], 1u << (e & 31));
+  for (int i = tid; i <= n; i += 256) {
+    // entry n stands for the newest block, always read
+    const int e = i < n ? sel[i] : nbk - 1;
+    if (e >= 0 && (e < nbk - 1 || i == n)) {
+      const unsigned int bit = 1u << (e & 31);
+      const unsigned int old = atomicOr(&lds_bits[e >> 5], bit);
+      if (short_list && !(old & bit)) listed[atomicAdd(&nlisted, 1)] = e;
+    }
   }
-  if (tid == 0) atomicOr(&lds_bits[(nbk - 1) >> 5], 1u << ((nbk - 1) & 31));
   __syncthreads();
   const int* bt = a.block_table + (size_t)s * a.bt_stride;
   int* out = a.cbt + (size_t)s * a.cbt_stride;
+  if (short_list) {
+    const int m = nlisted;  // distinct blocks, the newest included
+    for (int j = tid; j < m; j += 256) {
+      const int v = listed[j];
+      int rank = 0;
+      for (int k = 0; k < m; ++k) rank += listed[k] < v;
+      out[rank] = bt[v];
+    }
+    if (tid == 0) a.eff_ctx[s] = 16 * (m - 1) + min(16, ctx - 16 * (nbk - 1));
+    return;
+  }
   int base = 0;
   for (int w0 = 0; w0 < W; w0 += 256) {
     const int w = w0 + tid;
@@ -63,14 +86,16 @@ __global__ __launch_bounds__(256) void sparse_select_kernel(SparseSelectArgs a) 
   if (tid == 0) a.eff_ctx[s] = 16 * (base - 1) + min(16, ctx - 16 * (nbk - 1));
 }
 
-size_t sparse_select_lds_bytes(int max_context_len) {
+size_t sparse_select_lds_bytes(int max_context_len, int max_selected) {
   const int blocks = (max_context_len + 15) / 16;
-  return ((size_t)(blocks + 31) / 32 + 256) * sizeof(int);
+  const size_t base = ((size_t)(blocks + 31) / 32 + 256) * sizeof(int);
+  const size_t list = (size_t)(max_selected + 1) * sizeof(int);
+  return max_selected < kSparseRankMax && base + list <= kSparseMaxLds ? base + list : base;
 }
 
 hipError_t launch_sparse_select(const SparseSelectArgs& a, int num_seqs, hipStream_t stream) {
   if (num_seqs == 0) return hipSuccess;
-  const size_t lds = (size_t)(a.words_max + 256) * sizeof(int);
+  const size_t lds = (size_t)(a.words_max + 256 + (a.rank_list ? a.max_selected + 1 : 0)) * sizeof(int);
   hipLaunchKernelGGL(sparse_select_kernel, dim3((unsigned)num_seqs), dim3(256), lds, stream, a);
   return hipGetLastError();
 }
