@@ -205,10 +205,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // ---- per-lane constant offsets ----
   // copies: piece k of a tile = bytes [1024 k, 1024 k + 1024), wholly inside
   // block k / (PIECES / 2); this lane's source offset inside that block
-  auto src_off = [&](int k, int ln) {
-    const int P = 1024 * k + 16 * ln;
-    const int row = P / S::ROWB, pch = (P % S::ROWB) / 16;
-    return (uint32_t)((row & 15) * S::ROWB + 16 * (pch ^ row_swizzle<DK>(row)));
+  auto src_off = [&](int k, int ln) {  // (unsigned: division by a constant is a multiply)
+    const uint32_t P = 1024u * (uint32_t)k + 16u * (uint32_t)ln;
+    const uint32_t row = P / (uint32_t)S::ROWB, pch = (P - row * (uint32_t)S::ROWB) >> 4;
+    return (row & 15u) * (uint32_t)S::ROWB + 16u * (pch ^ (uint32_t)row_swizzle<DK>((int)row));
   };
   const int npieces = (S::PIECES - wave + NW - 1) / NW;  // uniform per wave
   const uint32_t ring_lds = lds_addr(ring), vt_lds = lds_addr(vt);
@@ -261,10 +261,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
       lsum[g] = 0.f;
     }
 
-    auto issue = [&](int i, int ln) {  // copies of the segment's pair i into slot i % 3
+    // block ids of the segment's pair i (scalar loads)
+    auto pair_blocks = [&](int i, int& b0, int& b1) {
       const int pb = 2 * (p0 + i);
-      const int b0 = bt[pb];
-      const int b1 = pb + 1 < nblk ? bt[pb + 1] : b0;
+      b0 = bt[pb];
+      b1 = bt[min(pb + 1, nblk - 1)];  // (a last odd block pairs with itself)
+    };
+    auto issue = [&](int i, int ln, int b0, int b1) {  // copies of the segment's pair i into slot i % 3
       const uint32_t slot = ring_lds + (uint32_t)((i % S::SLOTS) * S::TILEB);
 #pragma unroll
       for (int c = 0; c < S::MAXP; ++c) {
@@ -279,8 +282,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // count the copies, and a wait it placed for the queries inside the loop
     // would drain every copy in flight each step
     wait_vm<0>();
-    issue(0, lane);
-    if (n > 1) issue(1, lane);
+    int b0, b1;
+    pair_blocks(0, b0, b1);
+    issue(0, lane, b0, b1);
+    if (n > 1) {
+      pair_blocks(1, b0, b1);
+      issue(1, lane, b0, b1);
+    }
+    // the block ids of the next pair to copy are loaded one step ahead
+    if (n > 2) pair_blocks(2, b0, b1);
 
     for (int i = 0; i < n; ++i) {
       // the copies of pair i have landed (those of pair i + 1 may be in flight)
@@ -294,59 +304,109 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
       // with 128 heads the registers are full: lane-derived addresses are
       // recomputed once per step (see lane_id_here) instead of kept live
       const int ln = H >= 128 ? lane_id_here() : lane;
-      if (i + 2 < n) issue(i + 2, ln);
+      if (i + 2 < n) {
+        issue(i + 2, ln, b0, b1);
+        if (i + 3 < n) pair_blocks(i + 3, b0, b1);
+      }
       const int key0 = 32 * (p0 + i);
       const int kend = ctx - key0;  // keys of this tile at or past kend are masked
       const uint32_t slot = ring_lds + (uint32_t)((i % S::SLOTS) * S::TILEB);
 
-      // ---- transposed fp16 value tile: item = (key quad tq, 8-dim chunk tc) ----
+      // ---- transposed fp16 value tile: item = (key quad tq, 8-dim chunk tc);
+      // done after the score product's reads are issued, so that its reads
+      // wait behind the last score MFMAs ----
+      constexpr int TI = S::TITEMS / NT;  // items per thread
+      static_assert(S::TITEMS % NT == 0, "whole items per thread");
+      u32x4 th[TI][4];  // th[c][t][w]: bf16, then fp16, pair (dims 2w, 2w+1) of key 4 tq + t
+      auto transpose_load = [&]() {
 #pragma unroll
-      for (int it0 = 0; it0 < S::TITEMS; it0 += NT) {
-        const int it = it0 + 64 * wave + ln;
-        const int tq = it & 7, tc = it >> 3;
-        u32x4 h[4];  // h[t][w]: bf16, then fp16, pair (dims 2w, 2w+1) of key 4 tq + t
+        for (int c = 0; c < TI; ++c) {
+          const int it = NT * c + 64 * wave + ln;
+          const int tq = it & 7, tc = it >> 3;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int key = 4 * tq + t;
-          h[t] = lds_read16(slot + (uint32_t)(key * S::ROWB + 16 * (tc ^ row_swizzle<DK>(key))));
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bool ok = 4 * tq + t < kend;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t b = h[t][w];
-            h[t][w] = ok ? f16x2_bits(__uint_as_float(b << 16), __uint_as_float(b & 0xffff0000u)) : 0u;
+          for (int t = 0; t < 4; ++t) {
+            const int key = 4 * tq + t;
+            th[c][t] = lds_read16(slot + (uint32_t)(key * S::ROWB + 16 * (tc ^ row_swizzle<DK>(key))));
           }
         }
+      };
+      auto transpose_store = [&]() {
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          // dim 8 tc + d: keys 4 tq .. 4 tq + 3
-          const int w = d >> 1;
-          const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
-          const uint32_t lo2 = __builtin_amdgcn_perm(h[1][w], h[0][w], sel);
-          const uint32_t hi2 = __builtin_amdgcn_perm(h[3][w], h[2][w], sel);
-          lds_write8(vt_lds + (uint32_t)((8 * tc + d) * MLA_VT_ROW + 8 * tq), lo2, hi2);
+        for (int c = 0; c < TI; ++c) {
+          const int it = NT * c + 64 * wave + ln;
+          const int tq = it & 7, tc = it >> 3;
+          u32x4 (&h)[4] = th[c];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t keep = 4 * tq + t < kend ? 0xffffffffu : 0u;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const uint32_t b = h[t][w];
+              h[t][w] = f16x2_bits(__uint_as_float(b << 16), __uint_as_float(b & 0xffff0000u)) & keep;
+            }
+          }
+#pragma unroll
+          for (int d = 0; d < 8; ++d) {
+            // dim 8 tc + d: keys 4 tq .. 4 tq + 3
+            const int w = d >> 1;
+            const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+            const uint32_t lo2 = __builtin_amdgcn_perm(h[1][w], h[0][w], sel);
+            const uint32_t hi2 = __builtin_amdgcn_perm(h[3][w], h[2][w], sel);
+            lds_write8(vt_lds + (uint32_t)((8 * tc + d) * MLA_VT_ROW + 8 * tq), lo2, hi2);
+          }
         }
-      }
+      };
 
       // ---- scores S^T: per head group, 2 tiles of 16 permuted keys x 16 heads ----
-      f32x4 st[HG][2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int g = 0; g < HG; ++g) st[g][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // Operand chunk of k-step j: (4 j + rq) ^ swz. The swizzle only touches
+      // the low NB * 4 chunks' bits, so the address is one of NB per-lane
+      // bases plus a constant: bases[j % NB] + 64 NB (j / NB) bytes.
+      constexpr int NB = DK == 576 ? 2 : 4;
+      uint32_t kb[2][NB];
+      {
         const int r16 = ln & 15, rq = ln >> 4;
-        const int key = 8 * (r16 >> 2) + 4 * kt + (r16 & 3);
-        const uint32_t rb = slot + (uint32_t)(key * S::ROWB);
-        const int swz = row_swizzle<DK>(key);
 #pragma unroll
-        for (int j = 0; j < S::KS; ++j) {
-          const u32x4 kf = lds_read16(rb + (uint32_t)(16 * ((4 * j + rq) ^ swz)));
+        for (int kt = 0; kt < 2; ++kt) {
+          const int key = 8 * (r16 >> 2) + 4 * kt + (r16 & 3);
+          const int swz = row_swizzle<DK>(key);
 #pragma unroll
-          for (int g = 0; g < HG; ++g) st[g][kt] = mfma_bf16(kf, qf[g][j], st[g][kt]);
+          for (int b = 0; b < NB; ++b)
+            kb[kt][b] = slot + (uint32_t)(key * S::ROWB + 16 * (((b << 2) | rq) ^ swz));
         }
       }
+      f32x4 st[HG][2];
+#pragma unroll
+      for (int g = 0; g < HG; ++g) st[g][0] = st[g][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // k-step j of key tile kt is read PD reads ahead of its MFMAs
+      constexpr int NKR = 2 * S::KS, PD = 4;
+      auto kread = [&](int r) {
+        const int j = r >> 1, kt = r & 1;
+        return lds_read16(kb[kt][j % NB] + (uint32_t)(64 * NB * (j / NB)));
+      };
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4 kbuf[PD];
+#pragma unroll
+      for (int r = 0; r < PD; ++r) kbuf[r] = kread(r);
+#pragma unroll
+      for (int r = 0; r < NKR; ++r) {
+        const u32x4 kf = kbuf[r % PD];
+        if (r + PD < NKR) kbuf[r % PD] = kread(r + PD);
+#pragma unroll
+        for (int g = 0; g < HG; ++g) st[g][r & 1] = mfma_bf16(kf, qf[g][r >> 1], st[g][r & 1]);
+      }
+      transpose_load();
+      // keep PD reads in flight: reads, then (MFMAs of one read, next read);
+      // the transposition's reads go out behind the last score reads
+      __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
+#pragma unroll
+      for (int r = 0; r < NKR - PD; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, HG, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * TI, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, HG * PD, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      transpose_store();
       u32x4 pf[HG];
 #pragma unroll
       for (int g = 0; g < HG; ++g) {
@@ -390,11 +450,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
       barrier_keep_loads();  // the transposed value tile is complete
       // ---- O^T += V^T P^T ----
       const uint32_t pv_base = vt_lds + (uint32_t)((dp * DVW + (ln & 15)) * MLA_VT_ROW + 16 * (ln >> 4));
+      // (value fragments read VD ahead of their MFMAs)
+      constexpr int VD = 4;
+      u32x4 vbuf[VD];
+#pragma unroll
+      for (int t = 0; t < VD && t < DTW; ++t) vbuf[t] = lds_read16(pv_base + (uint32_t)(16 * t * MLA_VT_ROW));
 #pragma unroll
       for (int t = 0; t < DTW; ++t) {
-        const u32x4 vf = lds_read16(pv_base + (uint32_t)(16 * t * MLA_VT_ROW));
+        const u32x4 vf = vbuf[t % VD];
+        if (t + VD < DTW) vbuf[t % VD] = lds_read16(pv_base + (uint32_t)(16 * (t + VD) * MLA_VT_ROW));
 #pragma unroll
         for (int g = 0; g < HG; ++g) o[g][t] = mfma_f16(vf, pf[g], o[g][t]);
+      }
+      if constexpr (DTW > VD) {
+        __builtin_amdgcn_sched_group_barrier(0x100, VD, 0);
+#pragma unroll
+        for (int t = 0; t < DTW - VD; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x008, HG, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, HG * VD, 0);
       }
     }
     // ---- result of the segment ----
