@@ -85,11 +85,16 @@ typedef enum {
   PA_ERR_OUT_OF_BLOCKS = 5       /* block manager: too few free blocks (pa_blocks.h) */
 } pa_status;
 
-typedef enum {
+enum {
   PA_F32 = 0,
   PA_BF16 = 1,
   PA_FP8_E4M3 = 2                /* OCP e4m3fn, KV cache only */
-} pa_dtype;
+};
+/* A dtype argument: one of the PA_F32 / PA_BF16 / PA_FP8_E4M3 codes. It is
+   a plain int32_t, so that any other value reaches the library as it is and
+   is rejected there (PA_ERR_INVALID_ARGUMENT) rather than being an
+   out-of-range enum value. */
+typedef int32_t pa_dtype;
 
 #define PA_ABI_VERSION 1
 #define PA_BLOCK_SIZE 16
@@ -420,8 +425,10 @@ pa_status pa_check_batch(const int32_t* block_table, int32_t block_table_stride,
                          int32_t max_context_len, int32_t num_blocks, int32_t sliding_window,
                          const int64_t* slot_mapping);
 
-/* Static name of a status code. */
-const char* pa_status_string(pa_status s);
+/* Static name of a status code: any int (a pa_status value, or "PA_ERR_UNKNOWN"
+   for one that is not; an int so that an unknown code is not an out-of-range
+   enum value). */
+const char* pa_status_string(int32_t status);
 
 /* Detail of the calling thread's last non-OK status ("" if none). */
 const char* pa_last_error(void);

@@ -79,6 +79,55 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host sources of libpa.so: argument checking, plans, the block manager.
+HOST_SOURCES = ["pa_api.cpp", "pa_check.cpp", "pa_blocks.cpp"]
+SAN_LIB = os.path.join(BUILD, "libpa_host_sanitized.so")
+
+
+def asan_runtime() -> str:
+    """The AddressSanitizer runtime of hipcc's clang (preloaded into the
+    Python process that loads the sanitized library)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    base = os.path.join(rocm, "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(base), reverse=True) if os.path.isdir(base) else []:
+        cand = os.path.join(base, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(cand):
+            return cand
+    raise FileNotFoundError("libclang_rt.asan-x86_64.so not found under " + base)
+
+
+def build_host_sanitized() -> str:
+    """libpa with its host sources built under AddressSanitizer and
+    UndefinedBehaviorSanitizer (host code only: the GPU objects are the
+    regular ones), for the CPU tests of the host logic. Returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    flags = [f for f in compile_flags() if f != "-O3"] + ["-O1", "-g"] + san
+
+    def one(src: str) -> str:
+        obj = os.path.join(BUILD, "san_" + os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc()] + flags + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    gpu_objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s not in HOST_SOURCES]
+    if not all(os.path.exists(o) for o in gpu_objs):
+        build()
+    with ThreadPoolExecutor(len(HOST_SOURCES)) as ex:
+        host_objs = list(ex.map(one, HOST_SOURCES))
+    tmp = SAN_LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-o", tmp] + host_objs + gpu_objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

@@ -702,7 +702,7 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_
   return hip_status(e, "copy_blocks launch");
 }
 
-const char* pa_status_string(pa_status s) {
+const char* pa_status_string(int32_t s) {
   switch (s) {
     case PA_OK: return "PA_OK";
     case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT";
