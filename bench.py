@@ -637,6 +637,31 @@ def measure_ceilings(torch):
 
         t = time_runs(torch, f, 10, 2, lambda: None)
         res[name] = round(flops[0] / (t["median_ms"] * 1e-3) / 1e12, 1)
+    # LDS per compute unit (bytes per shader-clock cycle) and the issue mix of
+    # a softmax step (cycles per round of 16 MFMAs + 64 FMAs + 16 exp2 per
+    # wave), each from s_memtime cycle counts
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    cyc = torch.zeros(8 * ncu, dtype=torch.int64, device="cuda")
+    for kind, name in ((0, "lds_read16_bytes_per_clk_cu"), (1, "lds_read16_2way_bytes_per_clk_cu"),
+                       (2, "lds_write8_bytes_per_clk_cu")):
+        nb = peaks.lds(kind, 2000, ncu, sink, cyc)
+        torch.cuda.synchronize()
+        res[name] = round(nb / float(cyc[:ncu].max().item()), 1)
+    mix = {}
+    for waves in (4, 8):
+        for mode, name in ((0, "mfma"), (1, "valu"), (2, "interleaved")):
+            cyc.zero_()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            peaks.issue(mode, waves, 1000, ncu, sink, cyc)
+            ev1.record()
+            torch.cuda.synchronize()
+            c = float(cyc.view(ncu, 8)[:, :waves].max().item())
+            # cycles of one round per wave (with two waves per SIMD, the SIMD
+            # completes two rounds in that time), and the clock they ran at
+            mix[f"{name}_{waves // 4}_waves_per_simd_cycles"] = round(c / 1000, 1)
+            mix[f"{name}_{waves // 4}_waves_per_simd_clock_ghz"] = round(c / (ev0.elapsed_time(ev1) * 1e6), 2)
+    res["softmax_step_issue"] = mix
     return res
 
 

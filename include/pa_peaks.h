@@ -41,6 +41,31 @@ int32_t pa_peak_read_tiles(const void* buf, const int32_t* tile_ids, int32_t nti
  */
 int32_t pa_peak_mfma(int32_t kind, int32_t iters, int32_t grid_blocks, float* sink, pa_stream_t stream);
 
+/*
+ * LDS bandwidth of one compute unit: grid_blocks workgroups of 512 threads
+ * (8 waves; 96 KiB of LDS each, so one per compute unit) run `iters` rounds
+ * of 8 LDS accesses per lane; kind 0: 16-byte reads, consecutive lanes on
+ * consecutive addresses (no bank conflicts); kind 1: the same with a 32-byte
+ * lane stride (two-way conflicts); kind 2: 8-byte writes of consecutive
+ * lanes. Bytes per workgroup: iters * 8 * 512 * (16, 16 or 8).
+ * cycles: >= grid_blocks int64, each workgroup's loop time in shader-clock
+ * cycles (s_memtime). sink: >= 512 * grid_blocks uint32.
+ */
+int32_t pa_peak_lds(int32_t kind, int32_t iters, int32_t grid_blocks, uint32_t* sink, int64_t* cycles,
+                    pa_stream_t stream);
+
+/*
+ * Issue mix of one SIMD: grid_blocks workgroups of 64 * waves threads (waves
+ * 4 or 8: one or two waves per SIMD; 96 KiB of LDS each, so one per compute
+ * unit), each wave running `iters` rounds of 16 32x32x16 bf16 MFMAs and 64
+ * fp32 FMAs plus 16 exp2 (the softmax of a 32-key step), as mode 0: matrix
+ * work only, 1: vector work only, 2: both, interleaved (one MFMA, then 5
+ * vector instructions). cycles: >= grid_blocks * 8 int64, each wave's loop
+ * time in shader-clock cycles. sink: >= 512 * grid_blocks floats.
+ */
+int32_t pa_peak_issue(int32_t mode, int32_t waves, int32_t iters, int32_t grid_blocks, float* sink,
+                      int64_t* cycles, pa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

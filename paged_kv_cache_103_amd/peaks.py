@@ -11,7 +11,7 @@ import torch
 from . import _lib
 
 PEAKS_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpa_peaks.so")
-EXPORTED = ("pa_peak_read_tiles", "pa_peak_mfma")
+EXPORTED = ("pa_peak_read_tiles", "pa_peak_mfma", "pa_peak_lds", "pa_peak_issue")
 
 _L = None
 
@@ -27,6 +27,10 @@ def load() -> ctypes.CDLL:
         L.pa_peak_read_tiles.argtypes = [vp, vp, i32, i32, i32, vp, vp]
         L.pa_peak_mfma.restype = i32
         L.pa_peak_mfma.argtypes = [i32, i32, i32, vp, vp]
+        L.pa_peak_lds.restype = i32
+        L.pa_peak_lds.argtypes = [i32, i32, i32, vp, vp, vp]
+        L.pa_peak_issue.restype = i32
+        L.pa_peak_issue.argtypes = [i32, i32, i32, i32, vp, vp, vp]
         _L = L
     return _L
 
@@ -50,3 +54,29 @@ def mfma(kind: int, iters: int, grid_blocks: int, sink: torch.Tensor) -> float:
     if st != 0:
         raise RuntimeError(f"pa_peak_mfma launch failed (HIP error {st})")
     return 4.0 * 32768 * iters * grid_blocks * 4
+
+
+def lds(kind: int, iters: int, grid_blocks: int, sink: torch.Tensor, cycles: torch.Tensor) -> float:
+    """LDS traffic of one compute unit (kind 0: conflict-free 16-byte reads,
+    1: two-way conflicted 16-byte reads, 2: 8-byte writes); returns the bytes
+    each workgroup moves. cycles (int64, >= grid_blocks) receives each
+    workgroup's loop time in shader-clock cycles."""
+    assert sink.numel() * sink.element_size() >= 4 * 512 * grid_blocks
+    assert cycles.dtype == torch.int64 and cycles.numel() >= grid_blocks
+    st = load().pa_peak_lds(kind, iters, grid_blocks, sink.data_ptr(), cycles.data_ptr(), _lib._stream(None))
+    if st != 0:
+        raise RuntimeError(f"pa_peak_lds launch failed (HIP error {st})")
+    return float(iters) * 8 * 512 * (8 if kind == 2 else 16)
+
+
+def issue(mode: int, waves: int, iters: int, grid_blocks: int, sink: torch.Tensor, cycles: torch.Tensor) -> None:
+    """Matrix (mode 0), vector (1) or interleaved (2) work of a softmax step
+    per wave, with `waves` (4 or 8) waves per compute unit; cycles (int64, >=
+    8 * grid_blocks) receives each wave's loop time in shader-clock cycles."""
+    assert waves in (4, 8)
+    assert sink.numel() * sink.element_size() >= 4 * 512 * grid_blocks
+    assert cycles.dtype == torch.int64 and cycles.numel() >= 8 * grid_blocks
+    st = load().pa_peak_issue(mode, waves, iters, grid_blocks, sink.data_ptr(), cycles.data_ptr(),
+                              _lib._stream(None))
+    if st != 0:
+        raise RuntimeError(f"pa_peak_issue launch failed (HIP error {st})")
