@@ -20,13 +20,18 @@
 //    major with a per-row XOR swizzle of its 16-byte chunks (conflict-free
 //    score-operand reads);
 //  * one pass by all 512 threads writes the value part again, transposed and
-//    converted to fp16 ([512 dims][32 keys], 80-byte rows), zeroing keys past
-//    the context: the value product needs 8 consecutive keys of one dim per
-//    lane, the score product 8 consecutive dims of one key;
+//    converted to fp16 ([512 dims][32 keys], 64-byte rows with a chunk
+//    swizzle), zeroing keys past the context: the value product needs 8
+//    consecutive keys of one dim per lane, the score product 8 consecutive
+//    dims of one key;
 //  * scores S^T = C Q^T on 16x16x32 bf16 MFMAs (queries held in registers as
 //    the B operand, keys in the permuted row order that makes each lane's
 //    score accumulator its own P^T operand), online softmax with lazy
 //    rescaling, O^T += V^T P^T on 16x16x32 fp16 MFMAs with P scaled by 2^7.
+//    With 128 heads the value product instead runs on 32x32x16 fp16 tiles of
+//    32 heads x 256 dims per wave (half the value-tile reads): the wave that
+//    scored 16 heads leaves their P^T rows and rescale factors in LDS for the
+//    two waves that own those heads' outputs.
 //    A value beyond fp16's range (65504) becomes infinity in the tile and
 //    leaves inf or NaN in the outputs of every head; the merge kernel finds
 //    such rows and computes them again exactly (fp32, from the bf16 rows), so
@@ -45,11 +50,19 @@ namespace pa {
 namespace {
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int MLA_DV = 512;
-constexpr int MLA_VT_ROW = 80;  // bytes per transposed value row (64 data + 16 pad)
+constexpr int MLA_VT_ROW = 64;  // bytes per transposed value row: 32 keys in fp16
+// 16-byte chunk c (8 keys) of transposed value row d sits at chunk
+// c ^ vt_swizzle(d): 16 consecutive rows read at one chunk column hit 16
+// distinct bank groups.
+__device__ __forceinline__ int vt_swizzle(int d) { return (d >> 2) & 3; }
+__device__ __forceinline__ uint32_t vt_offset(int d, int chunk) {
+  return (uint32_t)(d * MLA_VT_ROW + 16 * (chunk ^ vt_swizzle(d)));
+}
 
 __device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -187,8 +200,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   constexpr int NDP = NW / NHG;        // value-dim parts
   constexpr int DVW = MLA_DV / NDP;    // value dims per wave
   constexpr int DTW = DVW / 16;        // 16-dim output tiles per wave
+  // 128 heads: the value product runs on 32x32 tiles of 32 heads x 256 dims
+  // per wave (half the value-tile reads of 16-head tiles), its weights P and
+  // rescale factors passed through LDS by the waves that scored those heads
+  constexpr bool WIDE = H == 128 && HG == 1 && NW == 8;
+  constexpr int WDT = 8;               // WIDE: 32-dim output tiles per wave
   __shared__ __attribute__((aligned(16))) uint8_t ring[S::SLOTS * S::TILEB];
   __shared__ __attribute__((aligned(16))) uint8_t vt[MLA_DV * MLA_VT_ROW];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[WIDE ? H * 64 : 16];  // P^T rows (heads) of 32 fp16 keys
+  __shared__ float alpha_sh[WIDE ? H : 1];  // per head: the rescale of this step
+  __shared__ float lsum_sh[WIDE ? H : 1];   // per head: the segment's sum
   __shared__ int psum[kMlaMaxSeqs + 1];
   __shared__ int scan[NT];
 
@@ -249,11 +270,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
       for (int j = 0; j < S::KS; ++j) qf[g][j] = load16(qp + 64 * j);
     }
-    f32x4 o[HG][DTW];
+    f32x4 o[HG][WIDE ? 1 : DTW];
+    f32x16 ow[WIDE ? WDT : 1];  // WIDE: dims 256 (wave / 4) + 32 t .. of heads 32 (wave % 4) ..
+    if constexpr (WIDE) {
 #pragma unroll
-    for (int g = 0; g < HG; ++g)
+      for (int t = 0; t < WDT; ++t) ow[t] = f32x16{};
+    } else {
 #pragma unroll
-      for (int t = 0; t < DTW; ++t) o[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int g = 0; g < HG; ++g)
+#pragma unroll
+        for (int t = 0; t < DTW; ++t) o[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     float m[HG], lsum[HG];
 #pragma unroll
     for (int g = 0; g < HG; ++g) {
@@ -284,10 +311,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     wait_vm<0>();
     int b0, b1;
     pair_blocks(0, b0, b1);
-    issue(0, lane, b0, b1);
+    issue(0, H >= 128 ? lane_id_here() : lane, b0, b1);
     if (n > 1) {
       pair_blocks(1, b0, b1);
-      issue(1, lane, b0, b1);
+      issue(1, H >= 128 ? lane_id_here() : lane, b0, b1);
     }
     // the block ids of the next pair to copy are loaded one step ahead
     if (n > 2) pair_blocks(2, b0, b1);
@@ -352,7 +379,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
             const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
             const uint32_t lo2 = __builtin_amdgcn_perm(h[1][w], h[0][w], sel);
             const uint32_t hi2 = __builtin_amdgcn_perm(h[3][w], h[2][w], sel);
-            lds_write8(vt_lds + (uint32_t)((8 * tc + d) * MLA_VT_ROW + 8 * tq), lo2, hi2);
+            lds_write8(vt_lds + vt_offset(8 * tc + d, tq >> 1) + 8 * (tq & 1), lo2, hi2);
           }
         }
       };
@@ -424,7 +451,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
           }
         tmax = strided_max<16>(tmax);  // key 0 of the tile is always valid
         const bool up = tmax > m[g] + 8.f;
-        if (__any(up)) {
+        if constexpr (WIDE) {
+          // the wave that owns this head's outputs applies the rescale
+          const float alpha = up ? __builtin_amdgcn_exp2f(m[g] - tmax) : 1.f;
+          m[g] = up ? tmax : m[g];
+          lsum[g] *= alpha;
+          if (q4 == 0) alpha_sh[16 * wave + c16] = alpha;
+        } else if (__any(up)) {
           const float alpha = up ? __builtin_amdgcn_exp2f(m[g] - tmax) : 1.f;
           m[g] = up ? tmax : m[g];
           lsum[g] *= alpha;
@@ -445,12 +478,59 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
         pf[g][1] = f16x2_bits(pv[2], pv[3]);
         pf[g][2] = f16x2_bits(pv[4], pv[5]);
         pf[g][3] = f16x2_bits(pv[6], pv[7]);
+        if constexpr (WIDE) {  // P^T row of head 16 wave + c16, keys 8 q4 .. 8 q4 + 7
+          typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+          const int head = 16 * wave + c16;
+          *(lds_u32x4*)(uintptr_t)(lds_addr(pbuf) + (uint32_t)(head * 64 + 16 * (q4 ^ vt_swizzle(head)))) = pf[g];
+        }
       }
 
-      barrier_keep_loads();  // the transposed value tile is complete
+      barrier_keep_loads();  // the transposed value tile (and P) are complete
+      if constexpr (WIDE) {
+        // ---- O^T += V^T P^T on 32x32x16 tiles: this wave's dims 256 (wave /
+        // 4) + 32 t + (lane % 32), heads 32 (wave % 4) + (lane % 32); k-step
+        // ks covers keys 16 ks + 8 (lane / 32) .. + 7 ----
+        const int l32 = ln & 31, kh = ln >> 5;
+        const int head = 32 * (wave & 3) + l32;
+        const float al = alpha_sh[head];
+        if (__any(al != 1.f)) {
+#pragma unroll
+          for (int t = 0; t < WDT; ++t) ow[t] *= al;
+        }
+        typedef __attribute__((address_space(3))) const u32x4 lds_cu32x4;
+        u32x4 pw[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          pw[ks] = *(lds_cu32x4*)(uintptr_t)(lds_addr(pbuf) + (uint32_t)(head * 64 + 16 * ((2 * ks + kh) ^ vt_swizzle(head))));
+        const int d0 = 256 * (wave >> 2) + l32;
+        uint32_t vb[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) vb[ks] = vt_lds + vt_offset(d0, 2 * ks + kh);
+        constexpr int NVR = 2 * WDT, VD = 4;  // value reads (tile t, k-step ks) = read 2 t + ks
+        auto vread = [&](int r) { return lds_read16(vb[r & 1] + (uint32_t)(32 * MLA_VT_ROW * (r >> 1))); };
+        u32x4 vbuf[VD];
+#pragma unroll
+        for (int r = 0; r < VD; ++r) vbuf[r] = vread(r);
+#pragma unroll
+        for (int r = 0; r < NVR; ++r) {
+          const u32x4 vf = vbuf[r % VD];
+          if (r + VD < NVR) vbuf[r % VD] = vread(r + VD);
+          ow[r >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, vf),
+                                                             __builtin_bit_cast(f16x8_t, pw[r & 1]), ow[r >> 1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, VD + 2, 0);
+#pragma unroll
+        for (int r = 0; r < NVR - VD; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, VD, 0);
+        continue;
+      }
       // ---- O^T += V^T P^T ----
-      const uint32_t pv_base = vt_lds + (uint32_t)((dp * DVW + (ln & 15)) * MLA_VT_ROW + 16 * (ln >> 4));
-      // (value fragments read VD ahead of their MFMAs)
+      const uint32_t pv_base = vt_lds + vt_offset(dp * DVW + (ln & 15), ln >> 4);
+      // (value fragments read VD ahead of their MFMAs; rows 16 t apart keep
+      // the swizzle)
       constexpr int VD = 4;
       u32x4 vbuf[VD];
 #pragma unroll
@@ -474,6 +554,52 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     }
     // ---- result of the segment ----
     const bool single = (sp0 / C) == ((sp0 + np - 1) / C);
+    if constexpr (WIDE) {
+      // the scoring waves publish each head's sum (and leave the summary's
+      // max and sum); the owners of the outputs normalise or store them
+      // (lane-derived addresses from a fresh lane id: kept live across the
+      // segment loop they would not fit the registers)
+      const int ln = lane_id_here();
+      const float L = strided_sum<16>(lsum[0]);
+      if ((ln >> 4) == 0) {
+        lsum_sh[16 * wave + (ln & 15)] = L;
+        if (!single) {
+          const size_t rec = (size_t)(blockIdx.x + s) * H + 16 * wave + (ln & 15);
+          a.part_ml[rec * 2] = m[0] - 7.f;
+          a.part_ml[rec * 2 + 1] = L;
+        }
+      }
+      barrier_keep_loads();
+      // lane: head 32 (wave % 4) + lane % 32; ow[t][4 j + r] is dim
+      // 256 (wave / 4) + 32 t + 8 j + 4 (lane / 32) + r
+      const int head = 32 * (wave & 3) + (ln & 31);
+      const int d0 = 256 * (wave >> 2) + 4 * (ln >> 5);
+      if (single) {
+        const float inv = 1.f / lsum_sh[head];
+        uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)s * H + head) * MLA_DV + d0;
+#pragma unroll
+        for (int t = 0; t < WDT; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            uint2 w;
+            w.x = pack_bf16x2(ow[t][4 * j] * inv, ow[t][4 * j + 1] * inv);
+            w.y = pack_bf16x2(ow[t][4 * j + 2] * inv, ow[t][4 * j + 3] * inv);
+            *reinterpret_cast<uint2*>(op + 32 * t + 8 * j) = w;
+          }
+      } else {
+        const size_t rec = (size_t)(blockIdx.x + s) * H + head;
+        float* op = a.part_o + rec * MLA_DV + d0;
+#pragma unroll
+        for (int t = 0; t < WDT; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<f32x4*>(op + 32 * t + 8 * j) =
+                f32x4{ow[t][4 * j], ow[t][4 * j + 1], ow[t][4 * j + 2], ow[t][4 * j + 3]};
+      }
+      barrier_keep_loads();  // the ring and the head sums are reused by the next segment
+      x = (long long)sp0 + p1;
+      continue;
+    }
 #pragma unroll
     for (int g = 0; g < HG; ++g) {
       const float L = strided_sum<16>(lsum[g]);
