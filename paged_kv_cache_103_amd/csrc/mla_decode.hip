@@ -28,10 +28,8 @@
 //    the B operand, keys in the permuted row order that makes each lane's
 //    score accumulator its own P^T operand), online softmax with lazy
 //    rescaling, O^T += V^T P^T on 16x16x32 fp16 MFMAs with P scaled by 2^7.
-//    With 128 heads the value product instead runs on 32x32x16 fp16 tiles of
-//    32 heads x 256 dims per wave (half the value-tile reads): the wave that
-//    scored 16 heads leaves their P^T rows and rescale factors in LDS for the
-//    two waves that own those heads' outputs.
+//    (128 heads take mla_decode_wide below: the same steps, the value
+//    product on 32x32 tiles, one barrier per step.)
 //    A value beyond fp16's range (65504) becomes infinity in the tile and
 //    leaves inf or NaN in the outputs of every head; the merge kernel finds
 //    such rows and computes them again exactly (fp32, from the bf16 rows), so
@@ -200,16 +198,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   constexpr int NDP = NW / NHG;        // value-dim parts
   constexpr int DVW = MLA_DV / NDP;    // value dims per wave
   constexpr int DTW = DVW / 16;        // 16-dim output tiles per wave
-  // 128 heads: the value product runs on 32x32 tiles of 32 heads x 256 dims
-  // per wave (half the value-tile reads of 16-head tiles), its weights P and
-  // rescale factors passed through LDS by the waves that scored those heads
-  constexpr bool WIDE = H == 128 && HG == 1 && NW == 8;
-  constexpr int WDT = 8;               // WIDE: 32-dim output tiles per wave
   __shared__ __attribute__((aligned(16))) uint8_t ring[S::SLOTS * S::TILEB];
   __shared__ __attribute__((aligned(16))) uint8_t vt[MLA_DV * MLA_VT_ROW];
-  __shared__ __attribute__((aligned(16))) uint8_t pbuf[WIDE ? H * 64 : 16];  // P^T rows (heads) of 32 fp16 keys
-  __shared__ float alpha_sh[WIDE ? H : 1];  // per head: the rescale of this step
-  __shared__ float lsum_sh[WIDE ? H : 1];   // per head: the segment's sum
   __shared__ int psum[kMlaMaxSeqs + 1];
   __shared__ int scan[NT];
 
@@ -270,17 +260,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
       for (int j = 0; j < S::KS; ++j) qf[g][j] = load16(qp + 64 * j);
     }
-    f32x4 o[HG][WIDE ? 1 : DTW];
-    f32x16 ow[WIDE ? WDT : 1];  // WIDE: dims 256 (wave / 4) + 32 t .. of heads 32 (wave % 4) ..
-    if constexpr (WIDE) {
+    f32x4 o[HG][DTW];
 #pragma unroll
-      for (int t = 0; t < WDT; ++t) ow[t] = f32x16{};
-    } else {
+    for (int g = 0; g < HG; ++g)
 #pragma unroll
-      for (int g = 0; g < HG; ++g)
-#pragma unroll
-        for (int t = 0; t < DTW; ++t) o[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+      for (int t = 0; t < DTW; ++t) o[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m[HG], lsum[HG];
 #pragma unroll
     for (int g = 0; g < HG; ++g) {
@@ -451,13 +435,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
           }
         tmax = strided_max<16>(tmax);  // key 0 of the tile is always valid
         const bool up = tmax > m[g] + 8.f;
-        if constexpr (WIDE) {
-          // the wave that owns this head's outputs applies the rescale
-          const float alpha = up ? __builtin_amdgcn_exp2f(m[g] - tmax) : 1.f;
-          m[g] = up ? tmax : m[g];
-          lsum[g] *= alpha;
-          if (q4 == 0) alpha_sh[16 * wave + c16] = alpha;
-        } else if (__any(up)) {
+        if (__any(up)) {
           const float alpha = up ? __builtin_amdgcn_exp2f(m[g] - tmax) : 1.f;
           m[g] = up ? tmax : m[g];
           lsum[g] *= alpha;
@@ -478,55 +456,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
         pf[g][1] = f16x2_bits(pv[2], pv[3]);
         pf[g][2] = f16x2_bits(pv[4], pv[5]);
         pf[g][3] = f16x2_bits(pv[6], pv[7]);
-        if constexpr (WIDE) {  // P^T row of head 16 wave + c16, keys 8 q4 .. 8 q4 + 7
-          typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-          const int head = 16 * wave + c16;
-          *(lds_u32x4*)(uintptr_t)(lds_addr(pbuf) + (uint32_t)(head * 64 + 16 * (q4 ^ vt_swizzle(head)))) = pf[g];
-        }
       }
 
-      barrier_keep_loads();  // the transposed value tile (and P) are complete
-      if constexpr (WIDE) {
-        // ---- O^T += V^T P^T on 32x32x16 tiles: this wave's dims 256 (wave /
-        // 4) + 32 t + (lane % 32), heads 32 (wave % 4) + (lane % 32); k-step
-        // ks covers keys 16 ks + 8 (lane / 32) .. + 7 ----
-        const int l32 = ln & 31, kh = ln >> 5;
-        const int head = 32 * (wave & 3) + l32;
-        const float al = alpha_sh[head];
-        if (__any(al != 1.f)) {
-#pragma unroll
-          for (int t = 0; t < WDT; ++t) ow[t] *= al;
-        }
-        typedef __attribute__((address_space(3))) const u32x4 lds_cu32x4;
-        u32x4 pw[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          pw[ks] = *(lds_cu32x4*)(uintptr_t)(lds_addr(pbuf) + (uint32_t)(head * 64 + 16 * ((2 * ks + kh) ^ vt_swizzle(head))));
-        const int d0 = 256 * (wave >> 2) + l32;
-        uint32_t vb[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) vb[ks] = vt_lds + vt_offset(d0, 2 * ks + kh);
-        constexpr int NVR = 2 * WDT, VD = 4;  // value reads (tile t, k-step ks) = read 2 t + ks
-        auto vread = [&](int r) { return lds_read16(vb[r & 1] + (uint32_t)(32 * MLA_VT_ROW * (r >> 1))); };
-        u32x4 vbuf[VD];
-#pragma unroll
-        for (int r = 0; r < VD; ++r) vbuf[r] = vread(r);
-#pragma unroll
-        for (int r = 0; r < NVR; ++r) {
-          const u32x4 vf = vbuf[r % VD];
-          if (r + VD < NVR) vbuf[r % VD] = vread(r + VD);
-          ow[r >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, vf),
-                                                             __builtin_bit_cast(f16x8_t, pw[r & 1]), ow[r >> 1], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, VD + 2, 0);
-#pragma unroll
-        for (int r = 0; r < NVR - VD; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, VD, 0);
-        continue;
-      }
+      barrier_keep_loads();  // the transposed value tile is complete
       // ---- O^T += V^T P^T ----
       const uint32_t pv_base = vt_lds + vt_offset(dp * DVW + (ln & 15), ln >> 4);
       // (value fragments read VD ahead of their MFMAs; rows 16 t apart keep
@@ -554,52 +486,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     }
     // ---- result of the segment ----
     const bool single = (sp0 / C) == ((sp0 + np - 1) / C);
-    if constexpr (WIDE) {
-      // the scoring waves publish each head's sum (and leave the summary's
-      // max and sum); the owners of the outputs normalise or store them
-      // (lane-derived addresses from a fresh lane id: kept live across the
-      // segment loop they would not fit the registers)
-      const int ln = lane_id_here();
-      const float L = strided_sum<16>(lsum[0]);
-      if ((ln >> 4) == 0) {
-        lsum_sh[16 * wave + (ln & 15)] = L;
-        if (!single) {
-          const size_t rec = (size_t)(blockIdx.x + s) * H + 16 * wave + (ln & 15);
-          a.part_ml[rec * 2] = m[0] - 7.f;
-          a.part_ml[rec * 2 + 1] = L;
-        }
-      }
-      barrier_keep_loads();
-      // lane: head 32 (wave % 4) + lane % 32; ow[t][4 j + r] is dim
-      // 256 (wave / 4) + 32 t + 8 j + 4 (lane / 32) + r
-      const int head = 32 * (wave & 3) + (ln & 31);
-      const int d0 = 256 * (wave >> 2) + 4 * (ln >> 5);
-      if (single) {
-        const float inv = 1.f / lsum_sh[head];
-        uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)s * H + head) * MLA_DV + d0;
-#pragma unroll
-        for (int t = 0; t < WDT; ++t)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            uint2 w;
-            w.x = pack_bf16x2(ow[t][4 * j] * inv, ow[t][4 * j + 1] * inv);
-            w.y = pack_bf16x2(ow[t][4 * j + 2] * inv, ow[t][4 * j + 3] * inv);
-            *reinterpret_cast<uint2*>(op + 32 * t + 8 * j) = w;
-          }
-      } else {
-        const size_t rec = (size_t)(blockIdx.x + s) * H + head;
-        float* op = a.part_o + rec * MLA_DV + d0;
-#pragma unroll
-        for (int t = 0; t < WDT; ++t)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<f32x4*>(op + 32 * t + 8 * j) =
-                f32x4{ow[t][4 * j], ow[t][4 * j + 1], ow[t][4 * j + 2], ow[t][4 * j + 3]};
-      }
-      barrier_keep_loads();  // the ring and the head sums are reused by the next segment
-      x = (long long)sp0 + p1;
-      continue;
-    }
 #pragma unroll
     for (int g = 0; g < HG; ++g) {
       const float L = strided_sum<16>(lsum[g]);
@@ -627,6 +513,350 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     }
     barrier_keep_loads();  // the ring is reused by the next segment
     x = (long long)sp0 + p1;
+  }
+}
+
+// ---- 128 heads: one barrier per step, the value product a step behind ----
+//
+// Per step i of 32 keys, after the step's one barrier: the copies of tile
+// i + 1 go out (a ring of two tile slots); the value product of tile i - 1
+// (32x32x16 fp16 tiles of 32 heads x 256 dims per wave, its weights P and
+// rescale factors left in LDS by the waves that scored those heads); the
+// score product of tile i (16 heads per wave, as above) with the
+// transposition of tile i's values; the softmax of tile i, whose P^T rows
+// and rescale factors go to LDS. The transposed values, P and the rescale
+// factors are double-buffered by step parity, so that nothing written in
+// step i is read before the next barrier. The prefix sums live in the ring
+// during setup only: a workgroup finds its first sequence by them and then
+// walks the sequences by their context lengths.
+template <int DK>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_decode_wide(MlaArgs a) {
+  using S = MlaShape<DK, 8>;
+  constexpr int H = 128, NW = 8, NT = 512, WDT = 8;
+  static_assert(S::TITEMS == NT, "one transposition item per thread");
+  static_assert((kMlaMaxSeqs + 1 + NT) * 4 <= 2 * S::TILEB, "setup arrays fit the ring");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[2 * S::TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t vt[2][MLA_DV * MLA_VT_ROW];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][H * 64];  // P^T rows (heads) of 32 fp16 keys
+  __shared__ float alpha_sh[2][H];  // per head: the rescale of the step's P
+  __shared__ float lsum_sh[H];      // per head: the segment's sum
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, q4 = lane >> 4;
+  const int NS = a.num_seqs;
+  typedef __attribute__((address_space(4))) const int cint;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  typedef __attribute__((address_space(3))) const u32x4 lds_cu32x4;
+
+  long long x, x_end;
+  int s = 0, sp0 = 0, C;
+  {
+    int* psum = reinterpret_cast<int*>(ring);
+    int* scan = psum + kMlaMaxSeqs + 1;
+    const int T = unit_prefix_sums<NT, 2>(a, psum, scan);
+    C = max(1, (T + (int)gridDim.x - 1) / (int)gridDim.x);
+    write_meta<NT>(a, psum, C);
+    x = (long long)blockIdx.x * C;
+    x_end = min<long long>((long long)(blockIdx.x + 1) * C, T);
+    if (x < x_end) {  // first sequence: last s with psum[s] <= x
+      int lo = 0, hi = NS - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (psum[mid] <= x) lo = mid;
+        else hi = mid - 1;
+      }
+      s = __builtin_amdgcn_readfirstlane(lo);
+      sp0 = __builtin_amdgcn_readfirstlane(psum[s]);
+    }
+    __syncthreads();  // the ring is free from here on
+  }
+  const int npieces = (S::PIECES - wave + NW - 1) / NW;  // uniform per wave
+  const uint32_t ring_lds = lds_addr(ring), vt_lds = lds_addr(vt), pb_lds = lds_addr(pbuf);
+  auto src_off = [&](int k, int ln) {
+    const uint32_t P = 1024u * (uint32_t)k + 16u * (uint32_t)ln;
+    const uint32_t row = P / (uint32_t)S::ROWB, pch = (P - row * (uint32_t)S::ROWB) >> 4;
+    return (row & 15u) * (uint32_t)S::ROWB + 16u * (pch ^ (uint32_t)row_swizzle<DK>((int)row));
+  };
+  const uint8_t* cache = reinterpret_cast<const uint8_t*>(a.cache);
+
+  while (x < x_end && s < NS) {
+    // pairs of sequence s, as the prefix sums count them (x lies in
+    // [sp0, sp0 + np) of the first non-empty one from s on)
+    const int cx = ((const cint*)a.context_lens)[s];
+    const int np = cx > 0 ? (((cx + 15) >> 4) + 1) >> 1 : 0;
+    if (np == 0) {
+      ++s;
+      continue;
+    }
+    const int p0 = (int)(x - sp0);
+    const int p1 = (int)(min<long long>(x_end, (long long)sp0 + np) - sp0);
+    const int n = p1 - p0;
+    const int ctx = ((const cint*)a.context_lens)[s];
+    const int nblk = (ctx + 15) >> 4;
+    const cint* bt = (const cint*)(a.block_table + (size_t)s * a.bt_stride);
+
+    // queries of this wave's 16 heads (B operand of the score product)
+    u32x4 qf[S::KS];
+    {
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.query) + ((size_t)s * H + 16 * wave + c16) * S::ROWB +
+                          16 * q4;
+#pragma unroll
+      for (int j = 0; j < S::KS; ++j) qf[j] = load16(qp + 64 * j);
+    }
+    f32x16 ow[WDT];  // dims 256 (wave / 4) + 32 t .. of heads 32 (wave % 4) ..
+#pragma unroll
+    for (int t = 0; t < WDT; ++t) ow[t] = f32x16{};
+    float m = -INFINITY, lsum = 0.f;
+
+    auto pair_blocks = [&](int i, int& b0, int& b1) {
+      const int pb = 2 * (p0 + i);
+      b0 = bt[pb];
+      b1 = bt[min(pb + 1, nblk - 1)];  // (a last odd block pairs with itself)
+    };
+    auto issue = [&](int i, int ln, int b0, int b1) {  // copies of the segment's pair i into slot i % 2
+      const uint32_t slot = ring_lds + (uint32_t)((i & 1) * S::TILEB);
+#pragma unroll
+      for (int c = 0; c < S::MAXP; ++c) {
+        if (c < npieces) {
+          const int k = wave + NW * c;
+          const int blk = k < S::PIECES / 2 ? b0 : b1;
+          dma16(cache + (size_t)(uint32_t)blk * S::BLKB, src_off(k, ln), slot + 1024u * (uint32_t)k);
+        }
+      }
+    };
+    // the queries have landed before any copy is issued (a wait the compiler
+    // placed for them later would drain the copies in flight)
+    wait_vm<0>();
+    int b0, b1;
+    pair_blocks(0, b0, b1);
+    issue(0, lane_id_here(), b0, b1);
+    if (n > 1) pair_blocks(1, b0, b1);  // (the next pair's ids, a step ahead)
+
+    for (int i = 0; i <= n; ++i) {
+      // tile i has landed (the only copies in flight); every wave is done
+      // with step i - 1
+      wait_vm<0>();
+      barrier_keep_loads();
+      const int ln = lane_id_here();  // (lane-derived values recomputed: the registers are full)
+      if (i + 1 < n) {
+        issue(i + 1, ln, b0, b1);
+        if (i + 2 < n) pair_blocks(i + 2, b0, b1);
+      }
+
+      // ---- value product of tile i - 1: lane's head 32 (wave % 4) + ln % 32,
+      // dims 256 (wave / 4) + 32 t + (ln % 32) of the A operand; k-step ks
+      // covers keys 16 ks + 8 (ln / 32) .. + 7 ----
+      if (i > 0) {
+        const int pp = (i - 1) & 1;
+        const int l32 = ln & 31, kh = ln >> 5;
+        const int head = 32 * (wave & 3) + l32;
+        const float al = alpha_sh[pp][head];
+        if (__any(al != 1.f)) {
+#pragma unroll
+          for (int t = 0; t < WDT; ++t) ow[t] *= al;
+        }
+        u32x4 pw[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          pw[ks] = *(lds_cu32x4*)(uintptr_t)(pb_lds + (uint32_t)(pp * H * 64 + head * 64 +
+                                                                 16 * ((2 * ks + kh) ^ vt_swizzle(head))));
+        const uint32_t vbase = vt_lds + (uint32_t)(pp * MLA_DV * MLA_VT_ROW);
+        const int d0 = 256 * (wave >> 2) + l32;
+        uint32_t vb[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) vb[ks] = vbase + vt_offset(d0, 2 * ks + kh);
+        constexpr int NVR = 2 * WDT, VD = 4;  // value reads (tile t, k-step ks) = read 2 t + ks
+        auto vread = [&](int r) { return lds_read16(vb[r & 1] + (uint32_t)(32 * MLA_VT_ROW * (r >> 1))); };
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 vbuf[VD];
+#pragma unroll
+        for (int r = 0; r < VD; ++r) vbuf[r] = vread(r);
+#pragma unroll
+        for (int r = 0; r < NVR; ++r) {
+          const u32x4 vf = vbuf[r % VD];
+          if (r + VD < NVR) vbuf[r % VD] = vread(r + VD);
+          ow[r >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, vf),
+                                                             __builtin_bit_cast(f16x8_t, pw[r & 1]), ow[r >> 1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, VD + 2, 0);
+#pragma unroll
+        for (int r = 0; r < NVR - VD; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, VD, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i == n) break;
+
+      // ---- score product and transposition of tile i ----
+      const int cp = i & 1;
+      const int kend = ctx - 32 * (p0 + i);  // keys of this tile at or past kend are masked
+      const uint32_t slot = ring_lds + (uint32_t)(cp * S::TILEB);
+      const uint32_t vdst = vt_lds + (uint32_t)(cp * MLA_DV * MLA_VT_ROW);
+      u32x4 th[4];  // th[t][w]: bf16, then fp16, pair (dims 2w, 2w+1) of key 4 tq + t
+      const int tq = (64 * wave + ln) & 7, tc = (64 * wave + ln) >> 3;
+      constexpr int NB = DK == 576 ? 2 : 4;  // (see the score reads above)
+      uint32_t kb[2][NB];
+      {
+        const int r16 = ln & 15, rq = ln >> 4;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const int key = 8 * (r16 >> 2) + 4 * kt + (r16 & 3);
+          const int swz = row_swizzle<DK>(key);
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            kb[kt][b] = slot + (uint32_t)(key * S::ROWB + 16 * (((b << 2) | rq) ^ swz));
+        }
+      }
+      f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      constexpr int NKR = 2 * S::KS, PD = 4;
+      auto kread = [&](int r) {
+        const int j = r >> 1, kt = r & 1;
+        return lds_read16(kb[kt][j % NB] + (uint32_t)(64 * NB * (j / NB)));
+      };
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4 kbuf[PD];
+#pragma unroll
+      for (int r = 0; r < PD; ++r) kbuf[r] = kread(r);
+#pragma unroll
+      for (int r = 0; r < NKR; ++r) {
+        const u32x4 kf = kbuf[r % PD];
+        if (r + PD < NKR) kbuf[r % PD] = kread(r + PD);
+        st[r & 1] = mfma_bf16(kf, qf[r >> 1], st[r & 1]);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int key = 4 * tq + t;
+        th[t] = lds_read16(slot + (uint32_t)(key * S::ROWB + 16 * (tc ^ row_swizzle<DK>(key))));
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
+#pragma unroll
+      for (int r = 0; r < NKR - PD; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, PD, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      const bool tail = kend < 32;  // (uniform) the context ends inside this tile
+      {  // transposed fp16 values of tile i, keys past the context zeroed
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t b = th[t][w];
+            th[t][w] = f16x2_bits(__uint_as_float(b << 16), __uint_as_float(b & 0xffff0000u));
+          }
+        }
+        if (tail) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t keep = 4 * tq + t < kend ? 0xffffffffu : 0u;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) th[t][w] &= keep;
+          }
+        }
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {  // dim 8 tc + d: keys 4 tq .. 4 tq + 3
+          const int w = d >> 1;
+          const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+          const uint32_t lo2 = __builtin_amdgcn_perm(th[1][w], th[0][w], sel);
+          const uint32_t hi2 = __builtin_amdgcn_perm(th[3][w], th[2][w], sel);
+          lds_write8(vdst + vt_offset(8 * tc + d, tq >> 1) + 8 * (tq & 1), lo2, hi2);
+        }
+      }
+
+      // ---- softmax of tile i: this lane's keys 8 q4 + 4 kt + r, head
+      // 16 wave + c16; P^T row and rescale factor to LDS ----
+      {
+        const int rq = ln >> 4, h16 = 16 * wave + (ln & 15);
+        float xv[2][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xv[kt][r] = st[kt][r] * a.scale_log2;
+        if (tail) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xv[kt][r] = (8 * rq + 4 * kt + r < kend) ? xv[kt][r] : -INFINITY;
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, xv[kt][r]);
+        tmax = strided_max<16>(tmax);  // key 0 of the tile is always valid
+        const bool up = tmax > m + 8.f;
+        const float alpha = up ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;
+        m = up ? tmax : m;
+        lsum *= alpha;
+        if (rq == 0) alpha_sh[cp][h16] = alpha;
+        // p scaled by 2^7 (at most 2^15): fp16 keeps small weights normal
+        const float mb = m - 7.f;
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(xv[e >> 2][e & 3] - mb);
+          lsum += pv[e];
+        }
+        const u32x4 pf = {f16x2_bits(pv[0], pv[1]), f16x2_bits(pv[2], pv[3]), f16x2_bits(pv[4], pv[5]),
+                          f16x2_bits(pv[6], pv[7])};
+        *(lds_u32x4*)(uintptr_t)(pb_lds + (uint32_t)(cp * H * 64 + h16 * 64 + 16 * (rq ^ vt_swizzle(h16)))) = pf;
+      }
+    }
+
+    // ---- result of the segment: the scoring waves publish each head's sum
+    // (and leave the summary's max and sum); the owners of the outputs
+    // normalise or store them ----
+    const bool single = (sp0 / C) == ((sp0 + np - 1) / C);
+    {
+      const int ln = lane_id_here();
+      const float L = strided_sum<16>(lsum);
+      if ((ln >> 4) == 0) {
+        lsum_sh[16 * wave + (ln & 15)] = L;
+        if (!single) {
+          const size_t rec = (size_t)(blockIdx.x + s) * H + 16 * wave + (ln & 15);
+          a.part_ml[rec * 2] = m - 7.f;
+          a.part_ml[rec * 2 + 1] = L;
+        }
+      }
+      barrier_keep_loads();
+      // lane: head 32 (wave % 4) + ln % 32; ow[t][4 j + r] is dim
+      // 256 (wave / 4) + 32 t + 8 j + 4 (ln / 32) + r
+      const int head = 32 * (wave & 3) + (ln & 31);
+      const int d0 = 256 * (wave >> 2) + 4 * (ln >> 5);
+      if (single) {
+        const float inv = 1.f / lsum_sh[head];
+        uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)s * H + head) * MLA_DV + d0;
+#pragma unroll
+        for (int t = 0; t < WDT; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            uint2 w;
+            w.x = pack_bf16x2(ow[t][4 * j] * inv, ow[t][4 * j + 1] * inv);
+            w.y = pack_bf16x2(ow[t][4 * j + 2] * inv, ow[t][4 * j + 3] * inv);
+            *reinterpret_cast<uint2*>(op + 32 * t + 8 * j) = w;
+          }
+      } else {
+        const size_t rec = (size_t)(blockIdx.x + s) * H + head;
+        float* op = a.part_o + rec * MLA_DV + d0;
+#pragma unroll
+        for (int t = 0; t < WDT; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<f32x4*>(op + 32 * t + 8 * j) =
+                f32x4{ow[t][4 * j], ow[t][4 * j + 1], ow[t][4 * j + 2], ow[t][4 * j + 3]};
+      }
+      barrier_keep_loads();  // the ring and the head sums are reused by the next segment
+    }
+    x = (long long)sp0 + p1;
+    if (p1 == np) {  // the sequence is done: the next segment starts the next one
+      sp0 += np;
+      ++s;
+    }
   }
 }
 
@@ -1008,6 +1238,8 @@ static hipError_t run_mla(const MlaArgs& a, int grid, hipStream_t st) {
   constexpr int NW = 8, HG = 1;
   if constexpr (H == 16)  // the waves split the keys
     hipLaunchKernelGGL((mla_decode_narrow<DK>), dim3((unsigned)grid), dim3(64 * kNarrowWaves), 0, st, a);
+  else if constexpr (H == 128)
+    hipLaunchKernelGGL((mla_decode_wide<DK>), dim3((unsigned)grid), dim3(512), 0, st, a);
   else
     hipLaunchKernelGGL((mla_decode_split<DK, H, NW, HG>), dim3((unsigned)grid), dim3(64 * NW), 0, st, a);
   hipError_t e = hipGetLastError();
