@@ -297,7 +297,7 @@ PROFILE_OF = {"fp8_decode": "decode_mfma_split_fp8_decode", "llama8b_decode": "d
               "agentic_decode_shared_prefix": "decode_mfma_split_shared_prefix_agentic_decode",
               "fp8_swa128": "decode_mfma_split_fp8_swa128", "tiny_decode": "decode_partition_kernel_tiny_decode",
               "mixed_step": "prefill_bf16_kernel_mixed_step", "sparse_decode": "decode_sparse_sparse_decode",
-              "mla_decode": "mla_decode_split_mla_decode_128h", "mla_decode_16h": "mla_decode_narrow_mla_decode_16h"}
+              "mla_decode": "mla_decode_wide_mla_decode_128h", "mla_decode_16h": "mla_decode_narrow_mla_decode_16h"}
 
 
 def kernel_source_digest(files):
@@ -594,7 +594,7 @@ def measure(name, pa, torch, W, args, flush):
         t = time_runs(torch, attend, args.runs, args.warmup, flush)
         nbytes = b.latent_bytes_read()
         flops = 2.0 * b.num_heads * (b.head_dim_k + 512) * int(b.context_lens.sum())
-        kernel = ("pa_mla_decode: mla_decode_split<576, 128, 8, 1> + mla_merge" if b.num_heads == 128 else
+        kernel = ("pa_mla_decode: mla_decode_wide<576> + mla_merge" if b.num_heads == 128 else
                   "pa_mla_decode: mla_decode_narrow<576> + mla_merge")
         res.update(timing=t, bytes_per_call=nbytes, flops_per_call=flops,
                    roofline=hbm_roofline(nbytes, t["median_ms"], name, kernel))
