@@ -454,6 +454,21 @@ int device_cu_count() {
   return n;
 }
 
+int device_lds_per_cu() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || n <= 0)
+    return 0;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 // Which decode kernel serves a request: the matrix-core kernel for bf16/fp8
 // caches (any group up to 16 query heads per KV head), the VALU kernel for
 // fp32 caches (and for every cache type when the caller asks for it:

@@ -26,6 +26,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -703,6 +704,321 @@ static hipError_t run_decode_mfma_kind(const DecodeArgs& a, int cache_kind, int 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int cache_kind, int head_size, hipStream_t st) {
   return a.num_groups > 0 ? run_decode_mfma_kind<true>(a, cache_kind, head_size, st)
                           : run_decode_mfma_kind<false>(a, cache_kind, head_size, st);
+}
+
+
+// ---------------------------------------------------------------------------
+// Decode beside a running prefill (mixed batches)
+// ---------------------------------------------------------------------------
+// In a step that mixes one-token rows with a long chunk ("从静态批处理到状态化
+// 推理集群", "Chunked prefill：在共置引擎里治理阶段干扰") the decode rows are
+// bound by HBM and the chunk by the matrix cores, so the two can share the
+// chip. The prefill kernel's workgroups hold most of a CU (8 waves of ~225
+// registers: 464 of each SIMD's 512, and ~68 KB of LDS), so a decode kernel
+// beside it must fit in the rest: one wave per SIMD of at most 48 registers
+// and one workgroup per CU of at most ~92 KB of LDS. This kernel keeps its
+// loads in flight in LDS instead of registers: each wave streams its 4 KiB
+// K and V tiles through a ring of kSideSlots tiles with direct global->LDS
+// copies (nontemporal: read once), and more than 80 KB of LDS per workgroup
+// keeps a second one off the same CU (which would leave no room there for a
+// prefill workgroup).
+//
+// Per 16-key block and KV head (G = 4 query heads, head size 128):
+//  * scores S^T = K Q^T on four 16x16x32 bf16 MFMAs; the 16 columns are the 4
+//    heads repeated, so lane 16q + i (i < 4) ends up holding head i's scores
+//    of keys 4q..4q+3;
+//  * O = P V on 4x4x4 (16-block) bf16 MFMAs: block b of output half h holds
+//    heads 0..3 x head dims 64h + 4b..4b+3, so lane l holds the 4 heads of dim
+//    64h + l (8 accumulator registers instead of the 32 a 16-column tile
+//    takes); P of key quad q is broadcast from block 4q, which is exactly
+//    where the score MFMA left it; P enters as bf16 hi + lo (two MFMAs).
+// The split plan, summary records and merge are those of decode_mfma_split
+// (wave w takes block-heads [w*C, (w+1)*C), summaries in slot w + stream).
+constexpr int kSideWaves = 4;
+constexpr int kSideSlots = 5;                                  // 4 KiB tiles per wave's ring
+constexpr int kSideRingBytes = kSideWaves * kSideSlots * 4096;
+constexpr int kSideQBytes = kSideWaves * 1024;                 // a wave's 4 query heads, bf16 [4][128]
+
+size_t decode_side_lds_bytes(int num_seqs) {
+  return (size_t)kSideRingBytes + kSideQBytes + (size_t)(num_seqs + 1 + 256) * sizeof(int);
+}
+
+typedef short side_s16x4 __attribute__((ext_vector_type(4)));
+
+// O += A B on the 16 4x4x4 blocks, A (P) taken from block 4q for all blocks.
+template <int Q>
+__device__ __forceinline__ f32x4 mfma_4x4x4_from(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
+  const side_s16x4 A = __builtin_bit_cast(side_s16x4, (u32x2){a0, a1});
+  const side_s16x4 B = __builtin_bit_cast(side_s16x4, (u32x2){b0, b1});
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(A, B, c, 4, 4 * Q, 0);
+}
+
+// 16-byte global -> LDS copy per lane (lane i lands at lds_base + 16 i),
+// nontemporal; inline assembly for the reasons given at the prefill kernel's
+// copies. M0 is restored.
+__device__ __forceinline__ void side_copy(const void* base, uint32_t lane_offset, uint32_t lds_base) {
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(lane_offset), "s"(base), "s"(lds_base)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void side_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// LDS reads of a slot are complete before a copy overwrites it.
+__device__ __forceinline__ void side_wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void decode_side(DecodeArgs a) {
+  static_assert(D == 128, "head size 128");
+  constexpr int G = 4, NS = kSideSlots;
+  constexpr uint32_t TILE = 16 * D * 2;
+  extern __shared__ __attribute__((aligned(16))) int side_lds[];
+  uint8_t* ring = reinterpret_cast<uint8_t*>(side_lds);
+  uint8_t* qslots = ring + kSideRingBytes;
+  int* psum = reinterpret_cast<int*>(qslots + kSideQBytes);
+  int* scan = psum + a.num_seqs + 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = a.num_kv_heads, NSEQ = a.num_seqs;
+
+  const int per_head = lds_exclusive_scan(
+      NSEQ, [&](int i) { int qr, cx, l0; return seq_blocks(a, i, qr, cx, l0); }, psum, scan);
+  const long long T = (long long)per_head * H;
+  const int C = split_chunk((int)min<long long>(T, 0x7fffffff), gridDim.x * kSideWaves);
+  if (blockIdx.x == 0) {  // for the merge kernel
+    if (tid == 0) a.meta[0] = C;
+    for (int i = tid; i <= NSEQ; i += 256) a.meta[1 + i] = psum[i];
+  }
+
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const uint32_t ring_lds =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)ring) + wave * NS * TILE;
+  const uint32_t q_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)qslots) + wave * 1024;
+  const uint8_t* ring_w = ring + wave * NS * TILE;
+  const uint8_t* q_w = qslots + wave * 1024;
+  // per-lane global offsets of the copies: K copy c brings (key l%16, chunk
+  // 4c + l/16) to byte 1024c + 16l of the slot, where lane l's score operand
+  // of k-step c is read; V copy 2h + c brings (row 64h + l, chunk c)
+  const uint32_t koff = (uint32_t)((lane & 15) * 256 + 16 * (lane >> 4));
+  const uint32_t voff = (uint32_t)(32 * lane);
+  typedef __attribute__((address_space(4))) const int cint;
+
+  const int w = blockIdx.x * kSideWaves + wave;
+  const long long x_end = min<long long>((long long)(w + 1) * C, T);
+  const size_t head_stride = (size_t)H * TILE;
+  long long x = (long long)w * C;
+  while (x < x_end) {
+    const int i = __builtin_amdgcn_readfirstlane(last_le(psum, NSEQ, x, H));
+    const int nb = __builtin_amdgcn_readfirstlane(psum[i + 1] - psum[i]);
+    const long long base = (long long)__builtin_amdgcn_readfirstlane(psum[i]) * H;
+    const int g = (int)((x - base) / nb);
+    const long long sstart = base + (long long)g * nb;
+    const long long seg_end = min(x_end, sstart + nb);
+    const int slot = w + i * H + g;
+    int qrow, ctx, lo;
+    seq_blocks(a, i, qrow, ctx, lo);
+    qrow = __builtin_amdgcn_readfirstlane(qrow);  // uniform: scalar copy bases
+    ctx = __builtin_amdgcn_readfirstlane(ctx);
+    lo = __builtin_amdgcn_readfirstlane(lo);
+    const int blk0 = (lo >> 4) + (int)(x - sstart);
+    const int nblk = (int)(seg_end - x);
+    const int kend = min(ctx, (blk0 + nblk) * 16);
+    const cint* bt = (const cint*)(a.block_table + (size_t)i * a.bt_stride);
+    const uint8_t* kcache = reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)g * TILE;
+    const uint8_t* vcache = reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * TILE;
+
+    // the 4 query heads (contiguous, 1 KiB) to LDS, then the first tiles
+    side_wait_lds();
+    side_copy(reinterpret_cast<const uint8_t*>(a.query) + ((size_t)qrow * a.num_heads + g * G) * D * 2,
+              16u * lane, q_lds);
+    const int ntile = 2 * nblk;  // tile u: block blk0 + u/2, K if u is even, else V
+    auto issue = [&](int u) {
+      const uint8_t* src = ((u & 1) ? vcache : kcache) + (size_t)(uint32_t)bt[blk0 + (u >> 1)] * head_stride;
+      const uint32_t dst = ring_lds + (uint32_t)(u % NS) * TILE;
+      if (u & 1) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) side_copy(src + 2048 * (c >> 1) + 16 * (c & 1), voff, dst + 1024 * c);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) side_copy(src + 64 * c, koff, dst + 1024 * c);
+      }
+    };
+    for (int u = 0; u < NS - 1 && u < ntile; ++u) issue(u);
+    // tile u is in LDS once at most 4 * (NS - 1) copies issued after it are
+    // outstanding; tile u + NS - 1 reuses the slot of tile u - 1
+    auto next = [&](int u) {
+      side_wait_lds();
+      if (u + NS - 1 < ntile) {
+        issue(u + NS - 1);
+        side_wait_vm<4 * (NS - 1)>();
+      } else {
+        side_wait_vm<0>();
+      }
+    };
+
+    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.f;
+    for (int n = 0; n < nblk; ++n) {
+      const int b = blk0 + n;
+      // ---- scores of block b ----
+      next(2 * n);
+      const uint8_t* ks = ring_w + ((2 * n) % NS) * TILE;
+      f32x4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + 1024 * j + 16 * lane);
+        const u32x4 qf = *reinterpret_cast<const u32x4*>(q_w + (lane & 3) * 256 + 64 * j + 16 * (lane >> 4));
+        st = mfma_bf16_16x16x32(kf, qf, st);
+      }
+      // lane's keys: b*16 + 4*(lane/16) + r, head lane % 4
+      const bool edge = b * 16 < lo || b * 16 + 16 > kend;
+      float xs[4], lmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = st[r] * a.scale_log2;
+        if (edge) {
+          const int kp = b * 16 + 4 * (lane >> 4) + r;
+          v = (kp >= lo && kp < kend) ? v : -INFINITY;
+        }
+        xs[r] = v;
+        lmax = fmaxf(lmax, v);
+      }
+      // lazy rescaling as in pair_step: the max moves only when a block's
+      // exceeds it by more than 2^8. The block's max over the four lane
+      // groups of a head is taken only when some lane's own scores do (a
+      // wave vote decides: the same outcome, without two cross-lane
+      // exchanges through LDS on most blocks)
+      if (__any(lmax > m + 8.f)) {
+        const float tmax = strided_max<16>(lmax);
+        const bool up = tmax > m + 8.f;
+        const float alpha = up ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;
+        m = up ? tmax : m;
+        lsum *= alpha;
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {  // lane hh holds head hh's factor
+          const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), hh));
+          o0[hh] *= ah;
+          o1[hh] *= ah;
+        }
+      }
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(xs[r] - m);
+        lsum += p[r];
+      }
+      const uint32_t h0 = pack_bf16x2(p[0], p[1]), h1 = pack_bf16x2(p[2], p[3]);
+      const uint32_t l0 = pack_bf16x2(p[0] - bf16_lo(h0), p[1] - bf16_hi(h0));
+      const uint32_t l1 = pack_bf16x2(p[2] - bf16_lo(h1), p[3] - bf16_hi(h1));
+
+      // ---- O += P V of block b ----
+      next(2 * n + 1);
+      const uint8_t* vs = ring_w + ((2 * n + 1) % NS) * TILE;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        u32x4 v0 = *reinterpret_cast<const u32x4*>(vs + 1024 * c + 16 * lane);        // dim lane, keys 8c..8c+7
+        u32x4 v1 = *reinterpret_cast<const u32x4*>(vs + 1024 * (2 + c) + 16 * lane);  // dim 64 + lane
+        if (b * 16 + 16 > kend) {  // keys past the context may hold anything: zero them
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int k0 = b * 16 + 8 * c + 2 * t;
+            const uint32_t msk = (k0 < kend ? 0x0000ffffu : 0u) | (k0 + 1 < kend ? 0xffff0000u : 0u);
+            v0[t] &= msk;
+            v1[t] &= msk;
+          }
+        }
+        if (c == 0) {
+          o0 = mfma_4x4x4_from<0>(h0, h1, v0[0], v0[1], o0);
+          o0 = mfma_4x4x4_from<0>(l0, l1, v0[0], v0[1], o0);
+          o1 = mfma_4x4x4_from<0>(h0, h1, v1[0], v1[1], o1);
+          o1 = mfma_4x4x4_from<0>(l0, l1, v1[0], v1[1], o1);
+          o0 = mfma_4x4x4_from<1>(h0, h1, v0[2], v0[3], o0);
+          o0 = mfma_4x4x4_from<1>(l0, l1, v0[2], v0[3], o0);
+          o1 = mfma_4x4x4_from<1>(h0, h1, v1[2], v1[3], o1);
+          o1 = mfma_4x4x4_from<1>(l0, l1, v1[2], v1[3], o1);
+        } else {
+          o0 = mfma_4x4x4_from<2>(h0, h1, v0[0], v0[1], o0);
+          o0 = mfma_4x4x4_from<2>(l0, l1, v0[0], v0[1], o0);
+          o1 = mfma_4x4x4_from<2>(h0, h1, v1[0], v1[1], o1);
+          o1 = mfma_4x4x4_from<2>(l0, l1, v1[0], v1[1], o1);
+          o0 = mfma_4x4x4_from<3>(h0, h1, v0[2], v0[3], o0);
+          o0 = mfma_4x4x4_from<3>(l0, l1, v0[2], v0[3], o0);
+          o1 = mfma_4x4x4_from<3>(h0, h1, v1[2], v1[3], o1);
+          o1 = mfma_4x4x4_from<3>(l0, l1, v1[2], v1[3], o1);
+        }
+      }
+    }
+
+    // ---- the segment's result: lane hh (< 4) holds head hh's max and sum ----
+    const float L = strided_sum<16>(lsum);
+    const bool single = (sstart / C) == ((sstart + nb - 1) / C);
+    float mh[4], Lh[4];
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      mh[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), hh));
+      Lh[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(L), hh));
+    }
+    if (single) {
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * a.num_heads + g * G) * D + lane;
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        const float inv = Lh[hh] > 0.f ? 1.f / Lh[hh] : 0.f;
+        op[hh * D] = f32_to_bf16(o0[hh] * inv);
+        op[hh * D + 64] = f32_to_bf16(o1[hh] * inv);
+      }
+      if (a.lse != nullptr && lane < 4)
+        a.lse[(size_t)qrow * a.num_heads + g * G + lane] = (m + log2f(L)) * kLn2;
+    } else {
+      const size_t rec = (size_t)slot * a.rec_cols;
+      float* op = a.part_o + rec * D + lane;
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        op[hh * D] = o0[hh];
+        op[hh * D + 64] = o1[hh];
+      }
+      if (lane < 4) {
+        a.part_ml[(rec + lane) * 2] = m;
+        a.part_ml[(rec + lane) * 2 + 1] = L;
+      }
+    }
+    (void)mh;
+    x = seg_end;
+  }
+}
+
+bool decode_side_supported(int q_kind, int cache_kind, int head_size, int group) {
+  return q_kind == KBF16 && cache_kind == KBF16 && head_size == 128 && group == 4;
+}
+
+// The side kernel (one workgroup per CU) and the merge, on `st`. The
+// workspace is the split plan's (a.split_waves >= the side kernel's waves).
+hipError_t launch_decode_side(const DecodeArgs& a, hipStream_t st) {
+  const int grid = device_cu_count();
+  if (a.split_waves < grid * kSideWaves || a.one_per_stream) return hipErrorInvalidValue;
+  const size_t lds = decode_side_lds_bytes(a.num_seqs);
+  static std::atomic<size_t> lds_set{0};
+  if (lds_set.load(std::memory_order_relaxed) < lds) {
+    hipError_t e = hipFuncSetAttribute((const void*)decode_side<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    lds_set.store(lds, std::memory_order_relaxed);
+  }
+  hipLaunchKernelGGL((decode_side<128>), dim3(grid), dim3(256), lds, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int waves = a.num_seqs * a.num_heads;
+  hipLaunchKernelGGL((decode_split_merge<128, false>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace pa

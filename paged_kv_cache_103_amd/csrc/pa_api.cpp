@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "pa_internal.h"
@@ -34,6 +35,41 @@ pa_status hip_status(hipError_t e, const char* what) {
     return PA_OK;
   }
   return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// A second stream per device for work that runs beside the caller's stream
+// (the one-token rows of a mixed batch beside its chunks), with the events
+// that fork it from and join it back to the caller's stream. Created on
+// first use at the default priority; guarded, with the enqueue sequence
+// that uses it, by g_side_mu.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+hipError_t side_stream_of_current_device(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  SideStream& ss = g_side[dev];
+  if (ss.stream == nullptr) {
+    SideStream n;
+    e = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (n.join) (void)hipEventDestroy(n.join);
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.stream) (void)hipStreamDestroy(n.stream);
+      return e;
+    }
+    ss = n;
+  }
+  *out = &ss;
+  return hipSuccess;
 }
 
 bool known_dtype(pa_dtype d) { return d == PA_F32 || d == PA_BF16 || d == PA_FP8_E4M3; }
@@ -642,12 +678,9 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
   d.num_kv_heads = num_kv_heads;
   d.window = sliding_window;
   d.scale_log2 = scale_log2;
-  if (any_single) {
-    hipError_t e = pa::launch_decode(d, (int)q_dtype, (int)cache_dtype, head_size, hs);
-    if (e != hipSuccess) return hip_status(e, "decode launch (one-token rows)");
-  }
+
+  pa::PrefillArgs p{};
   if (has_chunks) {
-    pa::PrefillArgs p{};
     p.out = out;
     p.query = query;
     p.k_cache = k_cache;
@@ -669,6 +702,46 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
     const long long bound_a = long_seqs + (num_q_tokens + tq - 1) / tq;
     const long long bound_b = long_seqs * ((max_q_len + tq - 1) / tq);
     p.num_tiles = (int)std::min(bound_a, bound_b);
+  }
+
+  // A mixed batch: the chunks bound by the matrix cores, the one-token rows
+  // by HBM ("从静态批处理到状态化推理集群", "Chunked prefill：在共置引擎里
+  // 治理阶段干扰"). Where the shapes allow, the rows run on a second stream
+  // beside the prefill kernel, one decode workgroup per CU next to each
+  // prefill workgroup (both only read the cache and they write disjoint
+  // rows of out); the caller's stream waits for both.
+  bool beside = false;
+  if (any_single && has_chunks && plan.split_waves > 0 && !plan.one_per_stream &&
+      pa::decode_side_supported((int)q_dtype, (int)cache_dtype, head_size, group)) {
+    const size_t side = pa::decode_side_lds_bytes(num_seqs);
+    const size_t pf = pa::prefill_lds_bytes((int)cache_dtype, head_size, group);
+    const size_t cap = (size_t)pa::device_lds_per_cu();
+    // more than half of a CU's LDS keeps a second decode workgroup off it
+    beside = pf > 0 && 2 * side > cap && side + pf + 2048 <= cap &&
+             plan.split_waves >= 4 * pa::device_cu_count();
+  }
+  if (beside) {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* ss = nullptr;
+    hipError_t e = side_stream_of_current_device(&ss);
+    if (e == hipSuccess) e = hipEventRecord(ss->fork, hs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
+    if (e != hipSuccess) return hip_status(e, "side stream fork");
+    e = pa::launch_prefill(p, (int)cache_dtype, head_size, hs);
+    if (e != hipSuccess) return hip_status(e, "prefill launch");
+    const hipError_t ed = pa::launch_decode_side(d, ss->stream);
+    e = hipEventRecord(ss->join, ss->stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(hs, ss->join, 0);
+    if (ed != hipSuccess) return hip_status(ed, "decode launch (one-token rows)");
+    if (e != hipSuccess) return hip_status(e, "side stream join");
+    g_last_error.clear();
+    return PA_OK;
+  }
+  if (any_single) {
+    hipError_t e = pa::launch_decode(d, (int)q_dtype, (int)cache_dtype, head_size, hs);
+    if (e != hipSuccess) return hip_status(e, "decode launch (one-token rows)");
+  }
+  if (has_chunks) {
     hipError_t e = pa::launch_prefill(p, (int)cache_dtype, head_size, hs);
     if (e != hipSuccess) return hip_status(e, "prefill launch");
   }

@@ -59,6 +59,8 @@ constexpr int kSharedPrefixMaxSeqs = 3000;
 int shared_prefix_meta_ints(int num_seqs, int num_groups);
 bool decode_uses_mfma(int q_kind, int cache_kind, int group);
 int device_cu_count();
+// LDS bytes one CU offers (shared by its resident workgroups).
+int device_lds_per_cu();
 
 struct DecodeArgs {
   void* out;
@@ -176,5 +178,15 @@ struct PrefillArgs {
 int prefill_tokens_per_tile(int group);
 bool prefill_supported(int q_kind, int cache_kind, int head_size, int group);
 hipError_t launch_prefill(const PrefillArgs& args, int cache_kind, int head_size, hipStream_t stream);
+// Static LDS bytes of one prefill workgroup (0 if unknown).
+size_t prefill_lds_bytes(int cache_kind, int head_size, int group);
+
+// Decode of a mixed batch's one-token rows beside the prefill kernel
+// (decode_mfma.hip): one workgroup of four waves per CU, at most 64
+// registers per wave, K/V streamed through LDS. Uses the split plan's
+// workspace and merge; LDS bytes per workgroup for num_seqs sequences.
+bool decode_side_supported(int q_kind, int cache_kind, int head_size, int group);
+size_t decode_side_lds_bytes(int num_seqs);
+hipError_t launch_decode_side(const DecodeArgs& args, hipStream_t stream);
 
 }  // namespace pa

@@ -187,7 +187,12 @@ constexpr int PF_NW = 8;             // waves per workgroup
 constexpr int PF_NT = 64 * PF_NW;    // threads per workgroup
 
 template <int D, int G, int CK>
-__global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(PrefillArgs a) {
+// Register budget: at most 224 per wave (the attribute's count is doubled on
+// this target, whose VGPR file holds the accumulation registers too), so
+// that two waves per SIMD leave 64 of the 512 to a decode wave running beside
+// them (decode_side).
+__global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2), amdgpu_num_vgpr(112))) void
+prefill_bf16_kernel(PrefillArgs a) {
   using S = PfShape<D>;
   constexpr int NW = PF_NW, NT = PF_NT;
   constexpr int TQ = 32 * NW / G;
@@ -629,9 +634,15 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
     const float L = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     const float inv = 1.f / L;
-    if (tok < ntok) {
+    // the lane's column again, from a fresh lane id: the compiler would
+    // otherwise keep the query row offset live across the whole loop
+    int le;
+    __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(le));
+    const int col_e = wave * 32 + (le & 31);
+    const int tok_e = col_e / G, head_e = col_e % G;
+    if (tok_e < ntok) {
       uint16_t* op = reinterpret_cast<uint16_t*>(a.out) +
-                     ((size_t)(q0 + tok0 + tok) * a.num_heads + g * G + head) * D + 4 * h;
+                     ((size_t)(q0 + tok0 + tok_e) * a.num_heads + g * G + head_e) * D + 4 * (le >> 5);
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
@@ -671,6 +682,20 @@ bool prefill_supported(int q_kind, int cache_kind, int head_size, int group) {
   if (head_size != 64 && head_size != 128) return false;
   if (!(group == 1 || group == 2 || group == 4 || group == 8 || group == 16)) return false;
   return q_kind == KBF16 && (cache_kind == KBF16 || cache_kind == KFP8);
+}
+
+size_t prefill_lds_bytes(int cache_kind, int head_size, int group) {
+  const void* f = nullptr;
+#define PA_PF_CASE(D, GG, CK) \
+  if (head_size == D && group == GG && cache_kind == CK) f = (const void*)prefill_bf16_kernel<D, GG, CK>;
+#define PA_PF_GROUPS(D, CK) PA_PF_CASE(D, 1, CK) PA_PF_CASE(D, 2, CK) PA_PF_CASE(D, 4, CK) PA_PF_CASE(D, 8, CK) PA_PF_CASE(D, 16, CK)
+  PA_PF_GROUPS(64, KBF16) PA_PF_GROUPS(128, KBF16) PA_PF_GROUPS(64, KFP8) PA_PF_GROUPS(128, KFP8)
+#undef PA_PF_GROUPS
+#undef PA_PF_CASE
+  if (f == nullptr) return 0;
+  hipFuncAttributes at;
+  if (hipFuncGetAttributes(&at, f) != hipSuccess) return 0;
+  return at.sharedSizeBytes;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int cache_kind, int head_size, hipStream_t stream) {
