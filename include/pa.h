@@ -359,6 +359,17 @@ size_t pa_mla_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads);
  *   again with the values in bf16 (exact) against the weights split into
  *   bf16 hi + lo, so every finite cached value is in the domain; the fp32
  *   accumulator needs 2^15 * sum_j |v_j| below 3.4e38.
+ * Streams: a batch holding both one-token rows and longer chunks, with bf16
+ *   queries and cache, head_size 128 and 4 query heads per KV head (and a
+ *   context long enough that the decode plan splits streams over waves),
+ *   has its one-token rows decoded on a second stream that the library owns
+ *   (one per device, default priority), next to the chunks' prefill kernel
+ *   on `stream` ("从静态批处理到状态化推理集群", "Chunked prefill：在共置引擎
+ *   里治理阶段干扰": decode rows and prefill chunks share a step). The second
+ *   stream starts after the work already on `stream` and `stream` waits for
+ *   it (events), so the call is ordered exactly like one on `stream` alone,
+ *   also under HIP graph capture of `stream`. Calls that overlap in time
+ *   from several host threads serialise their enqueueing on a lock.
  */
 pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, const void* v_cache,
                            const float* k_scale, const float* v_scale, const int32_t* block_table,
