@@ -56,7 +56,8 @@ WORKLOADS = {
     "fp8_swa128": "the fp8_decode batch with a 128-token sliding window (the last 8-9 blocks per sequence)",
     "tiny_decode": "4 sequences, contexts {17,40,64,100}, 8/2 heads, head 64, fp32; pa_decode",
     "mixed_step": "192 decode rows (context U{4096..32768}) + one 2048-token chunk on a 65536-token prefix, "
-                  "32/8 heads, head 128, bf16; step = KV write of the 2240 new tokens + pa_prefill_chunk",
+                  "32/8 heads, head 128, bf16; step = KV write of the 2240 new tokens + pa_prefill_chunk "
+                  "(the decode rows on a second stream beside the chunk)",
     "sparse_decode": "64 sequences, context U{32768..524288}, 128 chosen blocks + the newest each, 32/8 heads, "
                      "head 128, bf16; pa_decode_sparse",
     "mla_decode": "64 sequences, context U{4096..32768}, 128 heads sharing one latent row per token (512 + 64, "
@@ -548,7 +549,9 @@ def measure(name, pa, torch, W, args, flush):
         # overlapped (max of them), at the published peaks
         t_hbm = dbytes / (HBM_PEAK_GBS * 1e9) * 1e3
         t_mfma = flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) * 1e3
-        res["roofline"] = {"bound": "hbm+mfma", "kernel": "pa_prefill_chunk step (write, decode rows, chunk)",
+        res["roofline"] = {"bound": "hbm+mfma",
+                           "kernel": "pa_prefill_chunk step: write, then prefill_bf16_kernel beside decode_side + "
+                                     "decode_split_merge (two streams)",
                            "achieved_ms": t["median_ms"], "roofline_ms_serial": round(t_hbm + t_mfma, 4),
                            "roofline_ms_overlapped": round(max(t_hbm, t_mfma), 4),
                            "frac_serial": round((t_hbm + t_mfma) / t["median_ms"], 4),
