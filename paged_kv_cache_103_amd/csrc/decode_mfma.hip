@@ -713,10 +713,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int cache_kind, int head_size
 // In a step that mixes one-token rows with a long chunk ("从静态批处理到状态化
 // 推理集群", "Chunked prefill：在共置引擎里治理阶段干扰") the decode rows are
 // bound by HBM and the chunk by the matrix cores, so the two can share the
-// chip. The prefill kernel's workgroups hold most of a CU (8 waves of ~225
-// registers: 464 of each SIMD's 512, and ~68 KB of LDS), so a decode kernel
-// beside it must fit in the rest: one wave per SIMD of at most 48 registers
-// and one workgroup per CU of at most ~92 KB of LDS. This kernel keeps its
+// chip. The prefill kernel's workgroups hold most of a CU (8 waves of at
+// most 224 registers: 448 of each SIMD's 512, and ~68 KB of LDS), so a
+// decode kernel beside it must fit in the rest: one wave per SIMD of at most
+// 64 registers and one workgroup per CU of at most ~92 KB of LDS. This kernel keeps its
 // loads in flight in LDS instead of registers: each wave streams its 4 KiB
 // K and V tiles through a ring of kSideSlots tiles with direct global->LDS
 // copies (nontemporal: read once), and more than 80 KB of LDS per workgroup
@@ -753,31 +753,9 @@ __device__ __forceinline__ f32x4 mfma_4x4x4_from(uint32_t a0, uint32_t a1, uint3
   return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(A, B, c, 4, 4 * Q, 0);
 }
 
-// 16-byte global -> LDS copy per lane (lane i lands at lds_base + 16 i),
-// nontemporal; inline assembly for the reasons given at the prefill kernel's
-// copies. M0 is restored.
-__device__ __forceinline__ void side_copy(const void* base, uint32_t lane_offset, uint32_t lds_base) {
-  uint32_t saved;
-  __asm__ volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2 nt\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(lane_offset), "s"(base), "s"(lds_base)
-      : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void side_wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// LDS reads of a slot are complete before a copy overwrites it.
-__device__ __forceinline__ void side_wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 template <int D>
+// (amdgpu_num_vgpr counts half the registers on this target: 32 -> 64)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void decode_side(DecodeArgs a) {
   static_assert(D == 128, "head size 128");
   constexpr int G = 4, NS = kSideSlots;
@@ -838,8 +816,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
     const uint8_t* vcache = reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * TILE;
 
     // the 4 query heads (contiguous, 1 KiB) to LDS, then the first tiles
-    side_wait_lds();
-    side_copy(reinterpret_cast<const uint8_t*>(a.query) + ((size_t)qrow * a.num_heads + g * G) * D * 2,
+    wait_lgkmcnt0();
+    copy16_to_lds<true>(reinterpret_cast<const uint8_t*>(a.query) + ((size_t)qrow * a.num_heads + g * G) * D * 2,
               16u * lane, q_lds);
     const int ntile = 2 * nblk;  // tile u: block blk0 + u/2, K if u is even, else V
     auto issue = [&](int u) {
@@ -847,22 +825,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
       const uint32_t dst = ring_lds + (uint32_t)(u % NS) * TILE;
       if (u & 1) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) side_copy(src + 2048 * (c >> 1) + 16 * (c & 1), voff, dst + 1024 * c);
+        for (int c = 0; c < 4; ++c) copy16_to_lds<true>(src + 2048 * (c >> 1) + 16 * (c & 1), voff, dst + 1024 * c);
       } else {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) side_copy(src + 64 * c, koff, dst + 1024 * c);
+        for (int c = 0; c < 4; ++c) copy16_to_lds<true>(src + 64 * c, koff, dst + 1024 * c);
       }
     };
     for (int u = 0; u < NS - 1 && u < ntile; ++u) issue(u);
     // tile u is in LDS once at most 4 * (NS - 1) copies issued after it are
     // outstanding; tile u + NS - 1 reuses the slot of tile u - 1
     auto next = [&](int u) {
-      side_wait_lds();
+      wait_lgkmcnt0();
       if (u + NS - 1 < ntile) {
         issue(u + NS - 1);
-        side_wait_vm<4 * (NS - 1)>();
+        wait_vmcnt<4 * (NS - 1)>();
       } else {
-        side_wait_vm<0>();
+        wait_vmcnt<0>();
       }
     };
 

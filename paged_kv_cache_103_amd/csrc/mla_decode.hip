@@ -82,56 +82,8 @@ __device__ __forceinline__ int row_swizzle(int key) {
   else return (key & 3) | (((key >> 3) & 3) << 2);                              // rows of 64 chunks
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
-__device__ __forceinline__ void barrier_keep_loads() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
 
-// 16-byte global -> LDS copy per lane (lane i lands at lds_base + 16 i); see
-// the prefill kernel for why this is inline assembly. M0 is restored.
-__device__ __forceinline__ void dma16(const void* base, uint32_t lane_offset, uint32_t lds_base) {
-  uint32_t saved;
-  __asm__ volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(lane_offset), "s"(base), "s"(lds_base)
-      : "memory");
-}
-
-// The lane id, recomputed where it is used: the compiler cannot hoist a
-// volatile asm out of the loop, so values derived from it are rematerialised
-// instead of being kept live (or spilled, and a spill reload waits for every
-// copy in flight).
-__device__ __forceinline__ int lane_id_here() {
-  int l;
-  __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-  return l;
-}
-
-template <typename T>
-__device__ __forceinline__ uint32_t lds_addr(const T* p) {
-  typedef __attribute__((address_space(3))) const T lds_t;
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_t*)p);
-}
-__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
-  typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-  return *(const lds_u32x4*)(uintptr_t)addr;
-}
-__device__ __forceinline__ void lds_write8(uint32_t addr, uint32_t lo, uint32_t hi) {
-  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-  *(lds_u32x2*)(uintptr_t)addr = u32x2{lo, hi};
-}
 
 }  // namespace
 
@@ -285,14 +237,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
         if (c < npieces) {
           const int k = wave + NW * c;
           const int blk = k < S::PIECES / 2 ? b0 : b1;
-          dma16(cache + (size_t)(uint32_t)blk * S::BLKB, src_off(k, ln), slot + 1024u * (uint32_t)k);
+          copy16_to_lds(cache + (size_t)(uint32_t)blk * S::BLKB, src_off(k, ln), slot + 1024u * (uint32_t)k);
         }
       }
     };
     // the queries have landed before any copy is issued: the compiler cannot
     // count the copies, and a wait it placed for the queries inside the loop
     // would drain every copy in flight each step
-    wait_vm<0>();
+    wait_vmcnt<0>();
     int b0, b1;
     pair_blocks(0, b0, b1);
     issue(0, H >= 128 ? lane_id_here() : lane, b0, b1);
@@ -306,10 +258,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     for (int i = 0; i < n; ++i) {
       // the copies of pair i have landed (those of pair i + 1 may be in flight)
       if (i + 1 < n) {
-        if (npieces == S::MAXP) wait_vm<S::MAXP>();
-        else wait_vm<S::MAXP - 1>();
+        if (npieces == S::MAXP) wait_vmcnt<S::MAXP>();
+        else wait_vmcnt<S::MAXP - 1>();
       } else {
-        wait_vm<0>();
+        wait_vmcnt<0>();
       }
       barrier_keep_loads();  // every wave is done with pair i - 1
       // with 128 heads the registers are full: lane-derived addresses are
@@ -621,13 +573,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (c < npieces) {
           const int k = wave + NW * c;
           const int blk = k < S::PIECES / 2 ? b0 : b1;
-          dma16(cache + (size_t)(uint32_t)blk * S::BLKB, src_off(k, ln), slot + 1024u * (uint32_t)k);
+          copy16_to_lds(cache + (size_t)(uint32_t)blk * S::BLKB, src_off(k, ln), slot + 1024u * (uint32_t)k);
         }
       }
     };
     // the queries have landed before any copy is issued (a wait the compiler
     // placed for them later would drain the copies in flight)
-    wait_vm<0>();
+    wait_vmcnt<0>();
     int b0, b1;
     pair_blocks(0, b0, b1);
     issue(0, lane_id_here(), b0, b1);
@@ -636,7 +588,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i <= n; ++i) {
       // tile i has landed (the only copies in flight); every wave is done
       // with step i - 1
-      wait_vm<0>();
+      wait_vmcnt<0>();
       barrier_keep_loads();
       const int ln = lane_id_here();  // (lane-derived values recomputed: the registers are full)
       if (i + 1 < n) {
@@ -907,13 +859,13 @@ constexpr int kNarrowSlots = 8 / MLA_NARROW_WAVES;      // ring slots per wave (
 template <int COPIES, int NSL>
 __device__ __forceinline__ void wait_blocks(int ahead) {
   if constexpr (NSL >= 4) {
-    if (ahead >= 3) { wait_vm<3 * COPIES>(); return; }
+    if (ahead >= 3) { wait_vmcnt<3 * COPIES>(); return; }
   }
   if constexpr (NSL >= 3) {
-    if (ahead >= 2) { wait_vm<2 * COPIES>(); return; }
+    if (ahead >= 2) { wait_vmcnt<2 * COPIES>(); return; }
   }
-  if (ahead >= 1) { wait_vm<COPIES>(); return; }
-  wait_vm<0>();
+  if (ahead >= 1) { wait_vmcnt<COPIES>(); return; }
+  wait_vmcnt<0>();
 }
 
 template <int DK>
@@ -999,11 +951,11 @@ __global__ __launch_bounds__(64 * kNarrowWaves) __attribute__((amdgpu_waves_per_
       const uint8_t* base = cache + (size_t)(uint32_t)bt[b0 + i] * S::BLKB;
       const uint32_t slot = ring_lds + (uint32_t)((i & (NSL - 1)) * S::BLKB);
 #pragma unroll
-      for (int k = 0; k < S::COPIES; ++k) dma16(base, src[k], slot + 1024u * (uint32_t)k);
+      for (int k = 0; k < S::COPIES; ++k) copy16_to_lds(base, src[k], slot + 1024u * (uint32_t)k);
     };
     // the queries have landed before any copy is issued (a wait the compiler
     // placed for them later would drain the copies in flight)
-    wait_vm<0>();
+    wait_vmcnt<0>();
 #pragma unroll
     for (int j = 0; j < NSL - 1; ++j)
       if (j < n) issue(j);

@@ -136,4 +136,102 @@ __device__ __forceinline__ u32x2 load8_stream(const void* p) {
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// ---- LDS staging: direct global -> LDS copies and the waits around them ----
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding):
+// at most N of this wave's vector memory operations (loads and global -> LDS
+// copies, in issue order) still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// s_waitcnt lgkmcnt(0) alone: this wave's LDS (and scalar) operations done.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// Workgroup barrier that does not wait for this wave's outstanding memory
+// operations (copies of later steps stay in flight across it).
+__device__ __forceinline__ void barrier_keep_loads() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// A 16-byte global -> LDS copy per lane, from base + lane_offset (base
+// uniform): lane i's chunk lands at byte lds_base + 16 i. Written as inline
+// assembly so that the compiler does not see an LDS store: it would
+// otherwise drain every outstanding copy before each LDS read of a loop.
+// Completion is tracked by the vector-memory counter (wait_vmcnt); other
+// waves see the data after a barrier. M0 holds the LDS base of a copy (read
+// when the copy issues) and is restored afterwards; a copy must not directly
+// follow a write of M0. NT: nontemporal (data read once).
+template <bool NT = false>
+__device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t lane_offset, uint32_t lds_base) {
+  uint32_t saved;
+  if constexpr (NT) {
+    __asm__ volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(lane_offset), "s"(base), "s"(lds_base)
+        : "memory");
+  } else {
+    __asm__ volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(lane_offset), "s"(base), "s"(lds_base)
+        : "memory");
+  }
+}
+
+// Two such copies (a K and a V chunk, each from its own base) in one block.
+__device__ __forceinline__ void copy16x2_to_lds(const void* base0, uint32_t off0, uint32_t lds0, const void* base1,
+                                                uint32_t off1, uint32_t lds1) {
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %4\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off0), "s"(base0), "v"(off1), "s"(base1), "s"(lds0), "s"(lds1)
+      : "memory");
+}
+
+// The lane id, recomputed where it is used: the compiler cannot hoist a
+// volatile asm, so values derived from it are rematerialised instead of
+// being kept live across a loop (or spilled, and a spill reload waits for
+// every copy in flight).
+__device__ __forceinline__ int lane_id_here() {
+  int l;
+  __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// LDS byte address of a __shared__ object (uniform), and raw LDS accesses by
+// address.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  typedef __attribute__((address_space(3))) const T lds_t;
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_t*)p);
+}
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+  typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+  return *(const lds_u32x4*)(uintptr_t)addr;
+}
+__device__ __forceinline__ void lds_write8(uint32_t addr, uint32_t lo, uint32_t hi) {
+  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+  *(lds_u32x2*)(uintptr_t)addr = u32x2{lo, hi};
+}
+
 }  // namespace pa

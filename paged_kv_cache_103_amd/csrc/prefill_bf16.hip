@@ -124,65 +124,6 @@ __device__ __forceinline__ int step_key_of_row(int m) {
   return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// A 16-byte global -> LDS copy per lane, from base + lane_offset (base
-// uniform): lane i's chunk lands at byte lds_base + 16 i. Written as inline
-// assembly so that the compiler does not see an LDS store: it would
-// otherwise drain every outstanding copy before each LDS read of the loop.
-// Completion is tracked by the vector-memory counter (wait_vmcnt) and made
-// visible to the workgroup by a barrier. M0 holds the LDS base of a copy
-// (read when the copy issues) and is restored afterwards; a copy must not
-// directly follow a write of M0.
-__device__ __forceinline__ void copy_to_lds(const void* base, uint32_t lane_offset, uint32_t lds_base) {
-  uint32_t saved;
-  __asm__ volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(lane_offset), "s"(base), "s"(lds_base)
-      : "memory");
-}
-
-// One K and one V copy (as copy_to_lds, each from its own base).
-__device__ __forceinline__ void copy_kv_to_lds(const void* kbase, uint32_t koff, uint32_t klds, const void* vbase,
-                                               uint32_t voff, uint32_t vlds) {
-  uint32_t saved;
-  __asm__ volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %5\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %6\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, %4\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(koff), "s"(kbase), "v"(voff), "s"(vbase), "s"(klds), "s"(vlds)
-      : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_offset(const uint16_t* p) {
-  typedef __attribute__((address_space(3))) const uint16_t lds_u16;
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u16*)p);
-}
-
-// Workgroup barrier that does not wait for this wave's outstanding memory
-// operations (the copies of later steps stay in flight across it).
-__device__ __forceinline__ void step_barrier() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
 constexpr int PF_NW = 8;             // waves per workgroup
 constexpr int PF_NT = 64 * PF_NW;    // threads per workgroup
 
@@ -300,8 +241,8 @@ prefill_bf16_kernel(PrefillArgs a) {
       }
     }
   }
-  const uint32_t kring_lds = lds_offset(kring), vring_lds = lds_offset(vring);
-  const uint32_t rvring_lds = FP8 ? lds_offset(reinterpret_cast<const uint16_t*>(rvring)) : 0u;
+  const uint32_t kring_lds = lds_addr(kring), vring_lds = lds_addr(vring);
+  const uint32_t rvring_lds = FP8 ? lds_addr(reinterpret_cast<const uint16_t*>(rvring)) : 0u;
   // block ids are non-negative and a head's block stride is below 4 GiB
   auto copy_step = [&](int step, int kslot, int vslot) {
     if constexpr (CPW == 2) {
@@ -309,7 +250,7 @@ prefill_bf16_kernel(PrefillArgs a) {
       // the step
       const int b = min(b0 + 2 * step + (64 * wave) / (D * E), b_last);
       const uint64_t off = (uint64_t)(uint32_t)bt[b] * head_stride;
-      copy_kv_to_lds(kcache + off, cp_off[0], kring_lds + kslot * KSLOTB + 1024 * wave,
+      copy16x2_to_lds(kcache + off, cp_off[0], kring_lds + kslot * KSLOTB + 1024 * wave,
                      vcache + off, cp_off[1], vring_lds + vslot * (2 * S::VSLOT) + 1024 * wave);
     } else {
       static_assert(CPW == 1, "one or two copies per wave");
@@ -321,7 +262,7 @@ prefill_bf16_kernel(PrefillArgs a) {
       // (fp8: the raw V ring turns with the K ring)
       const uint32_t vdst = FP8 ? rvring_lds + kslot * RVSLOTB : vring_lds + vslot * (2 * S::VSLOT);
       const uint32_t lds = isv ? vdst + 1024 * jj : kring_lds + kslot * KSLOTB + 1024 * jj;
-      copy_to_lds((isv ? vcache : kcache) + off, cp_off[0], lds);
+      copy16_to_lds((isv ? vcache : kcache) + off, cp_off[0], lds);
     }
   };
 
@@ -337,9 +278,9 @@ prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
   for (int j = 0; j < KREADS; ++j) {
     if constexpr (FP8)
-      kaddr[j] = lds_offset(kring) + key_l * D + 16 * ((2 * j + h) ^ k8_swizzle<D>(key_l));
+      kaddr[j] = lds_addr(kring) + key_l * D + 16 * ((2 * j + h) ^ k8_swizzle<D>(key_l));
     else
-      kaddr[j] = lds_offset(kring) + 2 * (key_l * D + 8 * ((2 * j + h) ^ kswz_l));
+      kaddr[j] = lds_addr(kring) + 2 * (key_l * D + 8 * ((2 * j + h) ^ kswz_l));
   }
   u32x4 kf[KREADS];  // fp8: raw bytes of two k-steps, widened just before their MFMAs
   auto scores_load = [&](int slot) {
@@ -503,7 +444,7 @@ prefill_bf16_kernel(PrefillArgs a) {
   auto iteration = [&](auto masked_tag, int st, f32x16& sc, f32x16& sn) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     wait_vmcnt<(S::AHEAD - 2) * CPW>();  // the copies of step st+1 have landed
-    step_barrier();
+    barrier_keep_loads();
     if (pending) {
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt) o[dt] *= alpha;
@@ -593,7 +534,7 @@ prefill_bf16_kernel(PrefillArgs a) {
 
   // ---- epilogue: PV of the last step, values past the context zeroed ----
   wait_vmcnt<0>();
-  step_barrier();
+  barrier_keep_loads();
   if (pending) {
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt) o[dt] *= alpha;
@@ -636,8 +577,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     const float inv = 1.f / L;
     // the lane's column again, from a fresh lane id: the compiler would
     // otherwise keep the query row offset live across the whole loop
-    int le;
-    __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(le));
+    const int le = lane_id_here();
     const int col_e = wave * 32 + (le & 31);
     const int tok_e = col_e / G, head_e = col_e % G;
     if (tok_e < ntok) {
