@@ -18,7 +18,9 @@
 // Per step of 32 keys (two blocks):
 //  * the tile arrives by global->LDS copies issued two steps ahead, row
 //    major with a per-row XOR swizzle of its 16-byte chunks (conflict-free
-//    score-operand reads);
+//    score-operand reads); the copies are nontemporal, as every row is read
+//    once per call (measured: 16 heads 0.35 -> 0.26 ms, 128 heads ~5% faster
+//    on 64 sequences of 4K-32K keys);
 //  * one pass by all 512 threads writes the value part again, transposed and
 //    converted to fp16 ([512 dims][32 keys], 64-byte rows with a chunk
 //    swizzle), zeroing keys past the context: the value product needs 8
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
         if (c < npieces) {
           const int k = wave + NW * c;
           const int blk = k < S::PIECES / 2 ? b0 : b1;
-          copy16_to_lds(cache + (size_t)(uint32_t)blk * S::BLKB, src_off(k, ln), slot + 1024u * (uint32_t)k);
+          copy16_to_lds<true>(cache + (size_t)(uint32_t)blk * S::BLKB, src_off(k, ln), slot + 1024u * (uint32_t)k);
         }
       }
     };
@@ -573,7 +575,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (c < npieces) {
           const int k = wave + NW * c;
           const int blk = k < S::PIECES / 2 ? b0 : b1;
-          copy16_to_lds(cache + (size_t)(uint32_t)blk * S::BLKB, src_off(k, ln), slot + 1024u * (uint32_t)k);
+          copy16_to_lds<true>(cache + (size_t)(uint32_t)blk * S::BLKB, src_off(k, ln), slot + 1024u * (uint32_t)k);
         }
       }
     };
@@ -951,7 +953,7 @@ __global__ __launch_bounds__(64 * kNarrowWaves) __attribute__((amdgpu_waves_per_
       const uint8_t* base = cache + (size_t)(uint32_t)bt[b0 + i] * S::BLKB;
       const uint32_t slot = ring_lds + (uint32_t)((i & (NSL - 1)) * S::BLKB);
 #pragma unroll
-      for (int k = 0; k < S::COPIES; ++k) copy16_to_lds(base, src[k], slot + 1024u * (uint32_t)k);
+      for (int k = 0; k < S::COPIES; ++k) copy16_to_lds<true>(base, src[k], slot + 1024u * (uint32_t)k);
     };
     // the queries have landed before any copy is issued (a wait the compiler
     // placed for them later would drain the copies in flight)
