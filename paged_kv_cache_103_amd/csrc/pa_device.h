@@ -191,21 +191,37 @@ __device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t lane_of
 }
 
 // Two such copies (a K and a V chunk, each from its own base) in one block.
+template <bool NT = false>
 __device__ __forceinline__ void copy16x2_to_lds(const void* base0, uint32_t off0, uint32_t lds0, const void* base1,
                                                 uint32_t off1, uint32_t lds1) {
   uint32_t saved;
-  __asm__ volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %5\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %6\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, %4\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off0), "s"(base0), "v"(off1), "s"(base1), "s"(lds0), "s"(lds1)
-      : "memory");
+  if constexpr (NT) {
+    __asm__ volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %5\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt\n\t"
+        "s_mov_b32 m0, %6\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %4 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off0), "s"(base0), "v"(off1), "s"(base1), "s"(lds0), "s"(lds1)
+        : "memory");
+  } else {
+    __asm__ volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %5\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %6\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %4\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off0), "s"(base0), "v"(off1), "s"(base1), "s"(lds0), "s"(lds1)
+        : "memory");
+  }
 }
 
 // The lane id, recomputed where it is used: the compiler cannot hoist a
