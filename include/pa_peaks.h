@@ -23,12 +23,15 @@ typedef struct ihipStream_t* pa_stream_t;
 
 /*
  * Reads `ntiles` tiles of 4 KiB, tile t at byte offset 4096 * tile_ids[t] of
- * buf (every id in [0, buf_bytes / 4096)), as a paged gather does: one wave
- * per tile, 16-byte nontemporal loads. mode 0: each load instruction covers
- * 1 KiB contiguous; mode 1: the decode kernel's key pattern (64 bytes from
- * each of 16 rows of 256 bytes). grid_blocks workgroups of 256 threads
- * stride over the tiles. sink: >= grid_blocks uint32, written only to keep
- * the loads alive.
+ * buf (every id in [0, buf_bytes / 4096)), as a paged gather does. mode 0:
+ * one wave per tile, 16-byte nontemporal loads, each load instruction
+ * covering 1 KiB contiguous; mode 1: the same with the decode kernel's key
+ * pattern (64 bytes from each of 16 rows of 256 bytes); mode 2: 16-byte
+ * nontemporal global -> LDS copies, each wave a contiguous range of the list
+ * with one tile in flight while it reads the previous one back from LDS.
+ * grid_blocks workgroups of 256 threads share the tiles; another mode
+ * returns hipErrorInvalidValue. sink: >= grid_blocks uint32, written only to
+ * keep the loads alive.
  */
 int32_t pa_peak_read_tiles(const void* buf, const int32_t* tile_ids, int32_t ntiles, int32_t mode,
                            int32_t grid_blocks, uint32_t* sink, pa_stream_t stream);

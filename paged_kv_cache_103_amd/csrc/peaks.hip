@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "pa_device.h"
+
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -31,6 +33,47 @@ __global__ __launch_bounds__(256) void read_tiles(const u32x4* __restrict__ p, c
     // partly used vector is narrowed to 4-byte loads by the compiler)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc ^= a[j].x ^ a[j].y ^ a[j].z ^ a[j].w;
+  }
+  if (threadIdx.x == 0) sink[blockIdx.x] = acc;
+}
+
+// The same gather by direct global -> LDS copies (nontemporal), as the
+// side-by-side decode stages its tiles: each wave takes a contiguous range
+// of the tile list and keeps one tile in flight while it reads the other
+// from a ring of two (every copied byte is read back from LDS).
+__global__ __launch_bounds__(256) void read_tiles_lds(const uint8_t* p, const int* ids, int ntiles, uint32_t* sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4][2][4096];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = gridDim.x * 4;
+  const int per = (ntiles + nw - 1) / nw;
+  const int x0 = (blockIdx.x * 4 + wave) * per;
+  const int n = min(ntiles, x0 + per) - x0;
+  typedef __attribute__((address_space(4))) const int cint;
+  const cint* tc = (const cint*)ids;
+  const uint32_t ring_lds = pa::lds_addr(&ring[wave][0][0]);
+  auto issue = [&](int u) {  // tile x0 + u into slot u % 2
+    const uint8_t* src = p + (size_t)(uint32_t)tc[x0 + u] * 4096;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pa::copy16_to_lds<true>(src + 1024 * j, 16u * lane, ring_lds + (u & 1) * 4096 + 1024 * j);
+  };
+  uint32_t acc = 0;
+  if (n > 0) {
+    issue(0);
+    for (int u = 0; u < n; ++u) {
+      if (u + 1 < n) {
+        issue(u + 1);
+        pa::wait_vmcnt<4>();
+      } else {
+        pa::wait_vmcnt<0>();
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 v = pa::lds_read16(ring_lds + (u & 1) * 4096 + 1024 * j + 16 * lane);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+      }
+      pa::wait_lgkmcnt0();  // the slot's reads are done before the next copy into it
+    }
   }
   if (threadIdx.x == 0) sink[blockIdx.x] = acc;
 }
@@ -181,8 +224,13 @@ extern "C" int32_t pa_peak_read_tiles(const void* buf, const int32_t* tile_ids, 
   const u32x4* p = static_cast<const u32x4*>(buf);
   if (mode == 0)
     hipLaunchKernelGGL(read_tiles<0>, dim3(grid_blocks), dim3(256), 0, (hipStream_t)stream, p, tile_ids, ntiles, sink);
-  else
+  else if (mode == 1)
     hipLaunchKernelGGL(read_tiles<1>, dim3(grid_blocks), dim3(256), 0, (hipStream_t)stream, p, tile_ids, ntiles, sink);
+  else if (mode == 2)
+    hipLaunchKernelGGL(read_tiles_lds, dim3(grid_blocks), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<const uint8_t*>(buf), tile_ids, ntiles, sink);
+  else
+    return (int32_t)hipErrorInvalidValue;
   return (int32_t)hipGetLastError();
 }
 

@@ -37,7 +37,7 @@ def load() -> ctypes.CDLL:
 
 def read_tiles(buf: torch.Tensor, tile_ids: torch.Tensor, mode: int, grid_blocks: int, sink: torch.Tensor) -> None:
     """Gather the 4 KiB tiles tile_ids (int32) of buf; mode 0 contiguous 1 KiB
-    loads, 1 the decode kernel's key pattern."""
+    loads, 1 the decode kernel's key pattern, 2 global -> LDS copies."""
     assert tile_ids.dtype == torch.int32
     assert buf.numel() * buf.element_size() >= 4096 * (int(tile_ids.max()) + 1)
     assert sink.numel() * sink.element_size() >= 4 * grid_blocks

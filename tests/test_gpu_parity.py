@@ -619,6 +619,22 @@ def test_peak_probes_run():
     sink = torch.full((256 * 8,), -1.0, dtype=torch.float32, device=DEV)
     for mode in (0, 1):
         peaks.read_tiles(buf, ids, mode, 8, sink)
+    # the global->LDS gather reads the right bytes: each workgroup's thread 0
+    # leaves the XOR of the first 16 bytes of every 1 KiB of its wave's tiles
+    # (wave 0 of workgroup b takes tiles [4 b C, 4 b C + C), C = 64 / 32)
+    words = torch.randint(-2**31, 2**31 - 1, (64 * 1024,), dtype=torch.int32)
+    buf2 = words.to(DEV).view(torch.uint8)
+    sink2 = torch.zeros(8, dtype=torch.int32, device=DEV)
+    peaks.read_tiles(buf2, ids, 2, 8, sink2)
+    torch.cuda.synchronize()
+    w = words.view(64, 4, 256)[:, :, :4]  # tile, 1 KiB chunk, first 4 words
+    idl = ids.cpu().long()
+    for b in range(8):
+        want = 0
+        for t in idl[8 * b:8 * b + 2]:
+            for x in w[t].reshape(-1).tolist():
+                want ^= x
+        assert int(sink2[b].item()) == want, (b, int(sink2[b].item()), want)
     flops = peaks.mfma(0, 10, 8, sink)
     peaks.mfma(1, 10, 8, sink)
     torch.cuda.synchronize()
