@@ -718,7 +718,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int cache_kind, int head_size
 // decode kernel beside it must fit in the rest: one wave per SIMD of at most
 // 64 registers and one workgroup per CU of at most ~92 KB of LDS. This kernel keeps its
 // loads in flight in LDS instead of registers: each wave streams its 4 KiB
-// K and V tiles through a ring of kSideSlots tiles with direct global->LDS
+// K and V tiles through a 20 KiB ring (5 bf16 or 10 fp8 tiles) with direct global->LDS
 // copies (nontemporal: read once), and more than 80 KB of LDS per workgroup
 // keeps a second one off the same CU (which would leave no room there for a
 // prefill workgroup).
@@ -735,8 +735,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int cache_kind, int head_size
 // The split plan, summary records and merge are those of decode_mfma_split
 // (wave w takes block-heads [w*C, (w+1)*C), summaries in slot w + stream).
 constexpr int kSideWaves = 4;
-constexpr int kSideSlots = 5;                                  // 4 KiB tiles per wave's ring
-constexpr int kSideRingBytes = kSideWaves * kSideSlots * 4096;
+constexpr int kSideRingBytes = kSideWaves * 20 * 1024;        // 20 KiB ring per wave
 constexpr int kSideQBytes = kSideWaves * 1024;                 // a wave's 4 query heads, bf16 [4][128]
 
 size_t decode_side_lds_bytes(int num_seqs) {
@@ -753,13 +752,24 @@ __device__ __forceinline__ f32x4 mfma_4x4x4_from(uint32_t a0, uint32_t a1, uint3
   return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(A, B, c, 4, 4 * Q, 0);
 }
 
+// The value product of key quad Q (P broadcast from block 4Q), P as bf16
+// hi + lo against the quad's value operand (b0, b1).
+template <int Q>
+__device__ __forceinline__ f32x4 side_pv_quad(uint32_t h0, uint32_t h1, uint32_t l0, uint32_t l1, uint32_t b0,
+                                              uint32_t b1, f32x4 o) {
+  o = mfma_4x4x4_from<Q>(h0, h1, b0, b1, o);
+  return mfma_4x4x4_from<Q>(l0, l1, b0, b1, o);
+}
 
-template <int D>
 // (amdgpu_num_vgpr counts half the registers on this target: 32 -> 64)
+template <int CK, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void decode_side(DecodeArgs a) {
-  static_assert(D == 128, "head size 128");
-  constexpr int G = 4, NS = kSideSlots;
-  constexpr uint32_t TILE = 16 * D * 2;
+  constexpr int D = 128;
+  static_assert(G == 1 || G == 2 || G == 4, "groups of 1, 2 or 4 query heads");
+  constexpr bool FP8 = CK == KFP8;
+  constexpr uint32_t TILE = 16 * D * (FP8 ? 1 : 2);           // one (block, KV head) tile
+  constexpr int CPT = (int)TILE / 1024;                        // 1 KiB copies per tile
+  constexpr int NS = kSideRingBytes / kSideWaves / (int)TILE;  // tiles in a wave's ring (5 bf16, 10 fp8)
   extern __shared__ __attribute__((aligned(16))) int side_lds[];
   uint8_t* ring = reinterpret_cast<uint8_t*>(side_lds);
   uint8_t* qslots = ring + kSideRingBytes;
@@ -778,18 +788,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
     for (int i = tid; i <= NSEQ; i += 256) a.meta[1 + i] = psum[i];
   }
 
-  typedef __attribute__((address_space(3))) uint8_t lds_u8;
-  const uint32_t ring_lds =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)ring) + wave * NS * TILE;
-  const uint32_t q_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)qslots) + wave * 1024;
-  const uint8_t* ring_w = ring + wave * NS * TILE;
-  const uint8_t* q_w = qslots + wave * 1024;
-  // per-lane global offsets of the copies: K copy c brings (key l%16, chunk
-  // 4c + l/16) to byte 1024c + 16l of the slot, where lane l's score operand
-  // of k-step c is read; V copy 2h + c brings (row 64h + l, chunk c)
-  const uint32_t koff = (uint32_t)((lane & 15) * 256 + 16 * (lane >> 4));
-  const uint32_t voff = (uint32_t)(32 * lane);
+  const uint32_t ring_lds = lds_addr(ring) + wave * NS * TILE;
+  const uint32_t q_lds = lds_addr(qslots) + wave * 1024;
+  // Per-lane global offsets of the copies; copy c lands lane l's 16 bytes at
+  // byte 1024 c + 16 l of the slot, where lane l reads them:
+  //  bf16 K copy c: key l%16, 16-byte chunk 4c + l/16 (the score operand of
+  //   k-step c); fp8 K copy c: key l%16, bytes 64c + 16(l/16) (k-steps 2c and
+  //   2c + 1, 8 bytes each: the dims kstep_d0<1> assigns);
+  //  bf16 V copy 2h + c: dim row 64h + l, chunk c (keys 8c..8c+7); fp8 V copy
+  //   h: dim row 64h + l (16 keys).
+  const uint32_t koff = (uint32_t)((lane & 15) * (D * (FP8 ? 1 : 2)) + 16 * (lane >> 4));
+  const uint32_t voff = (uint32_t)((FP8 ? 16 : 32) * lane);
   typedef __attribute__((address_space(4))) const int cint;
+  typedef __attribute__((address_space(4))) const float cfloat;
 
   const int w = blockIdx.x * kSideWaves + wave;
   const long long x_end = min<long long>((long long)(w + 1) * C, T);
@@ -815,30 +826,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
     const uint8_t* kcache = reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)g * TILE;
     const uint8_t* vcache = reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * TILE;
 
-    // the 4 query heads (contiguous, 1 KiB) to LDS, then the first tiles
+    // the group's G query heads to LDS, repeated over the 4 MFMA rows (row r
+    // holds head r % G), then the first tiles
     wait_lgkmcnt0();
     copy16_to_lds<true>(reinterpret_cast<const uint8_t*>(a.query) + ((size_t)qrow * a.num_heads + g * G) * D * 2,
-              16u * lane, q_lds);
+                        16u * (uint32_t)(lane % (16 * G)), q_lds);
     const int ntile = 2 * nblk;  // tile u: block blk0 + u/2, K if u is even, else V
     auto issue = [&](int u) {
       const uint8_t* src = ((u & 1) ? vcache : kcache) + (size_t)(uint32_t)bt[blk0 + (u >> 1)] * head_stride;
       const uint32_t dst = ring_lds + (uint32_t)(u % NS) * TILE;
-      if (u & 1) {
+      if ((u & 1) && !FP8) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) copy16_to_lds<true>(src + 2048 * (c >> 1) + 16 * (c & 1), voff, dst + 1024 * c);
+      } else if (u & 1) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) copy16_to_lds<true>(src + 1024 * c, voff, dst + 1024 * c);
       } else {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) copy16_to_lds<true>(src + 64 * c, koff, dst + 1024 * c);
+        for (int c = 0; c < CPT; ++c) copy16_to_lds<true>(src + 64 * c, koff, dst + 1024 * c);
       }
     };
     for (int u = 0; u < NS - 1 && u < ntile; ++u) issue(u);
-    // tile u is in LDS once at most 4 * (NS - 1) copies issued after it are
+    // tile u is in LDS once at most CPT * (NS - 1) copies issued after it are
     // outstanding; tile u + NS - 1 reuses the slot of tile u - 1
     auto next = [&](int u) {
       wait_lgkmcnt0();
       if (u + NS - 1 < ntile) {
         issue(u + NS - 1);
-        wait_vmcnt<4 * (NS - 1)>();
+        wait_vmcnt<CPT * (NS - 1)>();
       } else {
         wait_vmcnt<0>();
       }
@@ -850,20 +865,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
       const int b = blk0 + n;
       // ---- scores of block b ----
       next(2 * n);
-      const uint8_t* ks = ring_w + ((2 * n) % NS) * TILE;
+      const uint32_t ks = ring_lds + (uint32_t)((2 * n) % NS) * TILE;
+      const uint32_t qs = q_lds + (uint32_t)((lane & 3) * 256);
       f32x4 st = {0.f, 0.f, 0.f, 0.f};
+      float kscale = a.scale_log2, vscale = 1.f;
+      if constexpr (FP8) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + 1024 * j + 16 * lane);
-        const u32x4 qf = *reinterpret_cast<const u32x4*>(q_w + (lane & 3) * 256 + 64 * j + 16 * (lane >> 4));
-        st = mfma_bf16_16x16x32(kf, qf, st);
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 kw = lds_read16(ks + 1024 * h + 16 * lane);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {  // k-step 2h + t: dims 64h + 16(l/16) + 8t
+            const u32x4 qf = lds_read16(qs + 128 * h + 32 * (lane >> 4) + 16 * t);
+            st = mfma_bf16_16x16x32(fp8x8_to_bf16x8(kw[2 * t], kw[2 * t + 1]), qf, st);
+          }
+        }
+        const uint32_t phys = (uint32_t)bt[b];  // the block's scales (scalar loads)
+        kscale *= ((const cfloat*)a.k_scale)[phys];
+        vscale = ((const cfloat*)a.v_scale)[phys];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 kf = lds_read16(ks + 1024 * j + 16 * lane);
+          const u32x4 qf = lds_read16(qs + 64 * j + 16 * (lane >> 4));
+          st = mfma_bf16_16x16x32(kf, qf, st);
+        }
       }
-      // lane's keys: b*16 + 4*(lane/16) + r, head lane % 4
+      // lane's keys: b*16 + 4*(lane/16) + r, head row lane % 4
       const bool edge = b * 16 < lo || b * 16 + 16 > kend;
       float xs[4], lmax = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float v = st[r] * a.scale_log2;
+        float v = st[r] * kscale;
         if (edge) {
           const int kp = b * 16 + 4 * (lane >> 4) + r;
           v = (kp >= lo && kp < kend) ? v : -INFINITY;
@@ -883,7 +915,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
         m = up ? tmax : m;
         lsum *= alpha;
 #pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {  // lane hh holds head hh's factor
+        for (int hh = 0; hh < 4; ++hh) {  // lane hh holds head row hh's factor
           const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), hh));
           o0[hh] *= ah;
           o1[hh] *= ah;
@@ -892,8 +924,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
       float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(xs[r] - m);
-        lsum += p[r];
+        const float e = __builtin_amdgcn_exp2f(xs[r] - m);
+        lsum += e;
+        p[r] = e * vscale;  // (fp8: the block's V scale moves onto the weights)
       }
       const uint32_t h0 = pack_bf16x2(p[0], p[1]), h1 = pack_bf16x2(p[2], p[3]);
       const uint32_t l0 = pack_bf16x2(p[0] - bf16_lo(h0), p[1] - bf16_hi(h0));
@@ -901,102 +934,128 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
 
       // ---- O += P V of block b ----
       next(2 * n + 1);
-      const uint8_t* vs = ring_w + ((2 * n + 1) % NS) * TILE;
+      const uint32_t vs = ring_lds + (uint32_t)((2 * n + 1) % NS) * TILE;
+      const bool vtail = b * 16 + 16 > kend;  // keys past the context may hold anything: zero them
+      // mask of the key pair (kk, kk + 1) in a packed bf16 word
+      auto keep2 = [&](int kk) {
+        return (kk < kend ? 0x0000ffffu : 0u) | (kk + 1 < kend ? 0xffff0000u : 0u);
+      };
+      if constexpr (FP8) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        u32x4 v0 = *reinterpret_cast<const u32x4*>(vs + 1024 * c + 16 * lane);        // dim lane, keys 8c..8c+7
-        u32x4 v1 = *reinterpret_cast<const u32x4*>(vs + 1024 * (2 + c) + 16 * lane);  // dim 64 + lane
-        if (b * 16 + 16 > kend) {  // keys past the context may hold anything: zero them
+        for (int h = 0; h < 2; ++h) {  // dim row 64h + lane, 16 keys
+          const u32x4 vw = lds_read16(vs + 1024 * h + 16 * lane);
+          uint32_t vb[8];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int k0 = b * 16 + 8 * c + 2 * t;
-            const uint32_t msk = (k0 < kend ? 0x0000ffffu : 0u) | (k0 + 1 < kend ? 0xffff0000u : 0u);
-            v0[t] &= msk;
-            v1[t] &= msk;
+          for (int q = 0; q < 4; ++q) fp8x4_to_bf16x4(vw[q], vb[2 * q], vb[2 * q + 1]);
+          if (vtail) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) vb[t] &= keep2(b * 16 + 2 * t);
           }
+          f32x4& o = h ? o1 : o0;
+          o = side_pv_quad<0>(h0, h1, l0, l1, vb[0], vb[1], o);
+          o = side_pv_quad<1>(h0, h1, l0, l1, vb[2], vb[3], o);
+          o = side_pv_quad<2>(h0, h1, l0, l1, vb[4], vb[5], o);
+          o = side_pv_quad<3>(h0, h1, l0, l1, vb[6], vb[7], o);
         }
-        if (c == 0) {
-          o0 = mfma_4x4x4_from<0>(h0, h1, v0[0], v0[1], o0);
-          o0 = mfma_4x4x4_from<0>(l0, l1, v0[0], v0[1], o0);
-          o1 = mfma_4x4x4_from<0>(h0, h1, v1[0], v1[1], o1);
-          o1 = mfma_4x4x4_from<0>(l0, l1, v1[0], v1[1], o1);
-          o0 = mfma_4x4x4_from<1>(h0, h1, v0[2], v0[3], o0);
-          o0 = mfma_4x4x4_from<1>(l0, l1, v0[2], v0[3], o0);
-          o1 = mfma_4x4x4_from<1>(h0, h1, v1[2], v1[3], o1);
-          o1 = mfma_4x4x4_from<1>(l0, l1, v1[2], v1[3], o1);
-        } else {
-          o0 = mfma_4x4x4_from<2>(h0, h1, v0[0], v0[1], o0);
-          o0 = mfma_4x4x4_from<2>(l0, l1, v0[0], v0[1], o0);
-          o1 = mfma_4x4x4_from<2>(h0, h1, v1[0], v1[1], o1);
-          o1 = mfma_4x4x4_from<2>(l0, l1, v1[0], v1[1], o1);
-          o0 = mfma_4x4x4_from<3>(h0, h1, v0[2], v0[3], o0);
-          o0 = mfma_4x4x4_from<3>(l0, l1, v0[2], v0[3], o0);
-          o1 = mfma_4x4x4_from<3>(h0, h1, v1[2], v1[3], o1);
-          o1 = mfma_4x4x4_from<3>(l0, l1, v1[2], v1[3], o1);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          u32x4 v0 = lds_read16(vs + 1024 * c + 16 * lane);        // dim lane, keys 8c..8c+7
+          u32x4 v1 = lds_read16(vs + 1024 * (2 + c) + 16 * lane);  // dim 64 + lane
+          if (vtail) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const uint32_t msk = keep2(b * 16 + 8 * c + 2 * t);
+              v0[t] &= msk;
+              v1[t] &= msk;
+            }
+          }
+          if (c == 0) {
+            o0 = side_pv_quad<0>(h0, h1, l0, l1, v0[0], v0[1], o0);
+            o1 = side_pv_quad<0>(h0, h1, l0, l1, v1[0], v1[1], o1);
+            o0 = side_pv_quad<1>(h0, h1, l0, l1, v0[2], v0[3], o0);
+            o1 = side_pv_quad<1>(h0, h1, l0, l1, v1[2], v1[3], o1);
+          } else {
+            o0 = side_pv_quad<2>(h0, h1, l0, l1, v0[0], v0[1], o0);
+            o1 = side_pv_quad<2>(h0, h1, l0, l1, v1[0], v1[1], o1);
+            o0 = side_pv_quad<3>(h0, h1, l0, l1, v0[2], v0[3], o0);
+            o1 = side_pv_quad<3>(h0, h1, l0, l1, v1[2], v1[3], o1);
+          }
         }
       }
     }
 
-    // ---- the segment's result: lane hh (< 4) holds head hh's max and sum ----
+    // ---- the segment's result: lane hh (< 4) holds head row hh's max and
+    // sum; rows hh < G are the group's heads ----
     const float L = strided_sum<16>(lsum);
     const bool single = (sstart / C) == ((sstart + nb - 1) / C);
-    float mh[4], Lh[4];
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      mh[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), hh));
-      Lh[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(L), hh));
-    }
     if (single) {
       uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * a.num_heads + g * G) * D + lane;
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        const float inv = Lh[hh] > 0.f ? 1.f / Lh[hh] : 0.f;
+      for (int hh = 0; hh < G; ++hh) {
+        const float Lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(L), hh));
+        const float inv = Lh > 0.f ? 1.f / Lh : 0.f;
         op[hh * D] = f32_to_bf16(o0[hh] * inv);
         op[hh * D + 64] = f32_to_bf16(o1[hh] * inv);
       }
-      if (a.lse != nullptr && lane < 4)
+      if (a.lse != nullptr && lane < G)
         a.lse[(size_t)qrow * a.num_heads + g * G + lane] = (m + log2f(L)) * kLn2;
     } else {
       const size_t rec = (size_t)slot * a.rec_cols;
       float* op = a.part_o + rec * D + lane;
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
+      for (int hh = 0; hh < G; ++hh) {
         op[hh * D] = o0[hh];
         op[hh * D + 64] = o1[hh];
       }
-      if (lane < 4) {
+      if (lane < G) {
         a.part_ml[(rec + lane) * 2] = m;
         a.part_ml[(rec + lane) * 2 + 1] = L;
       }
     }
-    (void)mh;
     x = seg_end;
   }
 }
 
 bool decode_side_supported(int q_kind, int cache_kind, int head_size, int group) {
-  return q_kind == KBF16 && cache_kind == KBF16 && head_size == 128 && group == 4;
+  return q_kind == KBF16 && (cache_kind == KBF16 || cache_kind == KFP8) && head_size == 128 &&
+         (group == 1 || group == 2 || group == 4);
 }
 
-// The side kernel (one workgroup per CU) and the merge, on `st`. The
-// workspace is the split plan's (a.split_waves >= the side kernel's waves).
-hipError_t launch_decode_side(const DecodeArgs& a, hipStream_t st) {
+template <int CK, int G>
+static hipError_t run_decode_side(const DecodeArgs& a, hipStream_t st) {
   const int grid = device_cu_count();
-  if (a.split_waves < grid * kSideWaves || a.one_per_stream) return hipErrorInvalidValue;
   const size_t lds = decode_side_lds_bytes(a.num_seqs);
-  static std::atomic<size_t> lds_set{0};
+  static std::atomic<size_t> lds_set{0};  // (per instantiation)
   if (lds_set.load(std::memory_order_relaxed) < lds) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_side<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipError_t e = hipFuncSetAttribute((const void*)decode_side<CK, G>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;
     lds_set.store(lds, std::memory_order_relaxed);
   }
-  hipLaunchKernelGGL((decode_side<128>), dim3(grid), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((decode_side<CK, G>), dim3(grid), dim3(256), lds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int waves = a.num_seqs * a.num_heads;
   hipLaunchKernelGGL((decode_split_merge<128, false>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+// The side kernel (one workgroup per CU) and the merge, on `st`. The
+// workspace is the split plan's (a.split_waves >= the side kernel's waves).
+hipError_t launch_decode_side(const DecodeArgs& a, int cache_kind, hipStream_t st) {
+  if (a.split_waves < device_cu_count() * kSideWaves || a.one_per_stream) return hipErrorInvalidValue;
+  const int G = a.num_heads / a.num_kv_heads;
+  if (cache_kind == KBF16) {
+    if (G == 4) return run_decode_side<KBF16, 4>(a, st);
+    if (G == 2) return run_decode_side<KBF16, 2>(a, st);
+    if (G == 1) return run_decode_side<KBF16, 1>(a, st);
+  } else if (cache_kind == KFP8) {
+    if (G == 4) return run_decode_side<KFP8, 4>(a, st);
+    if (G == 2) return run_decode_side<KFP8, 2>(a, st);
+    if (G == 1) return run_decode_side<KFP8, 1>(a, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

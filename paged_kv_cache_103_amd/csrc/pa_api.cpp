@@ -729,7 +729,7 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
     if (e != hipSuccess) return hip_status(e, "side stream fork");
     e = pa::launch_prefill(p, (int)cache_dtype, head_size, hs);
     if (e != hipSuccess) return hip_status(e, "prefill launch");
-    const hipError_t ed = pa::launch_decode_side(d, ss->stream);
+    const hipError_t ed = pa::launch_decode_side(d, (int)cache_dtype, ss->stream);
     e = hipEventRecord(ss->join, ss->stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(hs, ss->join, 0);
     if (ed != hipSuccess) return hip_status(ed, "decode launch (one-token rows)");

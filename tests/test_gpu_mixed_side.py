@@ -2,8 +2,9 @@
 
 pa_prefill_chunk decodes the one-token rows of a batch that also holds
 longer chunks on a second stream, next to the prefill kernel, when the
-shapes allow it (bf16 queries and cache, head size 128, 4 query heads per KV
-head, contexts long enough for the split plan, LDS for the sequence count):
+shapes allow it (bf16 queries, bf16 or fp8 e4m3 cache, head size 128, 1, 2
+or 4 query heads per KV head, contexts long enough for the split plan, LDS
+for the sequence count):
 "从静态批处理到状态化推理集群", "Chunked prefill：在共置引擎里治理阶段干扰" (a
 step mixes decode rows and prefill chunks). Every row is compared with the
 oracle at the usual bar; the split plan the side kernel leaves in the
@@ -74,20 +75,27 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", range(len(CASES)))
-def test_mixed_batch_rows_beside_prefill(case):
+# (case, query heads, KV heads, cache dtype): the group sizes and cache types
+# the side kernel serves
+SHAPES = [(0, 32, 8, "bf16"), (1, 32, 8, "bf16"), (2, 32, 8, "bf16"), (0, 32, 8, "fp8_e4m3"),
+          (1, 32, 8, "fp8_e4m3"), (2, 16, 8, "bf16"), (0, 8, 8, "fp8_e4m3"), (1, 16, 16, "bf16"),
+          (2, 16, 8, "fp8_e4m3")]
+
+
+@pytest.mark.parametrize("case,hq,hkv,cache", SHAPES)
+def test_mixed_batch_rows_beside_prefill(case, hq, hkv, cache):
     ctx, ql, win = CASES[case]
-    b = W.make_batch(f"side{case}", 980 + case, ctx, ql, 32, 8, 128, "bf16", "bf16", sliding_window=win,
-                     device=DEV, extra_blocks=2)
+    b = W.make_batch(f"side{case}_{hq}_{hkv}_{cache}", 980 + case + hq + 7 * hkv, ctx, ql, hq, hkv, 128, "bf16", cache,
+                     sliding_window=win, device=DEV, extra_blocks=2)
     out, ws = run_prefill(b)
     torch.cuda.synchronize()
-    check_all(b, out, f"mixed batch {case} (window {win})")
+    check_all(b, out, f"mixed batch {case} ({hq}/{hkv} heads, {cache}, window {win})")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     c = int(ws[:4].view(torch.int32).item())
     # the side kernel splits over 4 waves per CU, the stand-alone decode over
     # 8 (the two plans differ unless both hit the 8-block minimum)
     assert c == split_chunk(b, 4 * cus), (c, split_chunk(b, 4 * cus), split_chunk(b, 8 * cus))
-    if case != 1:
+    if split_chunk(b, 4 * cus) != split_chunk(b, 8 * cus):
         assert c != split_chunk(b, 8 * cus)
     _log(f"mixed batch {case}: rows decoded beside the prefill (chunk {c} blocks per wave)")
 
