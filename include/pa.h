@@ -360,8 +360,8 @@ size_t pa_mla_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads);
  *   bf16 hi + lo, so every finite cached value is in the domain; the fp32
  *   accumulator needs 2^15 * sum_j |v_j| below 3.4e38.
  * Streams: a batch holding both one-token rows and longer chunks, with bf16
- *   queries, a bf16 or fp8 e4m3 cache, head_size 128 and 1, 2 or 4 query
- *   heads per KV head (and a context long enough that the decode plan
+ *   queries, a bf16 or fp8 e4m3 cache, head_size 128 and 1, 2, 4 or 8
+ *   query heads per KV head (and a context long enough that the decode plan
  *   splits streams over waves),
  *   has its one-token rows decoded on a second stream that the library owns
  *   (one per device, default priority), next to the chunks' prefill kernel

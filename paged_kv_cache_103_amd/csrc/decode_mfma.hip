@@ -723,7 +723,9 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int cache_kind, int head_size
 // keeps a second one off the same CU (which would leave no room there for a
 // prefill workgroup).
 //
-// Per 16-key block and KV head (G = 4 query heads, head size 128):
+// Per 16-key block and KV head (G = 4 query heads, head size 128; groups of
+// 1 and 2 repeat their heads over the 4 rows, groups of 8 add a second set
+// of rows, 4..7, broadcast from block 4q + 1):
 //  * scores S^T = K Q^T on four 16x16x32 bf16 MFMAs; the 16 columns are the 4
 //    heads repeated, so lane 16q + i (i < 4) ends up holding head i's scores
 //    of keys 4q..4q+3;
@@ -736,36 +738,36 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int cache_kind, int head_size
 // (wave w takes block-heads [w*C, (w+1)*C), summaries in slot w + stream).
 constexpr int kSideWaves = 4;
 constexpr int kSideRingBytes = kSideWaves * 20 * 1024;        // 20 KiB ring per wave
-constexpr int kSideQBytes = kSideWaves * 1024;                 // a wave's 4 query heads, bf16 [4][128]
+// a wave's query rows (bf16 [rows][128]): 4 rows (the group's heads
+// repeated) for groups of up to 4, 8 for groups of 8
+__host__ __device__ constexpr int side_q_rows(int group) { return group == 8 ? 8 : 4; }
 
-size_t decode_side_lds_bytes(int num_seqs) {
-  return (size_t)kSideRingBytes + kSideQBytes + (size_t)(num_seqs + 1 + 256) * sizeof(int);
+size_t decode_side_lds_bytes(int num_seqs, int group) {
+  return (size_t)kSideRingBytes + (size_t)kSideWaves * side_q_rows(group) * 256 +
+         (size_t)(num_seqs + 1 + 256) * sizeof(int);
 }
 
 typedef short side_s16x4 __attribute__((ext_vector_type(4)));
 
-// O += A B on the 16 4x4x4 blocks, A (P) taken from block 4q for all blocks.
-template <int Q>
-__device__ __forceinline__ f32x4 mfma_4x4x4_from(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
-  const side_s16x4 A = __builtin_bit_cast(side_s16x4, (u32x2){a0, a1});
-  const side_s16x4 B = __builtin_bit_cast(side_s16x4, (u32x2){b0, b1});
-  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(A, B, c, 4, 4 * Q, 0);
-}
 
-// The value product of key quad Q (P broadcast from block 4Q), P as bf16
-// hi + lo against the quad's value operand (b0, b1).
-template <int Q>
-__device__ __forceinline__ f32x4 side_pv_quad(uint32_t h0, uint32_t h1, uint32_t l0, uint32_t l1, uint32_t b0,
-                                              uint32_t b1, f32x4 o) {
-  o = mfma_4x4x4_from<Q>(h0, h1, b0, b1, o);
-  return mfma_4x4x4_from<Q>(l0, l1, b0, b1, o);
+// The value product of one key quad with P broadcast from block ABID (4q
+// for the quad's heads 0..3, 4q + 1 for heads 4..7), P as bf16 hi + lo
+// against the quad's value operand (b0, b1).
+template <int ABID>
+__device__ __forceinline__ f32x4 side_pv(uint32_t h0, uint32_t h1, uint32_t l0, uint32_t l1, uint32_t b0, uint32_t b1,
+                                         f32x4 o) {
+  const side_s16x4 B = __builtin_bit_cast(side_s16x4, (u32x2){b0, b1});
+  o = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(side_s16x4, (u32x2){h0, h1}), B, o, 4, ABID, 0);
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(side_s16x4, (u32x2){l0, l1}), B, o, 4, ABID, 0);
 }
 
 // (amdgpu_num_vgpr counts half the registers on this target: 32 -> 64)
 template <int CK, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void decode_side(DecodeArgs a) {
   constexpr int D = 128;
-  static_assert(G == 1 || G == 2 || G == 4, "groups of 1, 2 or 4 query heads");
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "groups of 1, 2, 4 or 8 query heads");
+  constexpr int QR = side_q_rows(G);  // query rows per wave (row r: head r % G)
+  constexpr bool G8 = G == 8;         // heads 4..7 in a second set of accumulators
   constexpr bool FP8 = CK == KFP8;
   constexpr uint32_t TILE = 16 * D * (FP8 ? 1 : 2);           // one (block, KV head) tile
   constexpr int CPT = (int)TILE / 1024;                        // 1 KiB copies per tile
@@ -773,7 +775,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
   extern __shared__ __attribute__((aligned(16))) int side_lds[];
   uint8_t* ring = reinterpret_cast<uint8_t*>(side_lds);
   uint8_t* qslots = ring + kSideRingBytes;
-  int* psum = reinterpret_cast<int*>(qslots + kSideQBytes);
+  int* psum = reinterpret_cast<int*>(qslots + kSideWaves * QR * 256);
   int* scan = psum + a.num_seqs + 1;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -789,7 +791,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
   }
 
   const uint32_t ring_lds = lds_addr(ring) + wave * NS * TILE;
-  const uint32_t q_lds = lds_addr(qslots) + wave * 1024;
+  const uint32_t q_lds = lds_addr(qslots) + wave * QR * 256;
   // Per-lane global offsets of the copies; copy c lands lane l's 16 bytes at
   // byte 1024 c + 16 l of the slot, where lane l reads them:
   //  bf16 K copy c: key l%16, 16-byte chunk 4c + l/16 (the score operand of
@@ -827,10 +829,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
     const uint8_t* vcache = reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * TILE;
 
     // the group's G query heads to LDS, repeated over the 4 MFMA rows (row r
-    // holds head r % G), then the first tiles
+    // holds head r % G; groups of 8: 8 rows), then the first tiles
     wait_lgkmcnt0();
-    copy16_to_lds<true>(reinterpret_cast<const uint8_t*>(a.query) + ((size_t)qrow * a.num_heads + g * G) * D * 2,
-                        16u * (uint32_t)(lane % (16 * G)), q_lds);
+    {
+      const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.query) + ((size_t)qrow * a.num_heads + g * G) * D * 2;
+      if constexpr (G8) {
+        copy16_to_lds<true>(qsrc, 16u * lane, q_lds);
+        copy16_to_lds<true>(qsrc + 1024, 16u * lane, q_lds + 1024);
+      } else {
+        copy16_to_lds<true>(qsrc, 16u * (uint32_t)(lane % (16 * G)), q_lds);
+      }
+    }
     const int ntile = 2 * nblk;  // tile u: block blk0 + u/2, K if u is even, else V
     auto issue = [&](int u) {
       const uint8_t* src = ((u & 1) ? vcache : kcache) + (size_t)(uint32_t)bt[blk0 + (u >> 1)] * head_stride;
@@ -859,14 +868,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
       }
     };
 
-    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+    // O rows 0..3 (o0: dims 0..63, o1: 64..127) and, for groups of 8, rows
+    // 4..7 (o2, o3)
+    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f}, o2 = {0.f, 0.f, 0.f, 0.f}, o3 = {0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, lsum = 0.f;
     for (int n = 0; n < nblk; ++n) {
       const int b = blk0 + n;
       // ---- scores of block b ----
       next(2 * n);
       const uint32_t ks = ring_lds + (uint32_t)((2 * n) % NS) * TILE;
-      const uint32_t qs = q_lds + (uint32_t)((lane & 3) * 256);
+      const uint32_t qs = q_lds + (uint32_t)((lane & (QR - 1)) * 256);
       f32x4 st = {0.f, 0.f, 0.f, 0.f};
       float kscale = a.scale_log2, vscale = 1.f;
       if constexpr (FP8) {
@@ -890,7 +901,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
           st = mfma_bf16_16x16x32(kf, qf, st);
         }
       }
-      // lane's keys: b*16 + 4*(lane/16) + r, head row lane % 4
+      // lane's keys: b*16 + 4*(lane/16) + r, head row lane % QR
       const bool edge = b * 16 < lo || b * 16 + 16 > kend;
       float xs[4], lmax = -INFINITY;
 #pragma unroll
@@ -919,6 +930,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
           const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), hh));
           o0[hh] *= ah;
           o1[hh] *= ah;
+          if constexpr (G8) {
+            const float bh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 4 + hh));
+            o2[hh] *= bh;
+            o3[hh] *= bh;
+          }
         }
       }
       float p[4];
@@ -952,10 +968,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
             for (int t = 0; t < 8; ++t) vb[t] &= keep2(b * 16 + 2 * t);
           }
           f32x4& o = h ? o1 : o0;
-          o = side_pv_quad<0>(h0, h1, l0, l1, vb[0], vb[1], o);
-          o = side_pv_quad<1>(h0, h1, l0, l1, vb[2], vb[3], o);
-          o = side_pv_quad<2>(h0, h1, l0, l1, vb[4], vb[5], o);
-          o = side_pv_quad<3>(h0, h1, l0, l1, vb[6], vb[7], o);
+          o = side_pv<0>(h0, h1, l0, l1, vb[0], vb[1], o);
+          o = side_pv<4>(h0, h1, l0, l1, vb[2], vb[3], o);
+          o = side_pv<8>(h0, h1, l0, l1, vb[4], vb[5], o);
+          o = side_pv<12>(h0, h1, l0, l1, vb[6], vb[7], o);
+          if constexpr (G8) {
+            f32x4& ob = h ? o3 : o2;
+            ob = side_pv<1>(h0, h1, l0, l1, vb[0], vb[1], ob);
+            ob = side_pv<5>(h0, h1, l0, l1, vb[2], vb[3], ob);
+            ob = side_pv<9>(h0, h1, l0, l1, vb[4], vb[5], ob);
+            ob = side_pv<13>(h0, h1, l0, l1, vb[6], vb[7], ob);
+          }
         }
       } else {
 #pragma unroll
@@ -971,15 +994,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
             }
           }
           if (c == 0) {
-            o0 = side_pv_quad<0>(h0, h1, l0, l1, v0[0], v0[1], o0);
-            o1 = side_pv_quad<0>(h0, h1, l0, l1, v1[0], v1[1], o1);
-            o0 = side_pv_quad<1>(h0, h1, l0, l1, v0[2], v0[3], o0);
-            o1 = side_pv_quad<1>(h0, h1, l0, l1, v1[2], v1[3], o1);
+            o0 = side_pv<0>(h0, h1, l0, l1, v0[0], v0[1], o0);
+            o1 = side_pv<0>(h0, h1, l0, l1, v1[0], v1[1], o1);
+            o0 = side_pv<4>(h0, h1, l0, l1, v0[2], v0[3], o0);
+            o1 = side_pv<4>(h0, h1, l0, l1, v1[2], v1[3], o1);
+            if constexpr (G8) {
+              o2 = side_pv<1>(h0, h1, l0, l1, v0[0], v0[1], o2);
+              o3 = side_pv<1>(h0, h1, l0, l1, v1[0], v1[1], o3);
+              o2 = side_pv<5>(h0, h1, l0, l1, v0[2], v0[3], o2);
+              o3 = side_pv<5>(h0, h1, l0, l1, v1[2], v1[3], o3);
+            }
           } else {
-            o0 = side_pv_quad<2>(h0, h1, l0, l1, v0[0], v0[1], o0);
-            o1 = side_pv_quad<2>(h0, h1, l0, l1, v1[0], v1[1], o1);
-            o0 = side_pv_quad<3>(h0, h1, l0, l1, v0[2], v0[3], o0);
-            o1 = side_pv_quad<3>(h0, h1, l0, l1, v1[2], v1[3], o1);
+            o0 = side_pv<8>(h0, h1, l0, l1, v0[0], v0[1], o0);
+            o1 = side_pv<8>(h0, h1, l0, l1, v1[0], v1[1], o1);
+            o0 = side_pv<12>(h0, h1, l0, l1, v0[2], v0[3], o0);
+            o1 = side_pv<12>(h0, h1, l0, l1, v1[2], v1[3], o1);
+            if constexpr (G8) {
+              o2 = side_pv<9>(h0, h1, l0, l1, v0[0], v0[1], o2);
+              o3 = side_pv<9>(h0, h1, l0, l1, v1[0], v1[1], o3);
+              o2 = side_pv<13>(h0, h1, l0, l1, v0[2], v0[3], o2);
+              o3 = side_pv<13>(h0, h1, l0, l1, v1[2], v1[3], o3);
+            }
           }
         }
       }
@@ -995,8 +1030,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
       for (int hh = 0; hh < G; ++hh) {
         const float Lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(L), hh));
         const float inv = Lh > 0.f ? 1.f / Lh : 0.f;
-        op[hh * D] = f32_to_bf16(o0[hh] * inv);
-        op[hh * D + 64] = f32_to_bf16(o1[hh] * inv);
+        const float va = hh < 4 ? o0[hh & 3] : o2[hh & 3], vb = hh < 4 ? o1[hh & 3] : o3[hh & 3];
+        op[hh * D] = f32_to_bf16(va * inv);
+        op[hh * D + 64] = f32_to_bf16(vb * inv);
       }
       if (a.lse != nullptr && lane < G)
         a.lse[(size_t)qrow * a.num_heads + g * G + lane] = (m + log2f(L)) * kLn2;
@@ -1005,8 +1041,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
       float* op = a.part_o + rec * D + lane;
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        op[hh * D] = o0[hh];
-        op[hh * D + 64] = o1[hh];
+        op[hh * D] = hh < 4 ? o0[hh & 3] : o2[hh & 3];
+        op[hh * D + 64] = hh < 4 ? o1[hh & 3] : o3[hh & 3];
       }
       if (lane < G) {
         a.part_ml[(rec + lane) * 2] = m;
@@ -1019,22 +1055,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(32))) void deco
 
 bool decode_side_supported(int q_kind, int cache_kind, int head_size, int group) {
   return q_kind == KBF16 && (cache_kind == KBF16 || cache_kind == KFP8) && head_size == 128 &&
-         (group == 1 || group == 2 || group == 4);
+         (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
 template <int CK, int G>
 static hipError_t run_decode_side(const DecodeArgs& a, hipStream_t st) {
   const int grid = device_cu_count();
-  const size_t lds = decode_side_lds_bytes(a.num_seqs);
-  static std::atomic<size_t> lds_set{0};  // (per instantiation)
-  if (lds_set.load(std::memory_order_relaxed) < lds) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_side<CK, G>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
+  const size_t lds = decode_side_lds_bytes(a.num_seqs, G);
+  // the dynamic-LDS limit this instantiation was raised to, per device
+  static std::atomic<size_t> lds_set[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64 || lds_set[dev].load(std::memory_order_relaxed) < lds) {
+    e = hipFuncSetAttribute((const void*)decode_side<CK, G>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    lds_set.store(lds, std::memory_order_relaxed);
+    if (dev >= 0 && dev < 64) lds_set[dev].store(lds, std::memory_order_relaxed);
   }
   hipLaunchKernelGGL((decode_side<CK, G>), dim3(grid), dim3(256), lds, st, a);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int waves = a.num_seqs * a.num_heads;
   hipLaunchKernelGGL((decode_split_merge<128, false>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
@@ -1047,10 +1086,12 @@ hipError_t launch_decode_side(const DecodeArgs& a, int cache_kind, hipStream_t s
   if (a.split_waves < device_cu_count() * kSideWaves || a.one_per_stream) return hipErrorInvalidValue;
   const int G = a.num_heads / a.num_kv_heads;
   if (cache_kind == KBF16) {
+    if (G == 8) return run_decode_side<KBF16, 8>(a, st);
     if (G == 4) return run_decode_side<KBF16, 4>(a, st);
     if (G == 2) return run_decode_side<KBF16, 2>(a, st);
     if (G == 1) return run_decode_side<KBF16, 1>(a, st);
   } else if (cache_kind == KFP8) {
+    if (G == 8) return run_decode_side<KFP8, 8>(a, st);
     if (G == 4) return run_decode_side<KFP8, 4>(a, st);
     if (G == 2) return run_decode_side<KFP8, 2>(a, st);
     if (G == 1) return run_decode_side<KFP8, 1>(a, st);

@@ -713,7 +713,7 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
   bool beside = false;
   if (any_single && has_chunks && plan.split_waves > 0 && !plan.one_per_stream &&
       pa::decode_side_supported((int)q_dtype, (int)cache_dtype, head_size, group)) {
-    const size_t side = pa::decode_side_lds_bytes(num_seqs);
+    const size_t side = pa::decode_side_lds_bytes(num_seqs, group);
     const size_t pf = pa::prefill_lds_bytes((int)cache_dtype, head_size, group);
     const size_t cap = (size_t)pa::device_lds_per_cu();
     // more than half of a CU's LDS keeps a second decode workgroup off it

@@ -184,10 +184,10 @@ size_t prefill_lds_bytes(int cache_kind, int head_size, int group);
 // Decode of a mixed batch's one-token rows beside the prefill kernel
 // (decode_mfma.hip): one workgroup of four waves per CU, at most 64
 // registers per wave, K/V streamed through LDS; bf16 or fp8 caches, head
-// size 128, 1, 2 or 4 query heads per KV head. Uses the split plan's
+// size 128, 1, 2, 4 or 8 query heads per KV head. Uses the split plan's
 // workspace and merge; LDS bytes per workgroup for num_seqs sequences.
 bool decode_side_supported(int q_kind, int cache_kind, int head_size, int group);
-size_t decode_side_lds_bytes(int num_seqs);
+size_t decode_side_lds_bytes(int num_seqs, int group);
 hipError_t launch_decode_side(const DecodeArgs& args, int cache_kind, hipStream_t stream);
 
 }  // namespace pa

@@ -2,8 +2,8 @@
 
 pa_prefill_chunk decodes the one-token rows of a batch that also holds
 longer chunks on a second stream, next to the prefill kernel, when the
-shapes allow it (bf16 queries, bf16 or fp8 e4m3 cache, head size 128, 1, 2
-or 4 query heads per KV head, contexts long enough for the split plan, LDS
+shapes allow it (bf16 queries, bf16 or fp8 e4m3 cache, head size 128, 1, 2,
+4 or 8 query heads per KV head, contexts long enough for the split plan, LDS
 for the sequence count):
 "从静态批处理到状态化推理集群", "Chunked prefill：在共置引擎里治理阶段干扰" (a
 step mixes decode rows and prefill chunks). Every row is compared with the
@@ -79,7 +79,7 @@ CASES = [
 # the side kernel serves
 SHAPES = [(0, 32, 8, "bf16"), (1, 32, 8, "bf16"), (2, 32, 8, "bf16"), (0, 32, 8, "fp8_e4m3"),
           (1, 32, 8, "fp8_e4m3"), (2, 16, 8, "bf16"), (0, 8, 8, "fp8_e4m3"), (1, 16, 16, "bf16"),
-          (2, 16, 8, "fp8_e4m3")]
+          (2, 16, 8, "fp8_e4m3"), (0, 64, 8, "fp8_e4m3"), (1, 64, 8, "bf16")]
 
 
 @pytest.mark.parametrize("case,hq,hkv,cache", SHAPES)
