@@ -727,6 +727,7 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
     if (e == hipSuccess) e = hipEventRecord(ss->fork, hs);
     if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
     if (e != hipSuccess) return hip_status(e, "side stream fork");
+    p.nontemporal_kv = 1;
     e = pa::launch_prefill(p, (int)cache_dtype, head_size, hs);
     if (e != hipSuccess) return hip_status(e, "prefill launch");
     const hipError_t ed = pa::launch_decode_side(d, (int)cache_dtype, ss->stream);

@@ -171,6 +171,7 @@ struct PrefillArgs {
   int window;
   int num_tiles;  // grid bound on (sequence, query tile) pairs
   float scale_log2;
+  int nontemporal_kv;  // K/V copies nontemporal (set when a decode kernel runs beside)
 };
 // The chunked-prefill kernel (prefill_bf16.hip: 32x32 MFMA, bf16 scores and
 // fp16 values, direct global->LDS copies, 8 waves per workgroup) for bf16

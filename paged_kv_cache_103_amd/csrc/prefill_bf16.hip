@@ -40,11 +40,12 @@
 //    ALUs run the softmax of step i. The O^T rescale that a new running max
 //    asks for (lazy: only when the max grows by more than 2^8) is applied at
 //    the top of the next iteration, after step i-1's PV and before step i's;
-//  * K and V reach LDS by direct global->LDS copies (nontemporal: the 32
-//    tiles of a KV head read a block within microseconds of each other, and
-//    next to a decode kernel streaming other blocks the step measured ~1.5%
-//    faster), issued three steps ahead, into rings of three (K) and five (V)
-//    32-key slots, one barrier per step. A V slot is converted to fp16 in place two steps after its
+//  * K and V reach LDS by direct global->LDS copies issued three steps
+//    ahead, into rings of three (K) and five (V) 32-key slots, one barrier
+//    per step. The 32 tiles of a KV head read each block through their
+//    XCD's L2 (HBM fetches 1.00x the chunk's K/V); beside the decode kernel
+//    of a mixed batch the copies are nontemporal instead (the step ~2%
+//    faster there, at 1.33x the fetched bytes). A V slot is converted to fp16 in place two steps after its
 //    copy was issued and read by the PV product two steps later (each
 //    thread converts one 16-byte chunk). The copies place 16-byte chunks so
 //    that the MFMA operand reads hit distinct LDS banks;
@@ -252,8 +253,12 @@ prefill_bf16_kernel(PrefillArgs a) {
       // the step
       const int b = min(b0 + 2 * step + (64 * wave) / (D * E), b_last);
       const uint64_t off = (uint64_t)(uint32_t)bt[b] * head_stride;
-      copy16x2_to_lds<true>(kcache + off, cp_off[0], kring_lds + kslot * KSLOTB + 1024 * wave,
-                     vcache + off, cp_off[1], vring_lds + vslot * (2 * S::VSLOT) + 1024 * wave);
+      const uint32_t kdst = kring_lds + kslot * KSLOTB + 1024 * wave;
+      const uint32_t vdst = vring_lds + vslot * (2 * S::VSLOT) + 1024 * wave;
+      if (a.nontemporal_kv)
+        copy16x2_to_lds<true>(kcache + off, cp_off[0], kdst, vcache + off, cp_off[1], vdst);
+      else
+        copy16x2_to_lds<false>(kcache + off, cp_off[0], kdst, vcache + off, cp_off[1], vdst);
     } else {
       static_assert(CPW == 1, "one or two copies per wave");
       if (!copier) return;
@@ -264,7 +269,10 @@ prefill_bf16_kernel(PrefillArgs a) {
       // (fp8: the raw V ring turns with the K ring)
       const uint32_t vdst = FP8 ? rvring_lds + kslot * RVSLOTB : vring_lds + vslot * (2 * S::VSLOT);
       const uint32_t lds = isv ? vdst + 1024 * jj : kring_lds + kslot * KSLOTB + 1024 * jj;
-      copy16_to_lds<true>((isv ? vcache : kcache) + off, cp_off[0], lds);
+      if (a.nontemporal_kv)
+        copy16_to_lds<true>((isv ? vcache : kcache) + off, cp_off[0], lds);
+      else
+        copy16_to_lds<false>((isv ? vcache : kcache) + off, cp_off[0], lds);
     }
   };
 
