@@ -283,7 +283,7 @@ DECODE_SOURCES = ("decode_mfma.hip", "decode.hip", "pa_api.cpp", "pa_device.h", 
 PREFILL_SOURCES = ("prefill_bf16.hip", "prefill_tiles.h", "decode_mfma.hip", "decode.hip", "reshape_and_cache.hip",
                    "pa_api.cpp", "pa_device.h", "pa_internal.h")
 MLA_SOURCES = ("mla_decode.hip", "pa_api.cpp", "pa_device.h", "pa_internal.h")
-SPARSE_SOURCES = ("sparse_select.hip", "decode_mfma.hip", "decode.hip", "pa_api.cpp", "pa_device.h", "pa_internal.h")
+SPARSE_SOURCES = ("sparse_select.hip", "sparse_pick.h", "decode_mfma.hip", "decode.hip", "pa_api.cpp", "pa_device.h", "pa_internal.h")
 SOURCES_OF = {"fp8_decode": DECODE_SOURCES, "llama8b_decode": DECODE_SOURCES, "llama8b_decode_valu": DECODE_SOURCES,
               "agentic_decode": DECODE_SOURCES,
               "agentic_decode_shared_prefix": DECODE_SOURCES, "fp8_swa128": DECODE_SOURCES,
@@ -579,8 +579,8 @@ def measure(name, pa, torch, W, args, flush):
         nbytes = sparse_kv_bytes(b, choice)
         res.update(timing=t, kv_bytes_per_call=nbytes, dense_kv_bytes=b.kv_bytes_read(),
                    roofline=hbm_roofline(nbytes, t["median_ms"], name,
-                                         "pa_decode_sparse: sparse_select_kernel + decode_mfma_split + "
-                                         "decode_split_merge"))
+                                         "pa_decode_sparse: decode_sparse_fused (selection, decode and merge "
+                                         "in one launch)"))
         res["value"], res["unit"] = res["roofline"]["achieved"], "GB/s"
         if cpu:
             res["cpu_baseline"] = cpu_baseline(sparse_units(b, choice), budget, "GB/s",

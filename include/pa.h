@@ -254,6 +254,12 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_ca
  *   beyond: the block bitmap lives in 64 KiB of LDS). The workspace must
  *   hold pa_decode_sparse_workspace_bytes(...) bytes: it keeps the compacted
  *   block table ([num_seqs][max_selected + 1] int32) the decode then reads.
+ * Launches: with bf16/fp8 caches, max_selected < 1024 and at least two
+ *   (sequence, KV head) pairs per compute unit, one kernel selects, decodes
+ *   and merges (a workgroup per pair; the workspace is then left untouched);
+ *   otherwise a selection kernel writes the compacted tables and pa_decode's
+ *   kernels follow. Either way the result is the one defined above (the
+ *   rounding order of the merge differs between the two).
  */
 pa_status pa_decode_sparse(void* out, const void* query, const void* k_cache, const void* v_cache,
                            const float* k_scale, const float* v_scale, const int32_t* block_table,

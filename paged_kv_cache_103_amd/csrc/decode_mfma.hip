@@ -31,6 +31,7 @@
 
 #include "pa_device.h"
 #include "pa_internal.h"
+#include "sparse_pick.h"
 
 namespace pa {
 
@@ -267,26 +268,42 @@ __device__ __forceinline__ void wave_write(WaveAcc<D>& acc, const DecodeArgs& a,
   }
 }
 
+// Physical block ids of a stream, uniform over the wave. From a block-table
+// row in global memory: scalar loads through the constant address space (a
+// vector load would make the compiler wait for every outstanding K/V load
+// before using the id).
+struct TableIds {
+  const int* bt;
+  __device__ __forceinline__ int operator()(int i) const {
+    typedef __attribute__((address_space(4))) const int cint;
+    return ((const cint*)bt)[i];
+  }
+};
+// From a table in LDS (byte address `base`): LDS reads count on their own
+// counter, so they do not make the K/V loads wait either.
+struct LdsIds {
+  uint32_t base;
+  __device__ __forceinline__ int operator()(int i) const {
+    typedef __attribute__((address_space(3))) const int lint;
+    return __builtin_amdgcn_readfirstlane(*(const lint*)(uintptr_t)(base + 4u * (uint32_t)i));
+  }
+};
+
 // The blocks [b, blk1) of one stream segment, in pairs, with the next pair's
 // loads in flight while one is computed. Only the first pair (a window
 // start) and the last (context or segment end) can need masks; the pairs in
 // between run in a loop whose loads are unconditional, so that the compiler
 // keeps one pair's loads outstanding across the other's arithmetic.
-template <int CK, int D>
+template <int CK, int D, typename Ids = TableIds>
 __device__ __forceinline__ void wave_blocks(WaveAcc<D>& acc, const u32x4* qf, const uint8_t* kcache,
-                                            const uint8_t* vcache, const int* bt, int b, int blk1, int lo,
+                                            const uint8_t* vcache, Ids id_of, int b, int blk1, int lo,
                                             int ctx, size_t head_stride, const DecodeArgs& a, int c16, int q4) {
   const int np = (blk1 - b + 1) >> 1;
   if (np <= 0) return;
-  // block ids are uniform over the wave and read-only here: scalar loads
-  // through the constant address space (a vector load would make the
-  // compiler wait for every outstanding K/V load before using the id)
-  typedef __attribute__((address_space(4))) const int cint;
-  const cint* btc = (const cint*)(bt);
   auto ids = [&](int n, size_t& p0, size_t& p1) {
     const int bb = b + 2 * n;
-    p0 = (size_t)btc[bb];
-    p1 = (bb + 1 < blk1) ? (size_t)btc[bb + 1] : p0;
+    p0 = (size_t)id_of(bb);
+    p1 = (bb + 1 < blk1) ? (size_t)id_of(bb + 1) : p0;
   };
   auto run = [&](const PairRegs<CK, D>& r, size_t p0, size_t p1, int n) {
     const int bb = b + 2 * n;
@@ -501,7 +518,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         load_query<CK, D>(qf, a, qrow, g, G, c16, q4, G);
         wave_blocks<CK, D>(acc, qf, reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)g * S::TILE,
                            reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * S::TILE,
-                           a.block_table + (size_t)s * a.bt_stride, lo >> 4, (lo >> 4) + nb, lo, ctx,
+                           TableIds{a.block_table + (size_t)s * a.bt_stride}, lo >> 4, (lo >> 4) + nb, lo, ctx,
                            (size_t)H * S::TILE, a, c16, q4);
       }
       wave_write<D>(acc, a, 0, qrow, g, G, true, c16, q4, G);  // an empty range: zeros, lse -inf
@@ -560,8 +577,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int blk1 = (lo >> 4) + (int)(seg_end - sstart);
       const int kend = min(ctx, blk1 * 16);
       load_query<CK, D>(qf, a, qrow, g, G, c16, q4, G);
-      wave_blocks<CK, D>(acc, qf, kcache, vcache, a.block_table + (size_t)s * a.bt_stride, blk0, blk1, lo, kend,
-                         head_stride, a, c16, q4);
+      wave_blocks<CK, D>(acc, qf, kcache, vcache, TableIds{a.block_table + (size_t)s * a.bt_stride}, blk0, blk1,
+                         lo, kend, head_stride, a, c16, q4);
       const bool single = !grouped && (sstart / C) == ((sstart + nb - 1) / C);
       wave_write<D>(acc, a, slot, qrow, g, G, single, c16, q4, G);
     } else {
@@ -577,8 +594,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int blk0 = (int)(x - sstart);
       const int blk1 = (int)(seg_end - sstart);
       load_query<CK, D>(qf, a, m0, g, G, c16, q4, nmem * G);
-      wave_blocks<CK, D>(acc, qf, kcache, vcache, a.block_table + (size_t)first * a.bt_stride, blk0, blk1, 0,
-                         blk1 * 16, head_stride, a, c16, q4);
+      wave_blocks<CK, D>(acc, qf, kcache, vcache, TableIds{a.block_table + (size_t)first * a.bt_stride}, blk0,
+                         blk1, 0, blk1 * 16, head_stride, a, c16, q4);
       wave_write<D>(acc, a, slot, 0, g, G, false, c16, q4, nmem * G);
     }
     x = seg_end;
@@ -704,6 +721,127 @@ static hipError_t run_decode_mfma_kind(const DecodeArgs& a, int cache_kind, int 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int cache_kind, int head_size, hipStream_t st) {
   return a.num_groups > 0 ? run_decode_mfma_kind<true>(a, cache_kind, head_size, st)
                           : run_decode_mfma_kind<false>(a, cache_kind, head_size, st);
+}
+
+// ---------------------------------------------------------------------------
+// Sparse decode in one launch (many streams, short lists)
+// ---------------------------------------------------------------------------
+// Sparse attention reads only the blocks an indexer ranks highest ("宣稱省下
+// 106 倍成本…", "背景：什麼是稀疏注意力"), one list per sequence for all of its
+// heads. With at least two (sequence, KV head) streams per CU, each stream
+// gets a workgroup of its own, which
+//  * turns the sequence's list into its distinct blocks in ascending logical
+//    order, the newest block always last (an LDS bitmap drops repeats and
+//    ids outside [0, newest block); each first setter appends its block to
+//    a list and every listed block goes to its rank among them), and looks
+//    up their physical ids into a table in LDS;
+//  * splits that table evenly over its 4 waves, which walk their parts with
+//    the loop of the split kernel above (block ids read from the LDS table);
+//  * merges the 4 waves' (max, sum, unnormalised output) summaries in LDS,
+//    exactly as the merge kernel does, and writes the output rows.
+// So the selection, the decode and the merge are one launch, with no
+// workspace. The computation is that of the selection kernel followed by the
+// split plan, up to where the stream is cut into segments.
+template <int CK, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_sparse_fused(
+    DecodeArgs a, SparseSelectArgs sa) {
+  using S = MfmaDecodeShape<CK, D>;
+  // LDS: [bitmap words_max][list max_selected + 1][table max_selected + 1];
+  // after the walk, the same bytes hold the waves' summaries
+  extern __shared__ int lds[];
+  __shared__ int nlisted;
+  unsigned int* bits = reinterpret_cast<unsigned int*>(lds);
+  int* listed = lds + sa.words_max;
+  int* tbl = listed + sa.max_selected + 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, q4 = lane >> 4;
+  const int H = a.num_kv_heads, G = a.num_heads / H;
+  const int s = blockIdx.x / H, g = blockIdx.x % H;
+  u32x4 qf[S::DS];
+  load_query<CK, D>(qf, a, s, g, G, c16, q4, G);  // in flight during the selection
+
+  const int ctx = a.context_lens[s];
+  const int nbk = min(ctx > 0 ? (ctx + 15) >> 4 : 0, sa.blocks_max);
+  const int m = sparse_mark(sa, s, nbk, bits, listed, &nlisted);
+  sparse_rank(listed, m, sa.block_table + (size_t)s * sa.bt_stride, tbl);
+  __syncthreads();
+  const int keys = sparse_keys(m, ctx, nbk);
+
+  // this wave's part of the stream: whole pairs, the last part shorter
+  const int per = (((m + 3) >> 2) + 1) & ~1;
+  const int blk0 = min(m, wave * per), blk1 = min(m, blk0 + per);
+  WaveAcc<D> acc;
+#pragma unroll
+  for (int dt = 0; dt < S::DT; ++dt) acc.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  acc.m = -INFINITY;
+  acc.lsum = 0.f;
+  wave_blocks<CK, D>(acc, qf, reinterpret_cast<const uint8_t*>(a.k_cache) + (size_t)g * S::TILE,
+                     reinterpret_cast<const uint8_t*>(a.v_cache) + (size_t)g * S::TILE, LdsIds{lds_addr(tbl)}, blk0,
+                     blk1, 0, min(keys, blk1 * 16), (size_t)H * S::TILE, a, c16, q4);
+  const float L = strided_sum<16>(acc.lsum);
+  __syncthreads();  // every wave is done with the table
+
+  // summaries: o [4][G][D], then max [4][G] and sum [4][G]
+  float* mo = reinterpret_cast<float*>(lds);
+  float* mm = mo + 4 * G * D;
+  float* ml = mm + 4 * G;
+  if (c16 < G) {
+    float* op = mo + (size_t)(wave * G + c16) * D + 4 * q4;
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) *reinterpret_cast<f32x4*>(op + dt * 16) = acc.o[dt];
+    if (q4 == 0) {
+      mm[wave * G + c16] = acc.m;
+      ml[wave * G + c16] = L;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int c = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mm[w * G + c]);
+    float sum = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = mm[w * G + c];
+      const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);  // a wave without keys adds nothing
+      sum += ml[w * G + c] * wt;
+      o += mo[(size_t)(w * G + c) * D + d] * wt;
+    }
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;  // no keys at all: zeros
+    const size_t row = (size_t)s * a.num_heads + g * G + c;
+    reinterpret_cast<uint16_t*>(a.out)[row * D + d] = f32_to_bf16(o * inv);
+    if (a.lse != nullptr && d == 0) a.lse[row] = (M + log2f(sum)) * kLn2;
+  }
+}
+
+size_t decode_sparse_fused_lds_bytes(int words_max, int max_selected, int group, int head_size) {
+  if (max_selected < 0 || max_selected >= kSparseRankMax || group < 1 || group > 16 || words_max < 0) return 0;
+  const size_t pick = ((size_t)words_max + 2 * (size_t)(max_selected + 1)) * sizeof(int);
+  const size_t merge = (size_t)4 * group * (head_size + 2) * sizeof(float);
+  const size_t need = std::max(pick, merge);
+  return need + 16 <= kSparseMaxLds ? need : 0;  // (+ the static list counter)
+}
+
+template <int CK, int D>
+static hipError_t run_decode_sparse_fused(const DecodeArgs& a, const SparseSelectArgs& sa, size_t lds,
+                                          hipStream_t st) {
+  const unsigned grid = (unsigned)((long long)a.num_seqs * a.num_kv_heads);
+  hipLaunchKernelGGL((decode_sparse_fused<CK, D>), dim3(grid), dim3(256), lds, st, a, sa);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_sparse_fused(const DecodeArgs& a, const SparseSelectArgs& sa, int cache_kind,
+                                      int head_size, hipStream_t st) {
+  const size_t lds = decode_sparse_fused_lds_bytes(sa.words_max, sa.max_selected, a.num_heads / a.num_kv_heads,
+                                                   head_size);
+  if (lds == 0 || a.num_seqs <= 0) return hipErrorInvalidValue;
+  if (cache_kind == KBF16 && head_size == 128) return run_decode_sparse_fused<KBF16, 128>(a, sa, lds, st);
+  if (cache_kind == KBF16 && head_size == 64) return run_decode_sparse_fused<KBF16, 64>(a, sa, lds, st);
+  if (cache_kind == KFP8 && head_size == 128) return run_decode_sparse_fused<KFP8, 128>(a, sa, lds, st);
+  if (cache_kind == KFP8 && head_size == 64) return run_decode_sparse_fused<KFP8, 64>(a, sa, lds, st);
+  return hipErrorInvalidValue;
 }
 
 

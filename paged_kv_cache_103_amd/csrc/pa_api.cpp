@@ -589,12 +589,9 @@ pa_status pa_decode_sparse(void* out, const void* query, const void* k_cache, co
   sa.eff_ctx = reinterpret_cast<int*>(ws + align256((size_t)num_seqs * (size_t)(max_selected + 1) * sizeof(int)));
   sa.rank_list = pa::sparse_select_lds_bytes(max_context_len, max_selected) >
                  pa::sparse_select_lds_bytes(max_context_len, pa::kSparseRankMax);
-  hipError_t e = pa::launch_sparse_select(sa, num_seqs, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_status(e, "sparse block selection launch");
 
   const int32_t eff_max = 16 * (max_selected + 1);
   const pa::DecodePlan plan = make_plan(num_seqs, eff_max, num_heads, num_kv_heads, head_size, cache_dtype, 0);
-  const size_t dec_need = pa::decode_workspace_bytes(plan, num_seqs, num_heads, num_kv_heads, head_size);
   pa::DecodeArgs a{};
   a.out = out;
   a.query = query;
@@ -602,17 +599,31 @@ pa_status pa_decode_sparse(void* out, const void* query, const void* k_cache, co
   a.v_cache = v_cache;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
-  a.block_table = sa.cbt;
-  a.context_lens = sa.eff_ctx;
   a.cu_seqlens = nullptr;
-  bind_workspace(a, plan, dec_need ? ws + sparse_table_bytes(num_seqs, max_selected) : nullptr,
-                 num_seqs, num_heads, num_kv_heads, head_size);
-  a.bt_stride = sa.cbt_stride;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;
   a.window = 0;
   a.scale_log2 = scale * 1.4426950408889634f;
+  // Two or more streams per CU and a short list on the matrix-core kernel:
+  // one launch (a workgroup per stream selects, decodes and merges).
+  if (plan.split_waves > 0 && (long long)num_seqs * num_kv_heads >= 2LL * pa::device_cu_count() &&
+      pa::decode_sparse_fused_lds_bytes(sa.words_max, max_selected, num_heads / num_kv_heads, head_size) > 0) {
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.bt_stride = block_table_stride;
+    bind_workspace(a, plan, nullptr, num_seqs, num_heads, num_kv_heads, head_size);
+    hipError_t e = pa::launch_decode_sparse_fused(a, sa, (int)cache_dtype, head_size, (hipStream_t)stream);
+    return hip_status(e, "sparse decode launch");
+  }
+  hipError_t e = pa::launch_sparse_select(sa, num_seqs, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "sparse block selection launch");
+  const size_t dec_need = pa::decode_workspace_bytes(plan, num_seqs, num_heads, num_kv_heads, head_size);
+  a.block_table = sa.cbt;
+  a.context_lens = sa.eff_ctx;
+  bind_workspace(a, plan, dec_need ? ws + sparse_table_bytes(num_seqs, max_selected) : nullptr,
+                 num_seqs, num_heads, num_kv_heads, head_size);
+  a.bt_stride = sa.cbt_stride;
   e = pa::launch_decode(a, (int)q_dtype, (int)cache_dtype, head_size, (hipStream_t)stream);
   return hip_status(e, "sparse decode launch");
 }

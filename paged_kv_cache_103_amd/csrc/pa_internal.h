@@ -128,6 +128,14 @@ constexpr size_t kSparseMaxLds = 64 * 1024;  // bitmap + scan (+ list): contexts
 // max_selected < kSparseRankMax and it fits kSparseMaxLds (then it is used).
 size_t sparse_select_lds_bytes(int max_context_len, int max_selected);
 hipError_t launch_sparse_select(const SparseSelectArgs& a, int num_seqs, hipStream_t stream);
+// Selection, decode and merge in one launch (matrix-core kernel, a workgroup
+// per (sequence, KV head)): its LDS bytes, 0 when the shape is not served
+// (lists of kSparseRankMax entries or more, more than 16 heads per KV head,
+// or more than kSparseMaxLds).
+size_t decode_sparse_fused_lds_bytes(int words_max, int max_selected, int group, int head_size);
+// `a` carries the caller's block table and context lengths; no workspace.
+hipError_t launch_decode_sparse_fused(const DecodeArgs& a, const SparseSelectArgs& sa, int cache_kind,
+                                      int head_size, hipStream_t stream);
 
 // Decode over a paged latent (MLA) cache: [num_blocks][16][head_dim_k] bf16
 // rows shared by all heads; values are the rows' first 512 elements.

@@ -1,25 +1,21 @@
-// Sparse decode, first kernel (pa_decode_sparse, include/pa.h): turns each
-// sequence's list of chosen logical blocks into a compact block table of the
-// physical blocks it will read, in ascending logical order, with the newest
-// block always last, and the number of keys that leaves. The decode kernels
-// then run on that table unchanged: positions are already encoded in Q and K,
-// so only which keys are read matters, and every chosen key precedes the
-// query. Sparse attention reads only the top-k positions an indexer picks
-// ("宣稱省下 106 倍成本…", "背景：什麼是稀疏注意力"), so the bytes read stop growing
-// with the context (DeepSeek-V4.1 write-up, "三、第二招：把能合的内核全合成一个",
-// sparse MQA logits).
+// Sparse decode's selection kernel (pa_decode_sparse, include/pa.h), the
+// first of three launches when the one-launch kernel does not serve the call:
+// turns each sequence's list of chosen logical blocks into a compact block
+// table of the physical blocks it will read, in ascending logical order with
+// the newest block last, and the number of keys that leaves. The decode
+// kernels then run on that table unchanged: positions are already encoded in
+// Q and K, so only which keys are read matters, and every chosen key precedes
+// the query. The bytes read stop growing with the context (DeepSeek-V4.1
+// write-up, "三、第二招：把能合的内核全合成一个", sparse MQA logits).
 //
-// One workgroup per sequence. The chosen entries set bits of a per-sequence
-// bitmap of its logical blocks in LDS (so order and repeats do not matter,
-// and entries outside [0, newest block) are dropped). With short lists (at
-// most kSparseRankMax entries, the usual top-k sizes) the entry that sets a
-// bit first also appends its block to a list in LDS, and each listed block
-// goes to its rank among them: no scan over the bitmap's words. Longer lists
-// compact the set bits in ascending order by a workgroup scan of per-word
-// popcounts.
+// One workgroup per sequence; the marking and the ranking of short lists
+// are sparse_pick.h's. Longer lists (kSparseRankMax entries or more) are
+// compacted from the bitmap in ascending order by a workgroup scan of
+// per-word popcounts.
 #include <hip/hip_runtime.h>
 
 #include "pa_internal.h"
+#include "sparse_pick.h"
 
 namespace pa {
 
@@ -33,36 +29,16 @@ __global__ __launch_bounds__(256) void sparse_select_kernel(SparseSelectArgs a) 
   const int nbk = min(ctx > 0 ? (ctx + 15) >> 4 : 0, a.blocks_max);
   const int W = (nbk + 31) >> 5;
   const bool short_list = a.rank_list != 0;
-  for (int w = tid; w < W; w += 256) lds_bits[w] = 0u;
-  if (tid == 0) nlisted = 0;
-  __syncthreads();
+  const int m = sparse_mark(a, s, nbk, lds_bits, short_list ? listed : nullptr, &nlisted);
   if (nbk == 0) {  // uniform over the workgroup
     if (tid == 0) a.eff_ctx[s] = 0;
     return;
   }
-  const int n = min(max(a.num_selected != nullptr ? a.num_selected[s] : 0, 0), a.max_selected);
-  const int* sel = a.selected + (size_t)s * a.sel_stride;
-  for (int i = tid; i <= n; i += 256) {
-    // entry n stands for the newest block, always read
-    const int e = i < n ? sel[i] : nbk - 1;
-    if (e >= 0 && (e < nbk - 1 || i == n)) {
-      const unsigned int bit = 1u << (e & 31);
-      const unsigned int old = atomicOr(&lds_bits[e >> 5], bit);
-      if (short_list && !(old & bit)) listed[atomicAdd(&nlisted, 1)] = e;
-    }
-  }
-  __syncthreads();
   const int* bt = a.block_table + (size_t)s * a.bt_stride;
   int* out = a.cbt + (size_t)s * a.cbt_stride;
   if (short_list) {
-    const int m = nlisted;  // distinct blocks, the newest included
-    for (int j = tid; j < m; j += 256) {
-      const int v = listed[j];
-      int rank = 0;
-      for (int k = 0; k < m; ++k) rank += listed[k] < v;
-      out[rank] = bt[v];
-    }
-    if (tid == 0) a.eff_ctx[s] = 16 * (m - 1) + min(16, ctx - 16 * (nbk - 1));
+    sparse_rank(listed, m, bt, out);
+    if (tid == 0) a.eff_ctx[s] = sparse_keys(m, ctx, nbk);
     return;
   }
   int base = 0;
@@ -79,11 +55,11 @@ __global__ __launch_bounds__(256) void sparse_select_kernel(SparseSelectArgs a) 
       __syncthreads();
     }
     int pos = base + scan[tid] - c;
-    for (unsigned int m = v; m != 0u; m &= m - 1u) out[pos++] = bt[w * 32 + __builtin_ctz(m)];
+    for (unsigned int left = v; left != 0u; left &= left - 1u) out[pos++] = bt[w * 32 + __builtin_ctz(left)];
     base += scan[255];
     __syncthreads();
   }
-  if (tid == 0) a.eff_ctx[s] = 16 * (base - 1) + min(16, ctx - 16 * (nbk - 1));
+  if (tid == 0) a.eff_ctx[s] = sparse_keys(base, ctx, nbk);
 }
 
 size_t sparse_select_lds_bytes(int max_context_len, int max_selected) {

@@ -5,8 +5,9 @@ NaN, so reading any of them shows in the output. Cases: ragged contexts
 (1 token to several thousand), GQA groups 1..16, d 64/128, bf16 and fp8
 caches, lists with repeats, out-of-range ids, the newest block itself, and a
 tail past num_selected naming unchosen blocks; the empty choice; every
-block chosen (bitwise equal to pa_decode); and the benchmark's long-context
-batch on sampled sequences.
+block chosen (bitwise equal to pa_decode); batches of many streams, which
+one launch serves; and the benchmark's long-context batch on sampled
+sequences.
 """
 
 import numpy as np
@@ -125,6 +126,45 @@ def test_sparse_every_block_is_dense_decode_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), dense.view(torch.int16))
     check(b, choice, out, [0, 3], "sparse every block")
+
+
+FUSED_CASES = [
+    # (sequences, context range, k blocks, Hq, Hkv, D, cache dtype): at least
+    # two (sequence, KV head) streams per CU, so one launch serves the call
+    (64, (1, 6000), 40, 32, 8, 128, "bf16"),
+    (128, (1, 3000), 25, 8, 4, 64, "fp8_e4m3"),
+    (512, (1, 1200), 10, 16, 1, 128, "bf16"),         # G = 16
+    (256, (100, 4000), 60, 16, 2, 128, "fp8_e4m3"),   # G = 8
+    (600, (1, 400), 3, 1, 1, 64, "bf16"),             # G = 1, ragged grid
+    (64, (20000, 40000), 300, 32, 8, 128, "bf16"),    # long lists (parts of ~80 blocks)
+]
+
+
+@pytest.mark.parametrize("case", range(len(FUSED_CASES)))
+def test_sparse_one_launch(case):
+    """Batches with many streams take the one-launch kernel (selection,
+    decode and merge in a workgroup per stream), which leaves the workspace
+    untouched: checked, then every sequence against the oracle."""
+    S, (c0, c1), k, Hq, Hkv, D, cd = FUSED_CASES[case]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if S * Hkv < 2 * cus:
+        pytest.skip(f"{S * Hkv} streams are fewer than two per CU on this device ({cus} CUs)")
+    rng = np.random.default_rng(2600 + case)
+    ctx = rng.integers(c0, c1 + 1, S).tolist()
+    _log(f"sparse one-launch case {case}: {S} seqs, ctx {c0}..{c1}, k {k}, {Hq}/{Hkv} d{D} {cd}")
+    b, choice = W.make_sparse_batch(f"sparse_fused{case}", 2600 + case, ctx, k, Hq, Hkv, D, "bf16", cd, device=DEV,
+                                    noise=True)
+    m = b.meta(DEV)
+    c = choice.device(DEV)
+    ms = choice.selected.shape[1]
+    ws = torch.full((pa.decode_sparse_workspace_bytes(S, ms, Hq, Hkv, D, b.cache_dtype),), 0xA5, dtype=torch.uint8,
+                    device=DEV)
+    out = torch.empty_like(b.query)
+    pa.decode_sparse(out, b.query, b.k_cache, b.v_cache, m["block_table"], m["context_lens"], b.max_context_len,
+                     c["selected"], c["num_selected"], b.scale, b.k_scale, b.v_scale, ws)
+    torch.cuda.synchronize()
+    assert bool((ws == 0xA5).all()), "the one-launch path writes no workspace"
+    check(b, choice, out, range(S), f"sparse one-launch case {case}")
 
 
 def test_sparse_long_context_sampled():
