@@ -137,6 +137,7 @@ FUSED_CASES = [
     (256, (100, 4000), 60, 16, 2, 128, "fp8_e4m3"),   # G = 8
     (600, (1, 400), 3, 1, 1, 64, "bf16"),             # G = 1, ragged grid
     (64, (20000, 40000), 300, 32, 8, 128, "bf16"),    # long lists (parts of ~80 blocks)
+    (512, (1, 3000), 0, 8, 1, 128, "bf16"),           # nothing chosen: the newest block (and noise) only
 ]
 
 
@@ -165,6 +166,30 @@ def test_sparse_one_launch(case):
     torch.cuda.synchronize()
     assert bool((ws == 0xA5).all()), "the one-launch path writes no workspace"
     check(b, choice, out, range(S), f"sparse one-launch case {case}")
+
+
+def test_sparse_many_streams_long_lists_take_three_launches():
+    """Lists of 1024 entries or more are not served in one launch even with
+    many streams: the selection kernel writes its tables to the workspace
+    (checked) and the result still matches the oracle."""
+    S = 64
+    rng = np.random.default_rng(2700)
+    ctx = rng.integers(20000, 30000, S).tolist()
+    b, choice = W.make_sparse_batch("sparse_long_lists", 2700, ctx, 1100, 32, 8, 128, "bf16", "bf16", device=DEV,
+                                    noise=True)
+    ms = choice.selected.shape[1]
+    assert ms >= 1024
+    _log(f"sparse long lists: {S} seqs, max_selected {ms}")
+    m = b.meta(DEV)
+    c = choice.device(DEV)
+    ws = torch.full((pa.decode_sparse_workspace_bytes(S, ms, 32, 8, 128, b.cache_dtype),), 0xA5, dtype=torch.uint8,
+                    device=DEV)
+    out = torch.empty_like(b.query)
+    pa.decode_sparse(out, b.query, b.k_cache, b.v_cache, m["block_table"], m["context_lens"], b.max_context_len,
+                     c["selected"], c["num_selected"], b.scale, b.k_scale, b.v_scale, ws)
+    torch.cuda.synchronize()
+    assert not bool((ws == 0xA5).all()), "the three-launch path keeps its tables in the workspace"
+    check(b, choice, out, [0, 21, 42, 63], "sparse long lists")
 
 
 def test_sparse_long_context_sampled():
