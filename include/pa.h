@@ -130,6 +130,10 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
  * Supported: block_size 16; head_size 64 or 128; num_heads / num_kv_heads in
  *   {1, 2, 4, 8, 16}; (q, cache) dtypes (F32, F32), (BF16, BF16),
  *   (BF16, FP8_E4M3).
+ * Batches of more than 16000 sequences over bf16/fp8 caches run as
+ *   consecutive launches over groups of 16000 (the matrix-core kernel keeps
+ *   per-sequence prefix sums in LDS), reusing one workspace; the workspace
+ *   size is that of one group.
  */
 pa_status pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
                     const float* k_scale, const float* v_scale, const int32_t* block_table,
@@ -326,8 +330,11 @@ pa_status pa_merge_partials(void* out, float* lse_out, const void* parts, const 
  *   take part in the scores only, such as a positional part).
  * query: bf16 [num_seqs][num_heads][head_dim_k]; out: bf16
  *   [num_seqs][num_heads][512]; head_dim_v must be 512.
- * num_heads: 16, 32, 64 or 128; num_seqs at most 2048; context_lens[s] >= 1.
- * workspace: pa_mla_decode_workspace_bytes(num_seqs, num_heads) bytes.
+ * num_heads: 16, 32, 64 or 128; context_lens[s] >= 1. Batches of more than
+ *   2048 sequences run as consecutive launches over groups of 2048 (the
+ *   kernels keep per-sequence prefix sums in LDS), reusing one workspace.
+ * workspace: pa_mla_decode_workspace_bytes(num_seqs, num_heads) bytes (the
+ *   size for min(num_seqs, 2048) sequences).
  * Numerics: scores on bf16 matrix cores with fp32 accumulation. With 16
  *   heads the weighted sum multiplies the bf16 rows by the weights split
  *   into bf16 hi + lo (16 significant bits). With more heads the rows'

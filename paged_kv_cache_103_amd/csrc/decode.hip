@@ -484,11 +484,12 @@ DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num
   DecodePlan plan{};
   const int G = std::max(1, num_heads / std::max(1, num_kv_heads));
   // (the matrix-core kernel keeps per-sequence prefix sums in LDS: up to
-  // 16000 sequences per call; larger batches take the VALU kernel)
+  // kMfmaMaxSeqs sequences per launch; pa_decode splits larger batches, other
+  // callers' larger batches take the VALU kernel)
   int max_blocks = (max_context_len + 15) / 16;
   if (sliding_window > 0) max_blocks = std::min(max_blocks, (sliding_window + 15) / 16 + 1);
   if (max_blocks < 1) max_blocks = 1;
-  if (!force_valu && decode_uses_mfma(q_kind, cache_kind, G) && num_seqs <= 16000) {
+  if (!force_valu && decode_uses_mfma(q_kind, cache_kind, G) && num_seqs <= kMfmaMaxSeqs) {
     // two resident workgroups of four waves per CU
     plan.split_waves = 8 * device_cu_count();
     plan.pb = 0;

@@ -213,13 +213,25 @@ static void bind_workspace(pa::DecodeArgs& a, const pa::DecodePlan& plan, void* 
   }
 }
 
+// Sequences per launch of pa_decode: batches the matrix-core kernel serves
+// run as consecutive launches over groups of at most kMfmaMaxSeqs sequences
+// (sequences are independent), each reusing the same workspace.
+static int32_t decode_group_seqs(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, pa_dtype cache_dtype,
+                                 bool force_valu) {
+  const int q_kind = cache_dtype == PA_F32 ? PA_F32 : PA_BF16;
+  const int G = std::max(1, num_heads / std::max(1, num_kv_heads));
+  if (!force_valu && pa::decode_uses_mfma(q_kind, (int)cache_dtype, G)) return std::min(num_seqs, pa::kMfmaMaxSeqs);
+  return num_seqs;
+}
+
 static size_t decode_ws_bytes(int32_t num_seqs, int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
                               int32_t head_size, pa_dtype cache_dtype, int32_t sliding_window, bool force_valu) {
   if (num_seqs <= 0 || max_context_len <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0)
     return 0;
-  const pa::DecodePlan plan = make_plan(num_seqs, max_context_len, num_heads, num_kv_heads, head_size,
-                                        cache_dtype, sliding_window, force_valu);
-  return pa::decode_workspace_bytes(plan, num_seqs, num_heads, num_kv_heads, head_size);
+  const int32_t n = decode_group_seqs(num_seqs, num_heads, num_kv_heads, cache_dtype, force_valu);
+  const pa::DecodePlan plan = make_plan(n, max_context_len, num_heads, num_kv_heads, head_size, cache_dtype,
+                                        sliding_window, force_valu);
+  return pa::decode_workspace_bytes(plan, n, num_heads, num_kv_heads, head_size);
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
@@ -264,35 +276,42 @@ static pa_status decode_impl(void* out, float* lse, const void* query, const voi
     g_last_error.clear();
     return PA_OK;
   }
-  const pa::DecodePlan plan = make_plan(num_seqs, max_context_len, num_heads, num_kv_heads, head_size,
+  const int32_t group = decode_group_seqs(num_seqs, num_heads, num_kv_heads, cache_dtype, force_valu);
+  const pa::DecodePlan plan = make_plan(group, max_context_len, num_heads, num_kv_heads, head_size,
                                         cache_dtype, sliding_window, force_valu);
   if (lse != nullptr && plan.split_waves <= 0)
     return fail(PA_ERR_UNSUPPORTED, "partial decode needs the matrix-core kernel (bf16 queries, bf16 or fp8 "
-                "cache, at most 16000 sequences)");
-  const size_t need = pa::decode_workspace_bytes(plan, num_seqs, num_heads, num_kv_heads, head_size);
+                "cache)");
+  const size_t need = pa::decode_workspace_bytes(plan, group, num_heads, num_kv_heads, head_size);
   if (workspace_bytes < need || (need > 0 && workspace == nullptr))
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes (got %zu)", need,
                 workspace_bytes);
-  pa::DecodeArgs a{};
-  a.out = out;
-  a.query = query;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
-  a.block_table = block_table;
-  a.context_lens = context_lens;
-  a.cu_seqlens = nullptr;
-  bind_workspace(a, plan, need ? workspace : nullptr, num_seqs, num_heads, num_kv_heads, head_size);
-  a.bt_stride = block_table_stride;
-  a.num_seqs = num_seqs;
-  a.num_heads = num_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.window = sliding_window;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.lse = lse;
-  hipError_t e = pa::launch_decode(a, (int)q_dtype, (int)cache_dtype, head_size, (hipStream_t)stream);
-  return hip_status(e, "decode launch");
+  const size_t row_bytes = (size_t)num_heads * head_size * elem_bytes(q_dtype);  // a query / output row
+  for (int32_t s0 = 0; s0 < num_seqs; s0 += group) {
+    const int32_t n = std::min(group, num_seqs - s0);
+    pa::DecodeArgs a{};
+    a.out = static_cast<char*>(out) + (size_t)s0 * row_bytes;
+    a.query = static_cast<const char*>(query) + (size_t)s0 * row_bytes;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_table = block_table + (size_t)s0 * block_table_stride;
+    a.context_lens = context_lens + s0;
+    a.cu_seqlens = nullptr;
+    bind_workspace(a, plan, need ? workspace : nullptr, n, num_heads, num_kv_heads, head_size);
+    a.bt_stride = block_table_stride;
+    a.num_seqs = n;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.window = sliding_window;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.lse = lse != nullptr ? lse + (size_t)s0 * num_heads : nullptr;
+    hipError_t e = pa::launch_decode(a, (int)q_dtype, (int)cache_dtype, head_size, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "decode launch");
+  }
+  g_last_error.clear();
+  return PA_OK;
 }
 
 pa_status pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
@@ -366,9 +385,12 @@ pa_status pa_decode_partial(void* out, float* lse, const void* query, const void
                      num_blocks, q_dtype, cache_dtype, scale, 0, workspace, workspace_bytes, stream);
 }
 
+// Batches of more than mla_max_seqs() sequences run as consecutive launches
+// over groups of that many sequences (sequences are independent), each
+// reusing the same workspace.
 size_t pa_mla_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads) {
   if (num_seqs <= 0 || num_heads <= 0) return 0;
-  return pa::mla_workspace_bytes(num_seqs, num_heads, pa::device_cu_count());
+  return pa::mla_workspace_bytes(std::min(num_seqs, pa::mla_max_seqs()), num_heads, pa::device_cu_count());
 }
 
 pa_status pa_mla_decode(void* out, const void* query, const void* latent_cache, const int32_t* block_table,
@@ -376,8 +398,7 @@ pa_status pa_mla_decode(void* out, const void* query, const void* latent_cache, 
                         int32_t max_context_len, int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
                         int32_t block_size, int32_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype, float scale,
                         void* workspace, size_t workspace_bytes, pa_stream_t stream) {
-  if (num_seqs < 0 || num_seqs > pa::mla_max_seqs())
-    return fail(PA_ERR_UNSUPPORTED, "num_seqs must be in [0, %d] (got %d)", pa::mla_max_seqs(), num_seqs);
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0 (got %d)", num_seqs);
   if (block_size != PA_BLOCK_SIZE)
     return fail(PA_ERR_UNSUPPORTED, "block_size must be %d (got %d)", PA_BLOCK_SIZE, block_size);
   if (head_dim_v != 512) return fail(PA_ERR_UNSUPPORTED, "head_dim_v must be 512 (got %d)", head_dim_v);
@@ -401,23 +422,29 @@ pa_status pa_mla_decode(void* out, const void* query, const void* latent_cache, 
   if (!out || !query || !latent_cache || !block_table || !context_lens)
     return fail(PA_ERR_INVALID_ARGUMENT, "null device pointer");
   const int grid = pa::device_cu_count();
-  const size_t need = pa::mla_workspace_bytes(num_seqs, num_heads, grid);
+  const int group = pa::mla_max_seqs();
+  const size_t need = pa::mla_workspace_bytes(std::min(num_seqs, group), num_heads, grid);
   if (workspace_bytes < need || workspace == nullptr)
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "latent decode needs %zu workspace bytes (got %zu)", need,
                 workspace_bytes);
-  pa::MlaArgs a{};
-  a.out = out;
-  a.query = query;
-  a.cache = latent_cache;
-  a.block_table = block_table;
-  a.context_lens = context_lens;
-  pa::mla_bind_workspace(a, workspace, num_seqs, num_heads, grid);
-  a.bt_stride = block_table_stride;
-  a.num_seqs = num_seqs;
-  a.num_heads = num_heads;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = pa::launch_mla_decode(a, head_dim_k, grid, (hipStream_t)stream);
-  return hip_status(e, "latent decode launch");
+  for (int32_t s0 = 0; s0 < num_seqs; s0 += group) {  // (one launch pair per group of sequences)
+    const int32_t n = std::min(group, num_seqs - s0);
+    pa::MlaArgs a{};
+    a.out = static_cast<uint16_t*>(out) + (size_t)s0 * num_heads * head_dim_v;
+    a.query = static_cast<const uint16_t*>(query) + (size_t)s0 * num_heads * head_dim_k;
+    a.cache = latent_cache;
+    a.block_table = block_table + (size_t)s0 * block_table_stride;
+    a.context_lens = context_lens + s0;
+    pa::mla_bind_workspace(a, workspace, n, num_heads, grid);
+    a.bt_stride = block_table_stride;
+    a.num_seqs = n;
+    a.num_heads = num_heads;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    hipError_t e = pa::launch_mla_decode(a, head_dim_k, grid, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "latent decode launch");
+  }
+  g_last_error.clear();
+  return PA_OK;
 }
 
 pa_status pa_merge_partials(void* out, float* lse_out, const void* parts, const float* parts_lse, int32_t num_parts,

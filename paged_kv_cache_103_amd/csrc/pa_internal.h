@@ -58,6 +58,9 @@ size_t decode_shared_prefix_workspace_bytes(int num_seqs, int num_groups, int nu
 constexpr int kSharedPrefixMaxSeqs = 3000;
 int shared_prefix_meta_ints(int num_seqs, int num_groups);
 bool decode_uses_mfma(int q_kind, int cache_kind, int group);
+// Sequences one matrix-core decode launch takes (its per-sequence prefix sums
+// live in LDS); pa_decode runs larger batches as groups of this many.
+constexpr int kMfmaMaxSeqs = 16000;
 int device_cu_count();
 // LDS bytes one CU offers (shared by its resident workgroups).
 int device_lds_per_cu();

@@ -318,7 +318,8 @@ def test_mla_decode_rejects_bad_arguments(lib):
     assert call(dv=256) == 2
     assert call(cd=2) == 2
     assert call(B=32) == 2
-    assert call(S=4096) == 2
+    assert call(S=-1) == 1
+    assert call(S=4096, ws_bytes=64) == 3  # (more than 2048 sequences: groups, one workspace of 2048's size)
     assert call(bt_stride=2) == 1
     assert call(cache=None) == 1
     assert call(scale=0.0) == 1

@@ -3,7 +3,7 @@
 Unowned slots of the pool are NaN, so a read outside a context shows.
 Cases: ragged contexts from 1 token to several thousand for every head count
 (16, 32, 64, 128) and both row widths (512, 576); batches of many short
-sequences (each finished inside one worker; up to the 2048-sequence limit)
+sequences (each finished inside one worker; beyond 2048 sequences, in groups)
 and few long ones (split over many workers and merged), for the 16-head
 kernel too; the benchmark's batch on sampled sequences.
 """
@@ -64,14 +64,19 @@ def test_mla_small(H, DK):
     check(b, out, range(b.num_seqs), f"mla H={H} dk={DK}")
 
 
-@pytest.mark.parametrize("H,S", [(64, 1500), (16, 2048)])
+@pytest.mark.parametrize("H,S", [(64, 1500), (16, 2048), (16, 4500), (128, 2100)])
 def test_mla_many_short_sequences(H, S):
+    """Up to 2048 sequences per launch; larger batches run as groups of
+    2048 with one workspace (sampled sequences in every group, both sides of
+    each group boundary included)."""
     rng = np.random.default_rng(5)
     ctx = rng.integers(1, 200, S).tolist()
-    b = W.make_mla_batch(f"mla_short{H}", 1100, ctx, H, 576, device=DEV)
+    _log(f"mla many short: {S} sequences, {H} heads")
+    b = W.make_mla_batch(f"mla_short{H}_{S}", 1100, ctx, H, 576, device=DEV)
     out = run_mla(b)
     torch.cuda.synchronize()
-    check(b, out, list(range(0, S, 97)) + [S - 1], f"mla many short, {H} heads")
+    edges = [x for g in range(2048, S, 2048) for x in (g - 1, g)]
+    check(b, out, sorted(set(list(range(0, S, 97)) + [S - 1] + edges)), f"mla many short, {H} heads")
 
 
 def test_mla_few_long_sequences():

@@ -168,6 +168,34 @@ def test_decode_llama8b_full():
     check_rows(b, out, range(b.num_seqs), "llama8b_decode")
 
 
+@pytest.mark.parametrize("cd", ["bf16", "fp8_e4m3"])
+def test_decode_more_than_16000_sequences(cd):
+    """Beyond 16000 sequences pa_decode runs groups of 16000 on the
+    matrix-core kernel, one workspace (a group's) for all: sequences on both
+    sides of the group boundary and across the batch against the oracle,
+    and pa_decode_partial's outputs equal to pa_decode's bit for bit."""
+    S = 16500
+    rng = np.random.default_rng(4200)
+    ctx = rng.integers(1, 300, S).tolist()
+    _log(f"decode {S} sequences, ctx 1..299, 8/2 heads d64 {cd}")
+    b = W.make_batch(f"decode_{S}_{cd}", 4200, ctx, [1] * S, 8, 2, 64, "bf16", cd, device=DEV)
+    one_group = pa.decode_workspace_bytes(16000, b.max_context_len, 8, 2, 64, b.cache_dtype, 0)
+    assert one_group > 0  # (the split plan: some stream has more than 16 blocks)
+    assert pa.decode_workspace_bytes(S, b.max_context_len, 8, 2, 64, b.cache_dtype, 0) == one_group
+    out = run_decode(b)
+    torch.cuda.synchronize()
+    check_rows(b, out, [0, 1, 7999, 15998, 15999, 16000, 16001, 16499], f"decode {S} seqs {cd}")
+    m = b.meta(DEV)
+    part = torch.empty_like(b.query)
+    lse = torch.empty((S, 8), dtype=torch.float32, device=DEV)
+    ws = torch.empty(one_group, dtype=torch.uint8, device=DEV)
+    pa.decode_partial(part, lse, b.query, b.k_cache, b.v_cache, m["block_table"], m["context_lens"],
+                      b.max_context_len, b.scale, b.k_scale, b.v_scale, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(part.view(torch.int16), out.view(torch.int16))
+    assert bool(torch.isfinite(lse).all())
+
+
 def test_decode_agentic_sampled():
     b = W.make_config("agentic_decode", device=DEV)
     out = run_decode(b)
