@@ -618,7 +618,8 @@ pa_status pa_decode_sparse(void* out, const void* query, const void* k_cache, co
                  pa::sparse_select_lds_bytes(max_context_len, pa::kSparseRankMax);
 
   const int32_t eff_max = 16 * (max_selected + 1);
-  const pa::DecodePlan plan = make_plan(num_seqs, eff_max, num_heads, num_kv_heads, head_size, cache_dtype, 0);
+  const int32_t dgroup = decode_group_seqs(num_seqs, num_heads, num_kv_heads, cache_dtype, false);
+  const pa::DecodePlan plan = make_plan(dgroup, eff_max, num_heads, num_kv_heads, head_size, cache_dtype, 0);
   pa::DecodeArgs a{};
   a.out = out;
   a.query = query;
@@ -645,14 +646,24 @@ pa_status pa_decode_sparse(void* out, const void* query, const void* k_cache, co
   }
   hipError_t e = pa::launch_sparse_select(sa, num_seqs, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, "sparse block selection launch");
-  const size_t dec_need = pa::decode_workspace_bytes(plan, num_seqs, num_heads, num_kv_heads, head_size);
-  a.block_table = sa.cbt;
-  a.context_lens = sa.eff_ctx;
-  bind_workspace(a, plan, dec_need ? ws + sparse_table_bytes(num_seqs, max_selected) : nullptr,
-                 num_seqs, num_heads, num_kv_heads, head_size);
-  a.bt_stride = sa.cbt_stride;
-  e = pa::launch_decode(a, (int)q_dtype, (int)cache_dtype, head_size, (hipStream_t)stream);
-  return hip_status(e, "sparse decode launch");
+  // the decode over the compacted tables, in groups of sequences as pa_decode
+  const size_t dec_need = pa::decode_workspace_bytes(plan, dgroup, num_heads, num_kv_heads, head_size);
+  const size_t row_bytes = (size_t)num_heads * head_size * elem_bytes(q_dtype);
+  for (int32_t s0 = 0; s0 < num_seqs; s0 += dgroup) {
+    const int32_t n = std::min(dgroup, num_seqs - s0);
+    a.out = static_cast<char*>(out) + (size_t)s0 * row_bytes;
+    a.query = static_cast<const char*>(query) + (size_t)s0 * row_bytes;
+    a.block_table = sa.cbt + (size_t)s0 * sa.cbt_stride;
+    a.context_lens = sa.eff_ctx + s0;
+    bind_workspace(a, plan, dec_need ? ws + sparse_table_bytes(num_seqs, max_selected) : nullptr, n, num_heads,
+                   num_kv_heads, head_size);
+    a.bt_stride = sa.cbt_stride;
+    a.num_seqs = n;
+    e = pa::launch_decode(a, (int)q_dtype, (int)cache_dtype, head_size, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "sparse decode launch");
+  }
+  g_last_error.clear();
+  return PA_OK;
 }
 
 pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, const void* v_cache,
@@ -688,34 +699,41 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
   // Rows with one query token may exist unless every sequence provably has
   // max_q_len > 1 tokens (the only case the host scalars can prove).
   const bool any_single = !(has_chunks && (long long)num_q_tokens == (long long)num_seqs * max_q_len);
-  const pa::DecodePlan plan = make_plan(num_seqs, max_context_len, num_heads, num_kv_heads, head_size,
+  // (one-token rows of more than kMfmaMaxSeqs sequences: groups, as pa_decode)
+  const int32_t dgroup = decode_group_seqs(num_seqs, num_heads, num_kv_heads, cache_dtype, false);
+  const pa::DecodePlan plan = make_plan(dgroup, max_context_len, num_heads, num_kv_heads, head_size,
                                         cache_dtype, sliding_window);
   const size_t need =
-      any_single ? pa::decode_workspace_bytes(plan, num_seqs, num_heads, num_kv_heads, head_size) : 0;
+      any_single ? pa::decode_workspace_bytes(plan, dgroup, num_heads, num_kv_heads, head_size) : 0;
   if (workspace_bytes < need || (need > 0 && workspace == nullptr))
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "prefill needs %zu workspace bytes (got %zu)", need,
                 workspace_bytes);
   const hipStream_t hs = (hipStream_t)stream;
   const float scale_log2 = scale * 1.4426950408889634f;
 
-  // one-token rows: the decode kernel (skips rows of longer chunks)
-  pa::DecodeArgs d{};
-  d.out = out;
-  d.query = query;
-  d.k_cache = k_cache;
-  d.v_cache = v_cache;
-  d.k_scale = k_scale;
-  d.v_scale = v_scale;
-  d.block_table = block_table;
-  d.context_lens = context_lens;
-  d.cu_seqlens = cu_seqlens;
-  bind_workspace(d, plan, need ? workspace : nullptr, num_seqs, num_heads, num_kv_heads, head_size);
-  d.bt_stride = block_table_stride;
-  d.num_seqs = num_seqs;
-  d.num_heads = num_heads;
-  d.num_kv_heads = num_kv_heads;
-  d.window = sliding_window;
-  d.scale_log2 = scale_log2;
+  // one-token rows: the decode kernel (skips rows of longer chunks; query
+  // and output rows are addressed through cu_seqlens), for the sequences
+  // [s0, s0 + n)
+  auto decode_rows = [&](int32_t s0, int32_t n) {
+    pa::DecodeArgs d{};
+    d.out = out;
+    d.query = query;
+    d.k_cache = k_cache;
+    d.v_cache = v_cache;
+    d.k_scale = k_scale;
+    d.v_scale = v_scale;
+    d.block_table = block_table + (size_t)s0 * block_table_stride;
+    d.context_lens = context_lens + s0;
+    d.cu_seqlens = cu_seqlens + s0;
+    bind_workspace(d, plan, need ? workspace : nullptr, n, num_heads, num_kv_heads, head_size);
+    d.bt_stride = block_table_stride;
+    d.num_seqs = n;
+    d.num_heads = num_heads;
+    d.num_kv_heads = num_kv_heads;
+    d.window = sliding_window;
+    d.scale_log2 = scale_log2;
+    return d;
+  };
 
   pa::PrefillArgs p{};
   if (has_chunks) {
@@ -749,7 +767,7 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
   // prefill workgroup (both only read the cache and they write disjoint
   // rows of out); the caller's stream waits for both.
   bool beside = false;
-  if (any_single && has_chunks && plan.split_waves > 0 && !plan.one_per_stream &&
+  if (any_single && has_chunks && dgroup == num_seqs && plan.split_waves > 0 && !plan.one_per_stream &&
       pa::decode_side_supported((int)q_dtype, (int)cache_dtype, head_size, group)) {
     const size_t side = pa::decode_side_lds_bytes(num_seqs, group);
     const size_t pf = pa::prefill_lds_bytes((int)cache_dtype, head_size, group);
@@ -768,7 +786,7 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
     p.nontemporal_kv = 1;
     e = pa::launch_prefill(p, (int)cache_dtype, head_size, hs);
     if (e != hipSuccess) return hip_status(e, "prefill launch");
-    const hipError_t ed = pa::launch_decode_side(d, (int)cache_dtype, ss->stream);
+    const hipError_t ed = pa::launch_decode_side(decode_rows(0, num_seqs), (int)cache_dtype, ss->stream);
     e = hipEventRecord(ss->join, ss->stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(hs, ss->join, 0);
     if (ed != hipSuccess) return hip_status(ed, "decode launch (one-token rows)");
@@ -777,8 +795,11 @@ pa_status pa_prefill_chunk(void* out, const void* query, const void* k_cache, co
     return PA_OK;
   }
   if (any_single) {
-    hipError_t e = pa::launch_decode(d, (int)q_dtype, (int)cache_dtype, head_size, hs);
-    if (e != hipSuccess) return hip_status(e, "decode launch (one-token rows)");
+    for (int32_t s0 = 0; s0 < num_seqs; s0 += dgroup) {
+      hipError_t e = pa::launch_decode(decode_rows(s0, std::min(dgroup, num_seqs - s0)), (int)q_dtype,
+                                       (int)cache_dtype, head_size, hs);
+      if (e != hipSuccess) return hip_status(e, "decode launch (one-token rows)");
+    }
   }
   if (has_chunks) {
     hipError_t e = pa::launch_prefill(p, (int)cache_dtype, head_size, hs);

@@ -196,6 +196,22 @@ def test_decode_more_than_16000_sequences(cd):
     assert bool(torch.isfinite(lse).all())
 
 
+def test_mixed_batch_more_than_16000_rows():
+    """A mixed batch of 16,099 one-token rows and a 64-token chunk: the rows
+    run as groups of 16000 (addressed through cu_seqlens), the chunk on the
+    prefill kernel; the workspace is what pa_prefill_workspace_bytes says."""
+    S = 16100
+    rng = np.random.default_rng(4300)
+    ctx = rng.integers(1, 300, S).tolist()
+    ctx[-1] = 500
+    ql = [1] * (S - 1) + [64]
+    _log(f"mixed batch: {S - 1} one-token rows + a 64-token chunk, 8/2 heads d64")
+    b = W.make_batch("mixed_16100", 4300, ctx, ql, 8, 2, 64, "bf16", "bf16", device=DEV)
+    out = run_prefill(b)
+    torch.cuda.synchronize()
+    check_rows(b, out, [0, 15999, 16000, 16098, 16099], f"mixed batch of {S} sequences")
+
+
 def test_decode_agentic_sampled():
     b = W.make_config("agentic_decode", device=DEV)
     out = run_decode(b)

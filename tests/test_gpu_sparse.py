@@ -192,6 +192,23 @@ def test_sparse_many_streams_long_lists_take_three_launches():
     check(b, choice, out, [0, 21, 42, 63], "sparse long lists")
 
 
+def test_sparse_more_than_16000_sequences_three_launches():
+    """16,100 sequences whose lists are padded to 1030 entries (so the
+    three-launch path serves them): the selection covers every sequence and
+    the decode over the compacted tables runs as groups of 16000."""
+    S = 16100
+    rng = np.random.default_rng(2800)
+    ctx = rng.integers(1, 300, S).tolist()
+    b, choice = W.make_sparse_batch("sparse_16100", 2800, ctx, 3, 8, 2, 64, "bf16", "bf16", device=DEV, noise=True)
+    sel = np.full((S, 1030), -1, dtype=np.int32)
+    sel[:, :choice.selected.shape[1]] = choice.selected
+    choice = W.SparseChoice(sel, choice.num_selected, choice.chosen)
+    _log(f"sparse {S} sequences, lists padded to 1030 entries")
+    out = run_sparse(b, choice)
+    torch.cuda.synchronize()
+    check(b, choice, out, [0, 1, 15999, 16000, 16099], f"sparse {S} sequences")
+
+
 def test_sparse_long_context_sampled():
     """The benchmark's batch: 64 sequences, contexts U{32768..524288}, 128
     chosen blocks each, 32/8 heads, d 128, bf16."""
