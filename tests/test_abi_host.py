@@ -156,6 +156,21 @@ def test_workspace_queries(lib):
         lib.decode_workspace_bytes(193, 67584, 32, 8, 128, "bf16")
     # no one-token rows possible: no workspace
     assert lib.prefill_workspace_bytes(2, 600, 300, 5000, 32, 8, 128, "bf16") == 0
+    # beyond 16000 sequences the matrix-core decode runs groups of 16000 with
+    # one group's workspace (the VALU kernel, for fp32 caches, does not group)
+    for cd in ("bf16", "fp8_e4m3"):
+        g = lib.decode_workspace_bytes(16000, 8192, 32, 8, 128, cd)
+        assert g > lib.decode_workspace_bytes(15999, 8192, 32, 8, 128, cd)
+        assert lib.decode_workspace_bytes(16001, 8192, 32, 8, 128, cd) == g
+        assert lib.decode_workspace_bytes(100000, 8192, 32, 8, 128, cd) == g
+        assert lib.prefill_workspace_bytes(20000, 20100, 101, 8192, 32, 8, 128, cd) == g
+    assert lib.decode_workspace_bytes(20000, 8192, 8, 2, 64, "f32") > \
+        lib.decode_workspace_bytes(16000, 8192, 8, 2, 64, "f32")
+    # the latent decode: groups of 2048 sequences
+    L = lib.load()
+    m = L.pa_mla_decode_workspace_bytes(2048, 128)
+    assert m > L.pa_mla_decode_workspace_bytes(2047, 128)
+    assert L.pa_mla_decode_workspace_bytes(2049, 128) == m == L.pa_mla_decode_workspace_bytes(50000, 128)
 
 
 def test_shared_prefix_rejects_bad_arguments(lib):
