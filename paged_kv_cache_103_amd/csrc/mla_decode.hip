@@ -1133,12 +1133,30 @@ __global__ __launch_bounds__(256) void mla_merge(MlaArgs a) {
 #pragma unroll
   for (int k = 0; k < MLA_DV / 64; ++k) acc[k] = 0.f;
   float L = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[rec(i) * 2] - M);
-    L += w * a.part_ml[rec(i) * 2 + 1];
-    const float* row = a.part_o + rec(i) * MLA_DV;
+  // records in batches of RB, every load of a batch issued before the first
+  // is used (one memory round trip per batch instead of per record); the
+  // sums run in record order as one at a time would
+  constexpr int RB = 8;
+  for (int i0 = 0; i0 < n; i0 += RB) {
+    float ml[RB][2], v[RB][MLA_DV / 64];
 #pragma unroll
-    for (int k = 0; k < MLA_DV / 64; ++k) acc[k] = fmaf(w, row[64 * k + lane], acc[k]);
+    for (int u = 0; u < RB; ++u) {
+      const size_t r = rec(min(i0 + u, n - 1));  // (past the end: a valid record, not summed)
+      ml[u][0] = a.part_ml[r * 2];
+      ml[u][1] = a.part_ml[r * 2 + 1];
+      const float* row = a.part_o + r * MLA_DV;
+#pragma unroll
+      for (int k = 0; k < MLA_DV / 64; ++k) v[u][k] = row[64 * k + lane];
+    }
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      if (i0 + u < n) {
+        const float w = __builtin_amdgcn_exp2f(ml[u][0] - M);
+        L += w * ml[u][1];
+#pragma unroll
+        for (int k = 0; k < MLA_DV / 64; ++k) acc[k] = fmaf(w, v[u][k], acc[k]);
+      }
+    }
   }
   const float inv = 1.f / L;
   if constexpr (FP16_TILES) {
