@@ -348,11 +348,17 @@ template <int CK, int D>
 __device__ __forceinline__ void load_query(u32x4* qf, const DecodeArgs& a, int qrow, int g, int G, int c16,
                                            int q4, int ncols) {
   constexpr int E = CacheElem<CK>::bytes;
+  // G is a power of two (1..16): a shift and a mask, which the register
+  // allocator recomputes where it kept a division's results live across the
+  // block loop (and spilled them: the shared-prefix kernel on bf16 caches
+  // then ran ~6% slower than plain decode on the same bytes)
+  const int lg = __builtin_ctz((unsigned)G);
 #pragma unroll
   for (int j = 0; j < D / 32; ++j) {
     if (c16 < ncols) {
       const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) +
-                           ((size_t)(qrow + c16 / G) * a.num_heads + g * G + c16 % G) * D + kstep_d0<E>(j, q4);
+                           ((size_t)(qrow + (c16 >> lg)) * a.num_heads + g * G + (c16 & (G - 1))) * D +
+                           kstep_d0<E>(j, q4);
       qf[j] = load16(qp);
     } else {
       qf[j] = u32x4{0, 0, 0, 0};
